@@ -1,0 +1,166 @@
+"""Python access to the float64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product package.  It shares
+no code with the HIP library; inputs reach it as float64 copies of the
+stored values.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def build():
+    """Compile oracle.c into liboracle.so (gcc, OpenMP)."""
+    subprocess.run(["sh", os.path.join(_HERE, "build.sh")], check=True)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Temporarily route every oracle call to another build of oracle.c (tests only)."""
+    global _lib
+    saved = _load()
+    _lib = _configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _configure(lib):
+    lib.oracle_bf16_round.restype = ctypes.c_double
+    lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_round_array.restype = None
+    lib.oracle_bf16_round_array.argtypes = [_dp, _i64]
+    lib.oracle_rope.restype = None
+    lib.oracle_rope.argtypes = [_dp, _i64, _i64, _i64, _i64, _i64p, ctypes.c_double, ctypes.c_int]
+    lib.oracle_prefill.restype = ctypes.c_int
+    lib.oracle_prefill.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64p,
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int]
+    lib.oracle_stream_step.restype = ctypes.c_int
+    lib.oracle_stream_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64p, _dp, _i64, _i64, _i64,
+                                       _i64, _i64, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int]
+    lib.oracle_ring_append.restype = ctypes.c_int
+    lib.oracle_ring_append.argtypes = [_dp, _dp, _dp, _dp, _i64p, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, t=_dp):
+    return a.ctypes.data_as(t)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def bf16_round(x):
+    """Round float64 values to the nearest bfloat16 value (ties to even)."""
+    a = _f64(x).copy()
+    _load().oracle_bf16_round_array(_ptr(a), a.size)
+    return a
+
+
+def rope(x, pos=None, theta=1e6, bf16=False):
+    """Rotate x [B,T,H,D] (copy) with half-split RoPE; pos [B,T] absolute positions or None (= t)."""
+    a = _f64(x).copy()
+    B, T, H, D = a.shape
+    p = None
+    if pos is not None:
+        p = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, dtype=np.int64), (B, T)))
+    _load().oracle_rope(_ptr(a), B, T, H, D, None if p is None else _ptr(p, _i64p),
+                        float(theta), int(bool(bf16)))
+    return a
+
+
+def prefill(q, k, v, W, pos=None, theta=1e6, scale=None, bf16=False, rope_applied=False,
+            nthreads=0):
+    """Causal sliding-window attention over whole chunks; q,k,v [B,T,H,D] -> o [B,T,H,D] float64.
+
+    pos: None (positions 0..T-1), an int offset (positions pos+t), or an array [B,T].
+    bf16=True applies the bfloat16 contract (rotated q,k rounded to bf16).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    p = None
+    if pos is not None:
+        if np.isscalar(pos):
+            p = (np.int64(pos) + np.arange(T, dtype=np.int64))[None, :].repeat(B, 0)
+        else:
+            p = np.broadcast_to(np.asarray(pos, dtype=np.int64), (B, T))
+        p = np.ascontiguousarray(p, dtype=np.int64)
+    o = np.zeros_like(q)
+    rc = _load().oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, D, int(W),
+                                None if p is None else _ptr(p, _i64p), float(theta), float(scale),
+                                int(bool(bf16)), int(bool(rope_applied)), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return o
+
+
+def stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, W, theta=1e6, scale=None, bf16=False,
+                rope_applied=False, nthreads=0):
+    """One streaming step; q/k/v_new [S,n,H,D], rings [S,H,W,D], pos [S] -> o [S,n,H,D]."""
+    q_new, k_new, v_new = _f64(q_new), _f64(k_new), _f64(v_new)
+    ring_k, ring_v = _f64(ring_k), _f64(ring_v)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    S, n, H, D = q_new.shape
+    assert ring_k.shape == (S, H, W, D) and ring_v.shape == (S, H, W, D)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros_like(q_new)
+    rc = _load().oracle_stream_step(_ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k),
+                                    _ptr(ring_v), _ptr(pos, _i64p), _ptr(o), S, n, H, D, int(W),
+                                    float(theta), float(scale), int(bool(bf16)),
+                                    int(bool(rope_applied)), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_stream_step rejected its arguments")
+    return o
+
+
+def ring_append(ring_k, ring_v, k_new, v_new, pos, W, theta=1e6, bf16=False, rope_applied=False):
+    """Append in place: ring_k/ring_v float64 [S,H,W,D] and pos int64 [S] are modified."""
+    for a in (ring_k, ring_v):
+        assert a.dtype == np.float64 and a.flags.c_contiguous
+    assert pos.dtype == np.int64 and pos.flags.c_contiguous
+    k_new, v_new = _f64(k_new), _f64(v_new)
+    S, n, H, D = k_new.shape
+    rc = _load().oracle_ring_append(_ptr(ring_k), _ptr(ring_v), _ptr(k_new), _ptr(v_new),
+                                    _ptr(pos, _i64p), S, n, H, D, int(W), float(theta),
+                                    int(bool(bf16)), int(bool(rope_applied)))
+    if rc != 0:
+        raise ValueError("oracle_ring_append rejected its arguments")

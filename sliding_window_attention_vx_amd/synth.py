@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for the sliding-window RoPE attention path.
+
+This module only *draws* inputs: it holds none of the attention arithmetic
+(no rotation, no scores, no softmax).  Both the GPU path and the CPU oracle
+consume what it returns, so the same seed gives the same bytes on both sides.
+
+Workloads (shapes follow the Voxtral Realtime 2602 audio encoder: 32 heads of
+head_dim 64, window 750, RoPE theta 1e6, 4 encoder frames per streaming step;
+see the transcribe.cpp "Voxtral" family notes, section Architecture, Voxtral
+Realtime 2602):
+
+  tiny      B1  T64   H4  W16   fp32, N(0,1)
+  layer     B1  T1500 H32 W750  bf16, 0.5*N(0,1)
+  stack     32 layers x (B4 T1500 H32) W750 bf16, 0.5*N(0,1), one seed per layer
+  stream    64 streams x 4 new frames, H32, W750, bf16 ring pre-filled N(0,1),
+            first new position per stream ~ U{750..20000}
+  long      B8  T6000 H32 W750  bf16, N(0,1), 1% of key rows scaled x8
+
+Draw order for a prefill set: Q, K, V (each standard_normal float32 of shape
+[B,T,H,64]), then (long only) the stressed key-row choice.  Scaling happens in
+float32 (a power of two, so exact), then round-to-nearest-even to bfloat16
+for bf16 workloads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+
+import numpy as np
+
+HEAD_DIM = 64
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    T: int
+    H: int
+    W: int
+    dtype: str  # "f32" or "bf16"
+    scale: float  # multiplier applied to N(0,1) draws
+    seed: int
+    stress_frac: float = 0.0  # fraction of key rows multiplied by stress_mult
+    stress_mult: float = 1.0
+    layers: int = 1
+    theta: float = 1e6
+    D: int = HEAD_DIM
+
+
+@dataclasses.dataclass(frozen=True)
+class StreamConfig:
+    name: str
+    S: int
+    n: int
+    H: int
+    W: int
+    dtype: str
+    seed: int
+    pos_lo: int
+    pos_hi: int
+    theta: float = 1e6
+    D: int = HEAD_DIM
+
+
+CONFIGS = {
+    "tiny": PrefillConfig("tiny", B=1, T=64, H=4, W=16, dtype="f32", scale=1.0, seed=1),
+    "layer": PrefillConfig("layer", B=1, T=1500, H=32, W=750, dtype="bf16", scale=0.5, seed=2),
+    "stack": PrefillConfig("stack", B=4, T=1500, H=32, W=750, dtype="bf16", scale=0.5, seed=3,
+                           layers=32),
+    "stream": StreamConfig("stream", S=64, n=4, H=32, W=750, dtype="bf16", seed=4,
+                           pos_lo=750, pos_hi=20000),
+    "long": PrefillConfig("long", B=8, T=6000, H=32, W=750, dtype="bf16", scale=1.0, seed=5,
+                          stress_frac=0.01, stress_mult=8.0),
+}
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 storage conversion (input preparation only)
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 array holding exactly the bfloat16-representable nearest values."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# prefill sets
+# ---------------------------------------------------------------------------
+
+def make_prefill(B: int, T: int, H: int, *, seed, dtype: str = "bf16", scale: float = 1.0,
+                 stress_frac: float = 0.0, stress_mult: float = 1.0, D: int = HEAD_DIM):
+    """Draw Q, K, V of shape [B,T,H,D] as float32 arrays holding storage-dtype values.
+
+    `seed` is an int or a sequence of ints (numpy SeedSequence entropy).
+    Returns dict(q, k, v, stressed_rows) where stressed_rows is the sorted flat
+    index (over B*T*H rows of K) of the rows that were multiplied.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    shape = (B, T, H, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        s = np.float32(scale)
+        q *= s
+        k *= s
+        v *= s
+    stressed = np.zeros(0, dtype=np.int64)
+    if stress_frac > 0.0:
+        nrows = B * T * H
+        count = int(round(stress_frac * nrows))
+        stressed = np.sort(rng.choice(nrows, size=count, replace=False)).astype(np.int64)
+        kr = k.reshape(nrows, D)
+        kr[stressed] *= np.float32(stress_mult)
+    return dict(q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype), stressed_rows=stressed)
+
+
+def make_config(name: str, layer: int = 0):
+    """Prefill set for a named workload (for 'stack', one layer's set)."""
+    c = CONFIGS[name]
+    assert isinstance(c, PrefillConfig)
+    seed = [c.seed, layer] if c.layers > 1 else c.seed
+    return make_prefill(c.B, c.T, c.H, seed=seed, dtype=c.dtype, scale=c.scale,
+                        stress_frac=c.stress_frac, stress_mult=c.stress_mult, D=c.D)
+
+
+# ---------------------------------------------------------------------------
+# streaming sets
+# ---------------------------------------------------------------------------
+
+def make_stream_state(S: int, H: int, W: int, *, seed, pos_lo: int, pos_hi: int,
+                      dtype: str = "bf16", D: int = HEAD_DIM, full: bool = True):
+    """Pre-filled ring state for S streams.
+
+    Returns dict(ring_k, ring_v [S,H,W,D] float32 holding storage values, pos [S] int64).
+    pos[s] is the absolute position of the next frame to arrive, drawn
+    uniformly from {pos_lo..pos_hi}.  Ring slot j holds the frame whose
+    position p satisfies p mod W == j; with full=True all W slots hold the
+    frames pos-W..pos-1 (pos_lo must then be >= W).  The ring contents are
+    N(0,1) draws and are taken to be keys that are already rotated.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    ring_k = rng.standard_normal((S, H, W, D), dtype=np.float32)
+    ring_v = rng.standard_normal((S, H, W, D), dtype=np.float32)
+    pos = rng.integers(pos_lo, pos_hi, size=S, endpoint=True, dtype=np.int64)
+    if full and pos_lo < W:
+        raise ValueError("a full ring needs pos_lo >= W")
+    return dict(ring_k=_store(ring_k, dtype), ring_v=_store(ring_v, dtype), pos=pos)
+
+
+def make_stream_frames(S: int, n: int, H: int, *, seed, step: int, dtype: str = "bf16",
+                       D: int = HEAD_DIM, scale: float = 1.0):
+    """Fresh new-frame q, k, v [S,n,H,D] for streaming step `step`."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1000003, step])))
+    shape = (S, n, H, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        s = np.float32(scale)
+        q *= s
+        k *= s
+        v *= s
+    return dict(q=_store(q, dtype), k=_store(k, dtype), v=_store(v, dtype))
+
+
+def make_stream_config(name: str = "stream"):
+    c = CONFIGS[name]
+    assert isinstance(c, StreamConfig)
+    return make_stream_state(c.S, c.H, c.W, seed=c.seed, pos_lo=c.pos_lo, pos_hi=c.pos_hi,
+                             dtype=c.dtype, D=c.D)
+
+
+def band_pairs(T: int, W: int) -> int:
+    """Number of (query, key) pairs with 0 <= t-j < W, 0 <= j <= t < T (counting only)."""
+    if T <= W:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W

@@ -1,0 +1,378 @@
+"""Pins for the float64 CPU oracle, against facts fixed outside the oracle.
+
+Each test names what pins it: a brute-force dense formulation, torch's
+scaled_dot_product_attention, a closed form, an invariant the pages state
+(offline == streaming; full causal attention when T <= W), or a constant the
+pages print (tests/golden/voxtral_realtime_constants.json).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sliding_window_attention_vx_amd import synth
+from tests.refimpl import complex_rope, dense_band_attention, sdpa_band
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# --------------------------------------------------------------------------
+# bfloat16 rounding
+# --------------------------------------------------------------------------
+
+def test_bf16_round_matches_bit_rounding_of_float32():
+    # Independent implementation: integer round-to-nearest-even on float32 bits.
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 100000),
+                        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-39, -2.5e-40], dtype=np.float32)])
+    x = x.astype(np.float32)
+    want = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)).astype(np.float64)
+    got = oracle.bf16_round(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_ties_and_closed_forms():
+    u = 2.0 ** -7  # spacing of bf16 in [1, 2)
+    cases = {
+        1.0 + u / 2: 1.0,                  # tie -> even significand (1.0)
+        1.0 + 3 * u / 2: 1.0 + 2 * u,      # tie -> even (1 + 2u)
+        1.0 + u / 2 + 2.0 ** -40: 1.0 + u,  # just above the tie
+        -(1.0 + u / 2): -1.0,
+        1.0 / 3.0: 0.333984375,            # 171/512
+        math.pi: 3.140625,
+    }
+    for x, want in cases.items():
+        assert oracle.bf16_round(np.array([x]))[0] == want, x
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    x = rnd((1, 3, 2, 64), 1)
+    np.testing.assert_array_equal(oracle.rope(x, pos=np.zeros((1, 3), np.int64)), x)
+
+
+def test_rope_matches_complex_multiplication():
+    x = rnd((2, 5, 3, 64), 2)
+    pos = np.array([[0, 1, 749, 750, 19999], [3, 17, 1500, 6000, 123456]], dtype=np.int64)
+    got = oracle.rope(x, pos=pos, theta=1e6)
+    for b in range(2):
+        want = complex_rope(x[b], pos[b], theta=1e6)
+        np.testing.assert_allclose(got[b], want, rtol=0, atol=1e-9)
+
+
+def test_rope_d2_is_rotation_by_position_radians():
+    # D = 2: one pair with frequency theta^0 = 1, so the angle is the position itself.
+    x = rnd((1, 4, 1, 2), 3)
+    pos = np.array([[0, 1, 2, 1000]], dtype=np.int64)
+    got = oracle.rope(x, pos=pos, theta=12345.0)
+    z = (x[0, :, 0, 0] + 1j * x[0, :, 0, 1]) * np.exp(1j * pos[0].astype(float))
+    np.testing.assert_allclose(got[0, :, 0, 0], z.real, atol=1e-12)
+    np.testing.assert_allclose(got[0, :, 0, 1], z.imag, atol=1e-12)
+
+
+def test_rope_frequencies_closed_form_theta_1e6():
+    # theta = 1e6, D = 64: f_i = 1e6^(-2i/64) = 10^(-3i/16).  Rotating the basis
+    # vector e_i at position 1 turns it by exactly f_i radians into (cos, sin)
+    # on dims (i, i+32).
+    D = 64
+    closed = {0: 1.0, 8: 10 ** -1.5, 16: 1e-3, 24: 10 ** -4.5, 31: 10 ** (-93 / 16)}
+    for i, f in closed.items():
+        x = np.zeros((1, 1, 1, D))
+        x[0, 0, 0, i] = 1.0
+        r = oracle.rope(x, pos=np.array([[1]]), theta=1e6)[0, 0, 0]
+        assert abs(math.atan2(r[i + 32], r[i]) - f) < 1e-15 * max(1.0, f) + 1e-18, i
+        assert abs(r[i] ** 2 + r[i + 32] ** 2 - 1.0) < 1e-15
+        others = np.delete(r, [i, i + 32])
+        assert np.all(others == 0.0)
+
+
+def test_rope_preserves_pair_norms():
+    x = rnd((1, 6, 4, 64), 4)
+    pos = np.arange(6, dtype=np.int64)[None] * 3331
+    r = oracle.rope(x, pos=pos)
+    n0 = x[..., :32] ** 2 + x[..., 32:] ** 2
+    n1 = r[..., :32] ** 2 + r[..., 32:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-13)
+
+
+@pytest.mark.parametrize("shift", [1, 7, 750, 19999])
+def test_rope_relative_position_property(shift):
+    # <R(m)q, R(n)k> depends only on n - m.
+    q = rnd((1, 4, 2, 64), 5)
+    k = rnd((1, 4, 2, 64), 6)
+    m = np.array([[0, 5, 100, 749]])
+    n = np.array([[3, 5, 40, 0]])
+    s0 = np.sum(oracle.rope(q, pos=m) * oracle.rope(k, pos=n), axis=-1)
+    s1 = np.sum(oracle.rope(q, pos=m + shift) * oracle.rope(k, pos=n + shift), axis=-1)
+    np.testing.assert_allclose(s1, s0, rtol=1e-9, atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# prefill attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,W,H,D", [(1, 1, 1, 2), (2, 3, 1, 8), (5, 3, 2, 8), (16, 16, 1, 64),
+                                     (16, 1, 2, 8), (64, 16, 4, 64), (64, 69, 1, 64),
+                                     (40, 7, 3, 16)])
+def test_prefill_matches_dense_brute_force(T, W, H, D):
+    q, k, v = (rnd((1, T, H, D), s) for s in (10, 11, 12))
+    pos = np.arange(T)
+    got = oracle.prefill(q, k, v, W)[0]
+    want = dense_band_attention(complex_rope(q[0], pos), complex_rope(k[0], pos), v[0], W)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_prefill_full_causal_when_T_le_W():
+    # With T <= W the window never bites: plain causal attention (torch SDPA, is_causal).
+    B, T, H, D, W = 2, 48, 3, 64, 750
+    q, k, v = (rnd((B, T, H, D), s) for s in (20, 21, 22))
+    pos = np.arange(T)
+    qr = np.stack([complex_rope(q[b], pos) for b in range(B)])
+    kr = np.stack([complex_rope(k[b], pos) for b in range(B)])
+    want = sdpa_band(qr, kr, v, W, causal_flag=True)
+    np.testing.assert_allclose(oracle.prefill(q, k, v, W), want, rtol=0, atol=1e-12)
+
+
+def test_prefill_band_matches_sdpa_with_mask():
+    B, T, H, D, W = 1, 100, 2, 64, 37
+    q, k, v = (rnd((B, T, H, D), s) for s in (23, 24, 25))
+    pos = np.arange(T)
+    qr = complex_rope(q[0], pos)[None]
+    kr = complex_rope(k[0], pos)[None]
+    want = sdpa_band(qr, kr, v, W)
+    np.testing.assert_allclose(oracle.prefill(q, k, v, W), want, rtol=0, atol=1e-12)
+
+
+def test_window_one_returns_values_exactly():
+    q, k, v = (rnd((2, 9, 3, 64), s) for s in (30, 31, 32))
+    np.testing.assert_array_equal(oracle.prefill(q, k, v, 1), v)
+
+
+def test_constant_values_give_constant_output():
+    q, k = rnd((1, 30, 2, 64), 33), rnd((1, 30, 2, 64), 34)
+    v = np.full((1, 30, 2, 64), -2.75)
+    np.testing.assert_allclose(oracle.prefill(q, k, v, 11), v, rtol=0, atol=1e-14)
+
+
+def test_prefill_invariant_under_position_offset():
+    q, k, v = (rnd((1, 50, 2, 64), s) for s in (35, 36, 37))
+    o0 = oracle.prefill(q, k, v, 20, pos=0)
+    for off in (1, 750, 19999):
+        np.testing.assert_allclose(oracle.prefill(q, k, v, 20, pos=off), o0, rtol=0, atol=1e-9)
+
+
+def test_window_locality():
+    # Query t sees frames t-W+1..t: changing frame t-W leaves it unchanged,
+    # changing frame t-W+1 does not.
+    T, W, t = 40, 10, 30
+    q, k, v = (rnd((1, T, 1, 64), s) for s in (40, 41, 42))
+    o0 = oracle.prefill(q, k, v, W)
+    k1, v1 = k.copy(), v.copy()
+    k1[0, t - W] += 5.0
+    v1[0, t - W] += 5.0
+    o1 = oracle.prefill(q, k1, v1, W)
+    np.testing.assert_array_equal(o1[0, t], o0[0, t])
+    assert np.any(o1[0, t - W] != o0[0, t - W])
+    k2, v2 = k.copy(), v.copy()
+    k2[0, t - W + 1] += 5.0
+    v2[0, t - W + 1] += 5.0
+    o2 = oracle.prefill(q, k2, v2, W)
+    assert np.max(np.abs(o2[0, t] - o0[0, t])) > 1e-3
+
+
+def test_batch_and_heads_are_independent():
+    q, k, v = (rnd((3, 20, 4, 64), s) for s in (43, 44, 45))
+    full = oracle.prefill(q, k, v, 6)
+    for b in range(3):
+        for h in range(4):
+            one = oracle.prefill(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1],
+                                 v[b:b + 1, :, h:h + 1], 6)
+            np.testing.assert_array_equal(one[0, :, 0], full[b, :, h])
+
+
+def test_bf16_contract_rounds_rotated_qk():
+    # bf16 mode = brute force on bf16-rounded complex-rotated q, k (v untouched).
+    T, H, D, W = 33, 2, 64, 9
+    q, k, v = (rnd((1, T, H, D), s) for s in (46, 47, 48))
+    pos = np.arange(T)
+    qr = oracle.bf16_round(complex_rope(q[0], pos))
+    kr = oracle.bf16_round(complex_rope(k[0], pos))
+    want = dense_band_attention(qr, kr, v[0], W)
+    got = oracle.prefill(q, k, v, W, bf16=True)[0]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # and it differs from the exact mode by about bf16 resolution, not more
+    exact = oracle.prefill(q, k, v, W)[0]
+    d = np.max(np.abs(got - exact))
+    assert 1e-6 < d < 0.05
+
+
+def test_rope_applied_skips_rotation():
+    q, k, v = (rnd((1, 12, 2, 64), s) for s in (49, 50, 51))
+    pos = np.arange(12)
+    qr, kr = complex_rope(q[0], pos)[None], complex_rope(k[0], pos)[None]
+    np.testing.assert_allclose(oracle.prefill(qr, kr, v, 5, rope_applied=True),
+                               oracle.prefill(q, k, v, 5), rtol=0, atol=1e-12)
+
+
+def test_thread_count_does_not_change_results():
+    q, k, v = (rnd((2, 70, 3, 64), s) for s in (52, 53, 54))
+    a = oracle.prefill(q, k, v, 25, nthreads=1)
+    b = oracle.prefill(q, k, v, 25, nthreads=4)
+    np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# streaming: ring of W slots, attend then append
+# --------------------------------------------------------------------------
+
+def run_stream(q, k, v, W, chunks, bf16=False, start_pos=0):
+    """Feed [1,T,H,D] frames through stream_step + ring_append in chunks."""
+    B, T, H, D = q.shape
+    S = 1
+    ring_k = np.zeros((S, H, W, D))
+    ring_v = np.zeros((S, H, W, D))
+    # fill the ring with garbage: slots for positions < 0 must never be read
+    ring_k[:] = 1e3
+    ring_v[:] = -1e3
+    pos = np.array([start_pos], dtype=np.int64)
+    out = np.zeros_like(q)
+    t = 0
+    ci = 0
+    while t < T:
+        n = min(chunks[ci % len(chunks)], T - t)
+        ci += 1
+        sl = slice(t, t + n)
+        o = oracle.stream_step(q[:, sl], k[:, sl], v[:, sl], ring_k, ring_v, pos, W, bf16=bf16)
+        oracle.ring_append(ring_k, ring_v, k[:, sl], v[:, sl], pos, W, bf16=bf16)
+        out[:, sl] = o
+        t += n
+    assert pos[0] == start_pos + T
+    return out, ring_k, ring_v
+
+
+@pytest.mark.parametrize("chunks", [[1], [3], [4], [7], [50], [4, 1, 7, 3]])
+def test_streaming_equals_prefill(chunks):
+    # Offline and streaming encoders compute the same thing: chunked streaming
+    # over a W-slot ring equals whole-sequence prefill, across ring wraps.
+    W, T, H, D = 50, 160, 2, 64
+    q, k, v = (rnd((1, T, H, D), s) for s in (60, 61, 62))
+    got, _, _ = run_stream(q, k, v, W, chunks)
+    np.testing.assert_allclose(got, oracle.prefill(q, k, v, W), rtol=0, atol=1e-12)
+
+
+def test_streaming_equals_prefill_chunk_equal_to_window():
+    W, T = 16, 70
+    q, k, v = (rnd((1, T, 2, 64), s) for s in (63, 64, 65))
+    got, _, _ = run_stream(q, k, v, W, [W])
+    np.testing.assert_allclose(got, oracle.prefill(q, k, v, W), rtol=0, atol=1e-12)
+
+
+def test_streaming_equals_prefill_bf16_contract():
+    W, T = 24, 90
+    q, k, v = (rnd((1, T, 2, 64), s) for s in (66, 67, 68))
+    got, _, _ = run_stream(q, k, v, W, [4], bf16=True)
+    np.testing.assert_allclose(got, oracle.prefill(q, k, v, W, bf16=True), rtol=0, atol=1e-12)
+
+
+def test_streaming_at_real_window_three_wraps():
+    W, T = 750, 3 * 750 + 13
+    q, k, v = (rnd((1, T, 1, 64), s, 0.5) for s in (69, 70, 71))
+    got, _, _ = run_stream(q, k, v, W, [4])
+    np.testing.assert_allclose(got, oracle.prefill(q, k, v, W), rtol=0, atol=1e-12)
+
+
+def test_ring_holds_rotated_keys_at_position_mod_w():
+    W, T, H = 8, 21, 2
+    q, k, v = (rnd((1, T, H, 64), s) for s in (72, 73, 74))
+    _, rk, rv = run_stream(q, k, v, W, [3], start_pos=5)
+    kr = complex_rope(k[0], np.arange(5, 5 + T))
+    for t in range(T - W, T):
+        p = 5 + t
+        np.testing.assert_allclose(rk[0, :, p % W], kr[t], atol=1e-12)
+        np.testing.assert_array_equal(rv[0, :, p % W], v[0, t])
+
+
+def test_stream_step_from_absolute_positions_matches_prefill_slice():
+    # A ring pre-filled with rotated keys of positions P-W..P-1 behaves like the
+    # tail of a prefill over positions P-W..P+n-1.
+    W, n, H, P = 30, 4, 2, 12345
+    T = W + n
+    q, k, v = (rnd((1, T, H, 64), s) for s in (75, 76, 77))
+    posv = np.arange(P - W, P + n)
+    kr = complex_rope(k[0], posv)
+    ring_k = np.zeros((1, H, W, 64))
+    ring_v = np.zeros((1, H, W, 64))
+    for t in range(W):
+        ring_k[0, :, posv[t] % W] = kr[t]
+        ring_v[0, :, posv[t] % W] = v[0, t]
+    o = oracle.stream_step(q[:, W:], k[:, W:], v[:, W:], ring_k, ring_v,
+                           np.array([P], np.int64), W)
+    want = oracle.prefill(q, k, v, W, pos=P - W)[:, W:]
+    np.testing.assert_allclose(o, want, rtol=0, atol=1e-9)
+
+
+def test_stream_snapshot_resume_is_identical():
+    W, T = 20, 60
+    q, k, v = (rnd((1, T, 2, 64), s) for s in (78, 79, 80))
+    a, rk, rv = run_stream(q[:, :30], k[:, :30], v[:, :30], W, [4])
+    # resume twice from the same snapshot
+    outs = []
+    for _ in range(2):
+        rk2, rv2, pos = rk.copy(), rv.copy(), np.array([30], np.int64)
+        o = oracle.stream_step(q[:, 30:34], k[:, 30:34], v[:, 30:34], rk2, rv2, pos, W)
+        outs.append(o)
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_stream_rejects_chunk_larger_than_window():
+    ring = np.zeros((1, 1, 4, 64))
+    x = np.zeros((1, 5, 1, 64))
+    with pytest.raises(ValueError):
+        oracle.stream_step(x, x, x, ring, ring, np.array([0], np.int64), 4)
+
+
+# --------------------------------------------------------------------------
+# constants the pages print
+# --------------------------------------------------------------------------
+
+def test_workload_constants_match_pages():
+    c = json.load(open(os.path.join(GOLDEN, "voxtral_realtime_constants.json")))
+    W = c["encoder_window_frames"]["value"]
+    for name in ("layer", "stack", "long", "stream"):
+        cfg = synth.CONFIGS[name]
+        assert cfg.W == W
+        assert cfg.theta == c["encoder_rope_theta"]["value"]
+        assert cfg.D == c["encoder_head_dim"]["value"]
+        assert cfg.H == c["encoder_heads"]["value"]
+    assert synth.CONFIGS["stream"].n == c["encoder_frames_per_step"]["value"]
+    # 30 s of audio at 16 kHz / hop 160 / stride 2 = 1500 encoder frames
+    frames = 30 * c["sample_rate_hz"]["value"] // c["mel_hop"]["value"] // c["conv2_stride"]["value"]
+    assert frames == synth.CONFIGS["layer"].T == 1500
+    assert c["mel_frames_per_audio_token"]["value"] // c["conv2_stride"]["value"] == 4
+
+
+def test_oracle_regression_record_tiny():
+    # Written by tests/golden/make_oracle_golden.py (oracle only); guards
+    # against unintended changes of the oracle's arithmetic.
+    rec = json.load(open(os.path.join(GOLDEN, "oracle_tiny.json")))
+    c = synth.CONFIGS["tiny"]
+    x = synth.make_config("tiny")
+    assert {k: synth.sha256(x[k]) for k in ("q", "k", "v")} == rec["input_sha256"]
+    o = oracle.prefill(x["q"], x["k"], x["v"], c.W, theta=c.theta)
+    assert abs(o.sum() - rec["sum"]) < 1e-9
+    assert abs((o * o).sum() - rec["sum_sq"]) < 1e-9
+    for key, val in rec["samples"].items():
+        t, h, d = map(int, key.split(","))
+        assert abs(o[0, t, h, d] - val) < 1e-12
