@@ -1,0 +1,265 @@
+"""Benchmark: sliding-window (W=750) RoPE attention on one MI355X.
+
+One step = the whole hot path on synthetic inputs already resident in HBM:
+  * prefill of one encoder layer's attention, B1 T1500 H32 D64, bf16 in and
+    out, RoPE fused into the tile loads (cos/sin table built once, outside the
+    timed region, like any RoPE cache);
+  * one batched streaming step, 64 streams x 4 new frames, H32 D64, 750-slot
+    bf16 rings: vx_swa_attn_stream_step then vx_kv_ring_append.
+Positions advance 4 per step; two ring sets alternate so the working set
+(786 MB) exceeds the 256 MB last-level cache; new frames cycle through 8
+pre-drawn batches.
+
+Printed value: prefill TFLOP/s over the unmasked band FLOPs
+(4*64*pairs*H*B, pairs = W(W+1)/2 + (T-W)W), from HIP events around
+back-to-back launches on the launch stream.  The streaming step is reported
+in microseconds and GB/s of algorithmic HBM bytes.  The CPU baseline is the
+float64 oracle timed on the host on the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def band_flops(B, T, H, W, D=64):
+    from sliding_window_attention_vx_amd.synth import band_pairs
+    return 4.0 * D * band_pairs(T, W) * H * B
+
+
+def stream_bytes(S, n, H, W, D=64, elem=2):
+    """Algorithmic HBM bytes of one streaming step (attend + append).
+
+    Per (stream, head): the ring keys and values the queries need (W-1 slots
+    each, since the oldest slot's frame has left every query's window once
+    the new frames arrive), the new q, k, v rows, the output rows, and the
+    appended k and v rows; plus pos read and written per stream.
+    """
+    row = D * elem
+    per_sh = 2 * (W - 1) * row + 3 * n * row + n * row + 2 * n * row
+    return S * H * per_sh + S * 16
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=10,
+                    help="oracle repetitions of the prefill workload for the CPU baseline")
+    ap.add_argument("--only", choices=["prefill", "stream", "copy"], default=None,
+                    help="profiling aid: launch only this kernel (or a plain device copy of "
+                         "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the work shards by batch, head or stream with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sliding_window_attention_vx_amd as vx
+    from sliding_window_attention_vx_amd import synth
+
+    if not os.path.exists(vx.LIB_PATH):
+        from sliding_window_attention_vx_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.only == "copy":
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e_.record()
+        torch.cuda.synchronize()
+        us = s_.elapsed_time(e_) * 1e3 / args.steps
+        print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "us": round(us, 2),
+                          "GBps_read_plus_write": round(2 * n / us / 1e3, 1)}))
+        return
+
+    def to(x, dt=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
+
+    # ---- prefill workload: one encoder layer, T=1500
+    pc = synth.CONFIGS["layer"]
+    x = synth.make_config("layer")
+    q, k, v = to(x["q"]), to(x["k"]), to(x["v"])
+    o = torch.empty_like(q)
+    table = vx.rope_table(0, pc.T)
+    flops = band_flops(pc.B, pc.T, pc.H, pc.W)
+
+    # ---- streaming workload
+    sc = synth.CONFIGS["stream"]
+    rings = []
+    for r in range(2):
+        st = synth.make_stream_state(sc.S, sc.H, sc.W, seed=[sc.seed, r], pos_lo=sc.pos_lo,
+                                     pos_hi=sc.pos_hi)
+        rings.append((to(st["ring_k"]), to(st["ring_v"]),
+                      torch.from_numpy(st["pos"].copy()).to(dev)))
+    frames = []
+    for i in range(8):
+        fr = synth.make_stream_frames(sc.S, sc.n, sc.H, seed=sc.seed, step=i)
+        frames.append((to(fr["q"]), to(fr["k"]), to(fr["v"])))
+    so = torch.empty_like(frames[0][0])
+    sbytes = stream_bytes(sc.S, sc.n, sc.H, sc.W)
+
+    def prefill():
+        vx.prefill(q, k, v, window=pc.W, table=table, out=o)
+
+    def stream(i):
+        rk, rv, pos = rings[i % 2]
+        qn, kn, vn = frames[i % 8]
+        vx.stream_step(qn, kn, vn, rk, rv, pos, window=sc.W, out=so)
+        return rk, rv, pos, kn, vn
+
+    def append(args_):
+        rk, rv, pos, kn, vn = args_
+        vx.ring_append(rk, rv, kn, vn, pos, window=sc.W)
+
+    def step(i):
+        prefill()
+        append(stream(i))
+
+    if args.only is not None:
+        fn = (lambda j: prefill()) if args.only == "prefill" else (lambda j: append(stream(j)))
+        for j in range(args.warmup):
+            fn(j)
+        torch.cuda.synchronize()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for j in range(args.steps):
+            fn(j)
+        e_.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "us_per_launch": round(s_.elapsed_time(e_) * 1e3 /
+                                                                     args.steps, 3)}))
+        return
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, with per-kernel events on the launch stream
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = evs[i]
+        e[0].record()
+        prefill()
+        e[1].record()
+        a = stream(args.warmup + i)
+        e[2].record()
+        append(a)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / K
+    pre_in_step = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    str_in_step = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    app_in_step = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+
+    # ---- per-kernel average launch duration: back-to-back launches between two events
+    def per_launch_us(fn, reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for j in range(reps):
+            fn(j)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / reps
+
+    reps = max(K, 20)
+    pre_us = per_launch_us(lambda j: prefill(), reps)
+    stream_us = per_launch_us(lambda j: stream(j), reps)
+    step_us = per_launch_us(lambda j: append(stream(j)), reps)
+
+    tflops = flops / (pre_us * 1e-6) / 1e12
+    stream_gbs = sbytes / (stream_us * 1e-6) / 1e9
+
+    out = {
+        "metric": "SWA-750 attention TFLOP/s (T=1500, 32h x 64, bf16) + streaming step us",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill B1 T1500 H32 D64 W750 bf16 (RoPE theta 1e6 fused) + streaming "
+                        "step S64 n4 H32 D64 W750 bf16 (attend + ring append)",
+            "global_batch": pc.B,
+            "seq_len": pc.T,
+            "parallelism": "none (one GPU)",
+        },
+        "prefill_us": round(pre_us, 3),
+        "stream_step_us": round(step_us, 3),
+        "stream_attend_us": round(stream_us, 3),
+        "in_step_event_us": {"prefill": round(pre_in_step, 3), "stream_attend": round(str_in_step, 3),
+                             "ring_append": round(app_in_step, 3)},
+        "roofline": {
+            "kernel": "prefill_mfma_kernel",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "roofline_stream": {
+            "kernel": "stream_step_kernel",
+            "bound": "hbm",
+            "achieved": round(stream_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        for _ in range(args.cpu_reps):
+            oracle.prefill(x["q"], x["k"], x["v"], pc.W, bf16=True, nthreads=nt)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(flops * args.cpu_reps / cpu_s / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": nt,
+            "kind": "oracle",
+            "sample": f"float64 oracle (bf16 contract), the full prefill workload B1 T1500 H32 "
+                      f"W750 x {args.cpu_reps} repetitions, {cpu_s:.1f} s on {nt} threads",
+        }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * vx.h - C ABI of the MI355X (gfx950) sliding-window RoPE attention library.
+ *
+ * The operation is the self-attention of the Voxtral Realtime 2602 audio
+ * encoder (transcribe.cpp "Voxtral" family notes, section Architecture,
+ * Voxtral Realtime 2602): causal attention of each encoder frame over the
+ * most recent W = 750 frames including itself, 32 heads of head_dim 64, with
+ * rotary position embedding (RoPE, theta = 1e6) on queries and keys.  It comes
+ * in two forms:
+ *   - prefill: a whole chunk in one call (the Core AI port's batched
+ *     first-chunk encoder, "Voxtral Mini 4B Realtime - Core AI", section
+ *     "Why two encoders?");
+ *   - streaming: 4 new encoder frames per step (same family notes, Streaming
+ *     schedule: 8 mel frames = 4 encoder frames = one 80 ms audio token),
+ *     attending to a W-slot ring of past rotated keys and values.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, frees nothing and keeps no pointer after a call
+ *     returns.  It holds no state and may be called from several host
+ *     threads at once.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and never synchronise; a fault in a
+ *     kernel surfaces at the caller's next synchronising HIP call.
+ *   - Layouts are dense row-major: activations [B,T,H,D] (D fastest), rings
+ *     [S,H,W,D].  D (head_dim) must be 64.
+ *   - Every argument is checked on the host before anything is launched.  On
+ *     any error nothing is launched and no buffer is touched; the status
+ *     says why and vx_last_error() gives a message (thread-local).  A failed
+ *     kernel launch returns VX_E_HIP.
+ *   - Empty work (B == 0, T == 0 or S == 0) returns VX_OK without launching.
+ *   - RoPE pairs dimension i with i + D/2 (half-split) and turns the pair by
+ *     angle position * theta^(-2i/D); the angle is formed in float64 and its
+ *     cosine and sine rounded to float32; the rotation itself is float32 and
+ *     the rotated value is rounded to the storage dtype (nearest-even).
+ */
+#ifndef VX_H
+#define VX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VX_OK = 0,
+  VX_E_NULL = 1,   /* a required pointer is NULL */
+  VX_E_SHAPE = 2,  /* a size is negative, zero where it must not be, or too large */
+  VX_E_DTYPE = 3,  /* unsupported dtype or dtype pair */
+  VX_E_ALIGN = 4,  /* a tensor pointer is not 16-byte aligned */
+  VX_E_RANGE = 5,  /* a value is out of range (window, theta, scale, n > W, positions, table) */
+  VX_E_HIP = 6     /* the HIP runtime reported an error when launching */
+} vx_status;
+
+typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
+
+/* Flags for vx_attn_cfg.flags. */
+#define VX_FLAG_VALU_KERNEL 1u /* prefill: use the float32 vector-ALU kernel instead of the
+                                  bf16 matrix-core kernel (a cross-check; bf16 inputs still
+                                  get bf16-rounded rotated q and k) */
+
+typedef struct {
+  int32_t head_dim;      /* must be 64                                              */
+  int32_t window;        /* W >= 1 (750 for the Voxtral Realtime encoder)           */
+  double rope_theta;     /* > 0 (1e6)                                               */
+  float softmax_scale;   /* >= 0; 0 means 1/sqrt(head_dim)                          */
+  int32_t io_dtype;      /* vx_dtype of q, k, v and of the rings                    */
+  int32_t out_dtype;     /* vx_dtype of o; pairs: bf16->bf16, bf16->f32, f32->f32   */
+  uint32_t flags;        /* VX_FLAG_* bits, 0 by default                            */
+} vx_attn_cfg;
+
+/* Fills `cfg` with the Voxtral Realtime encoder defaults: head_dim 64,
+ * window 750, theta 1e6, scale 1/8, bf16 in and out, no flags. */
+void vx_default_cfg(vx_attn_cfg *cfg);
+
+/* RoPE cosine/sine table for `count` consecutive positions starting at
+ * `p_begin` (>= 0).  table: device float32 [count][2][head_dim/2]:
+ * table[j][0][i] = cos((p_begin+j) * theta^(-2i/D)), table[j][1][i] = sin(...).
+ * Only cfg->head_dim and cfg->rope_theta are read.  The table depends on
+ * nothing else, so one table serves every layer and call that uses these
+ * positions. */
+vx_status vx_rope_table(float *table, int64_t p_begin, int32_t count, const vx_attn_cfg *cfg,
+                        void *stream);
+
+/* In-place RoPE of q and k, both [B,T,H,D] of cfg->io_dtype; row t of every
+ * batch entry sits at absolute position pos0 + t (pos0 >= 0).  Either q or k
+ * may be NULL (not both).  V is never rotated. */
+vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, int64_t pos0,
+                     const vx_attn_cfg *cfg, void *stream);
+
+/* Causal sliding-window attention over whole chunks (no history):
+ *   o[b,t,h] = sum_j softmax_j(scale * q'[b,t,h] . k'[b,j,h]) v[b,j,h],
+ *   j = max(0, t-W+1) .. t,
+ * where q', k' are q, k rotated at positions pos0 + t (pos0 >= 0).
+ * q, k, v: [B,T,H,D] cfg->io_dtype; o: [B,T,H,D] cfg->out_dtype (must not
+ * alias the inputs).
+ * rope_applied != 0: q and k are already rotated; `rope_table` is ignored.
+ * rope_applied == 0: the kernel rotates q and k as it loads them, reading
+ *   cos/sin from `rope_table` (made by vx_rope_table) which covers positions
+ *   table_p0 .. table_p0 + table_len - 1; those must include
+ *   pos0 .. pos0 + T - 1, else VX_E_RANGE. */
+vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
+                              int32_t T, int32_t H, int64_t pos0, int32_t rope_applied,
+                              const float *rope_table, int64_t table_p0, int64_t table_len,
+                              const vx_attn_cfg *cfg, void *stream);
+
+/* One streaming step for S independent streams with n new frames each
+ * (1 <= n <= min(W, 64); a longer first chunk goes through the prefill).
+ * q_new, k_new, v_new, o: [S,n,H,D]; ring_k (rotated keys) and ring_v: [S,H,W,D] in cfg->io_dtype; slot j of a ring holds the frame at
+ * absolute position p with p mod W == j.  pos: device int64 [S], the absolute
+ * position of the first new frame of each stream (= frames appended so far;
+ * a stream starts at 0 with any ring contents, since slots of positions < 0
+ * are never read; negative values count as 0 history).  New query i of
+ * stream s (position P = pos[s] + i) attends to ring frames at positions
+ * max(0, P-W+1) .. pos[s]-1 and to new frames pos[s] .. P.  New q and k are
+ * rotated here unless rope_applied != 0.  Reads the ring and pos, never
+ * writes them: call vx_kv_ring_append afterwards, on the same stream. */
+vx_status vx_swa_attn_stream_step(const void *q_new, const void *k_new, const void *v_new,
+                                  const void *ring_k, const void *ring_v, const int64_t *pos,
+                                  void *o, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
+                                  const vx_attn_cfg *cfg, void *stream);
+
+/* Appends n new frames per stream: rotates k_new (unless rope_applied != 0)
+ * at positions pos[s] + i, writes it and v_new to slot (pos[s] + i) mod W of
+ * ring_k / ring_v, then sets pos[s] += n on the device.  Shapes and dtypes as
+ * in vx_swa_attn_stream_step.  Must follow every read of the ring for this
+ * step (same stream): the slots it overwrites still hold keys that the
+ * step's queries need. */
+vx_status vx_kv_ring_append(void *ring_k, void *ring_v, const void *k_new, const void *v_new,
+                            int64_t *pos, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
+                            const vx_attn_cfg *cfg, void *stream);
+
+/* Static description of a status code. */
+const char *vx_status_string(vx_status s);
+
+/* Message for the last non-OK status returned on the calling thread
+ * ("" if none).  Valid until the next vx_* call on this thread. */
+const char *vx_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t vx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VX_H */

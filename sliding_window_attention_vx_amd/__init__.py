@@ -1,0 +1,249 @@
+"""Sliding-window RoPE attention for MI355X (gfx950): Python binding of libvx.
+
+Causal attention of each frame over the last `window` frames (itself
+included) with half-split RoPE on queries and keys -- the self-attention of
+the Voxtral Realtime 2602 audio encoder (W = 750, 32 heads x 64, theta 1e6;
+transcribe.cpp "Voxtral" family notes, section Architecture).  Every call
+marshals torch tensors into the C ABI of include/vx.h; all arithmetic runs in
+the HIP kernels of libvx.so.  PyTorch only provides device memory and
+streams.  There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
+    "WINDOW", "THETA", "HEAD_DIM",
+]
+
+WINDOW = 750
+THETA = 1e6
+HEAD_DIM = 64
+
+VX_F32, VX_BF16 = 0, 1
+VX_FLAG_VALU_KERNEL = 1
+_STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported dtype",
+           4: "misaligned pointer", 5: "value out of range", 6: "HIP runtime error"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvx.so")
+
+
+class VxError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        self.status = status
+        super().__init__(f"{func}: {_STATUS.get(status, status)}: {msg}")
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_SIGS = {
+    "vx_default_cfg": (None, [ctypes.POINTER(_Cfg)]),
+    "vx_rope_table": (ctypes.c_int, [_vp, _i64, _i32, ctypes.POINTER(_Cfg), _vp]),
+    "vx_rope_qk": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i64, ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp,
+                                           _i64, _i64, ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                               _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
+    "vx_kv_ring_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         ctypes.POINTER(_Cfg), _vp]),
+    "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "vx_last_error": (ctypes.c_char_p, []),
+    "vx_version": (_i32, []),
+}
+_lib = None
+
+
+def lib():
+    """The loaded libvx.so (ctypes).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sliding_window_attention_vx_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+class Config:
+    """Attention parameters (mirrors vx_attn_cfg)."""
+
+    def __init__(self, window=WINDOW, theta=THETA, scale=0.0, io_dtype="bf16", out_dtype=None,
+                 valu=False):
+        self.window = int(window)
+        self.theta = float(theta)
+        self.scale = float(scale)
+        self.io_dtype = io_dtype
+        self.out_dtype = out_dtype or io_dtype
+        self.valu = bool(valu)
+
+    def c(self):
+        d = {"bf16": VX_BF16, "f32": VX_F32}
+        return _Cfg(HEAD_DIM, self.window, self.theta, self.scale, d[self.io_dtype],
+                    d[self.out_dtype], VX_FLAG_VALU_KERNEL if self.valu else 0)
+
+
+def _check(status, func):
+    if status != 0:
+        raise VxError(status, func, lib().vx_last_error().decode())
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def rope_table(p_begin, count, theta=THETA, device="cuda", out=None):
+    """cos/sin table [count, 2, 32] float32 for positions p_begin .. p_begin+count-1."""
+    import torch
+    if out is None:
+        out = torch.empty((count, 2, HEAD_DIM // 2), dtype=torch.float32, device=device)
+    _dev_tensor(out, "out")
+    cfg = Config(theta=theta).c()
+    _check(lib().vx_rope_table(_ptr(out), int(p_begin), int(count), ctypes.byref(cfg),
+                               _stream(out)), "vx_rope_table")
+    return out
+
+
+def rope_qk(q, k, pos0=0, theta=THETA):
+    """Rotate q and k [B,T,H,64] in place (either may be None)."""
+    t = q if q is not None else k
+    for name, x in (("q", q), ("k", k)):
+        if x is not None:
+            _dev_tensor(x, name)
+            if x.shape != t.shape or x.dtype != t.dtype:
+                raise ValueError("q and k must have the same shape and dtype")
+    if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
+        raise ValueError("expected [B, T, H, 64]")
+    B, T, H, _ = t.shape
+    cfg = Config(theta=theta, io_dtype=_dt(t)).c()
+    _check(lib().vx_rope_qk(_ptr(q), _ptr(k), B, T, H, int(pos0), ctypes.byref(cfg), _stream(t)),
+           "vx_rope_qk")
+
+
+def prefill(q, k, v, window=WINDOW, pos0=0, theta=THETA, scale=0.0, rope_applied=False,
+            table=None, table_p0=0, out=None, out_dtype=None, valu=False):
+    """Causal sliding-window attention over whole chunks; q,k,v [B,T,H,64] -> o [B,T,H,64].
+
+    With rope_applied=False the kernel rotates q and k using `table` (from
+    rope_table, covering positions pos0..pos0+T-1 starting at table_p0); if no
+    table is given one is made for exactly those positions.
+    """
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(x, name)
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError("q, k, v must all be [B, T, H, 64]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, T, H, _ = q.shape
+    io = _dt(q)
+    od = out_dtype or (_dt(out) if out is not None else io)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q.device)
+    _dev_tensor(out, "out")
+    if out.shape != q.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
+    tlen = 0
+    if not rope_applied:
+        if table is None:
+            table = rope_table(pos0, T, theta, device=q.device)
+            table_p0 = pos0
+        _dev_tensor(table, "table")
+        tlen = table.shape[0]
+    cfg = Config(window, theta, scale, io, od, valu).c()
+    _check(lib().vx_swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, int(pos0),
+                                     int(bool(rope_applied)), _ptr(table), int(table_p0), int(tlen),
+                                     ctypes.byref(cfg), _stream(q)), "vx_swa_attn_prefill")
+    return out
+
+
+def _stream_shapes(q_new, ring_k, ring_v, pos, window):
+    if q_new.dim() != 4 or q_new.shape[-1] != HEAD_DIM:
+        raise ValueError("new frames must be [S, n, H, 64]")
+    S, n, H, _ = q_new.shape
+    if ring_k.shape != (S, H, window, HEAD_DIM) or ring_v.shape != ring_k.shape:
+        raise ValueError(f"rings must be [S, H, W, 64] = {(S, H, window, HEAD_DIM)}")
+    import torch
+    if pos.dtype != torch.int64 or pos.shape != (S,):
+        raise ValueError("pos must be int64 [S]")
+    return S, n, H
+
+
+def stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, window=WINDOW, theta=THETA, scale=0.0,
+                rope_applied=False, out=None, out_dtype=None):
+    """One streaming step (reads the rings and pos, writes o [S,n,H,64])."""
+    import torch
+    for name, x in (("q_new", q_new), ("k_new", k_new), ("v_new", v_new), ("ring_k", ring_k),
+                    ("ring_v", ring_v), ("pos", pos)):
+        _dev_tensor(x, name)
+    S, n, H = _stream_shapes(q_new, ring_k, ring_v, pos, window)
+    if k_new.shape != q_new.shape or v_new.shape != q_new.shape:
+        raise ValueError("q_new, k_new, v_new must have the same shape")
+    io = _dt(q_new)
+    if any(_dt(x) != io for x in (k_new, v_new, ring_k, ring_v)):
+        raise ValueError("new frames and rings must share a dtype")
+    od = out_dtype or (_dt(out) if out is not None else io)
+    if out is None:
+        out = torch.empty(q_new.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q_new.device)
+    _dev_tensor(out, "out")
+    cfg = Config(window, theta, scale, io, od).c()
+    _check(lib().vx_swa_attn_stream_step(_ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k),
+                                         _ptr(ring_v), _ptr(pos), _ptr(out), S, n, H,
+                                         int(bool(rope_applied)), ctypes.byref(cfg),
+                                         _stream(q_new)), "vx_swa_attn_stream_step")
+    return out
+
+
+def ring_append(ring_k, ring_v, k_new, v_new, pos, window=WINDOW, theta=THETA, rope_applied=False):
+    """Append the new frames to the rings in place and advance pos by n."""
+    for name, x in (("k_new", k_new), ("v_new", v_new), ("ring_k", ring_k), ("ring_v", ring_v),
+                    ("pos", pos)):
+        _dev_tensor(x, name)
+    S, n, H = _stream_shapes(k_new, ring_k, ring_v, pos, window)
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    io = _dt(k_new)
+    cfg = Config(window, theta, 0.0, io, io).c()
+    _check(lib().vx_kv_ring_append(_ptr(ring_k), _ptr(ring_v), _ptr(k_new), _ptr(v_new), _ptr(pos),
+                                   S, n, H, int(bool(rope_applied)), ctypes.byref(cfg),
+                                   _stream(k_new)), "vx_kv_ring_append")

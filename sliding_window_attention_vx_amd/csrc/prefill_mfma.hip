@@ -1,0 +1,372 @@
+// Causal sliding-window prefill with RoPE on bf16 matrix cores (gfx950).
+//
+// Work unit: one workgroup = NW waves for one (batch, head) and a tile of
+// BM = 32*NW consecutive queries; wave w owns queries qw .. qw+31.  The
+// workgroup walks the 64-key tiles that intersect the band
+// [q0-W+1, q0+BM-1] (banded tile skipping: tiles outside it are never
+// loaded), and each wave skips the 32-key halves that lie outside its own
+// band and masks only the halves that straddle a band edge.
+//
+// Per 32-key half and wave (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   S^T = K' Q'^T  : A = K' rows from LDS (16 B per lane), B = Q' in registers.
+//                    Lane l holds the scores of query l%32 for 16 keys, so
+//                    the row max is an in-register max and one swap with
+//                    lane l^32.
+//   P^T = exp2(S^T * scale*log2e - m)  (lazy max: m moves only when a
+//                    score exceeds it by more than 8, so p <= 256)
+//   O^T += V^T P^T : B = P^T straight from the score registers (bf16);
+//                    A = V^T from LDS, where V was written transposed with
+//                    the key order permuted (bits 2 and 3 of the key index
+//                    swapped) so that each lane's eight keys are one 16-byte
+//                    LDS read matching the score register layout.
+// RoPE is fused into the loads: each lane rotates its own Q' row halves
+// (pairs (i, i+32) are lane-local) and the staging threads rotate each K
+// tile once per workgroup, reading cos/sin from the float32 table; rotated
+// values are rounded to bf16 (the storage type of a rotated tensor).
+// LDS rows are 144 bytes (128 + 16 pad) so that 16-byte reads of 32
+// consecutive rows hit distinct banks.  K/V staging is double buffered:
+// the next tile's global loads are issued before the current tile's MFMAs.
+#include "vx_launch.h"
+
+namespace vx {
+
+namespace {
+
+constexpr int kBN = 64;                    // keys per staged tile
+constexpr int kRow = 144;                  // LDS bytes per row
+constexpr int kTileBytes = 64 * kRow;      // one K' tile or one V^T tile
+constexpr float kLazy = 8.0f;              // log2-domain slack of the running max
+
+__device__ __forceinline__ int vt_phys(int kk) {
+  // key index inside a 64-key tile -> column in the V^T row (bits 2 and 3 swapped)
+  return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+template <int NW>
+struct Stage {
+  static constexpr int NT = NW * 64;
+  static constexpr int UK = 256 / NT;  // K units per thread (row, chunk pair)
+  static constexpr int UV = 256 / NT;  // V units per thread (row pair, chunk)
+  u32x4 kx[UK], ky[UK];
+  float kc[UK][8], ks[UK][8];
+  u32x4 v0[UV], v1[UV];
+};
+
+template <int NW>
+__device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
+                                           const bf16* __restrict__ v, size_t rs, int T, int kt0,
+                                           bool rope, const float* __restrict__ table,
+                                           int64_t row0, int tid) {
+  constexpr int NT = Stage<NW>::NT;
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UK; ++j) {
+    const int u = tid + j * NT;
+    const int r = u >> 2, cp = u & 3;
+    const int key = kt0 + r;
+    if (key < T) {
+      const bf16* kp = k + (size_t)key * rs + 8 * cp;
+      st.kx[j] = *reinterpret_cast<const u32x4*>(kp);
+      st.ky[j] = *reinterpret_cast<const u32x4*>(kp + kHalf);
+      if (rope) {
+        const float* cs = table + (row0 + key) * kD + 8 * cp;
+        load8(cs, st.kc[j]);
+        load8(cs + kHalf, st.ks[j]);
+      }
+    } else {
+      st.kx[j] = u32x4{0, 0, 0, 0};
+      st.ky[j] = u32x4{0, 0, 0, 0};
+      if (rope) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          st.kc[j][e] = 1.f;
+          st.ks[j][e] = 0.f;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UV; ++j) {
+    const int u = tid + j * NT;
+    const int rp = u & 31, c = u >> 5;
+    const int key = kt0 + 2 * rp;
+    const u32x4 zero = {0, 0, 0, 0};
+    st.v0[j] = key < T ? *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c) : zero;
+    st.v1[j] = key + 1 < T ? *reinterpret_cast<const u32x4*>(v + (size_t)(key + 1) * rs + 8 * c)
+                           : zero;
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char* Vb, bool rope,
+                                             int tid) {
+  constexpr int NT = Stage<NW>::NT;
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UK; ++j) {
+    const int u = tid + j * NT;
+    const int r = u >> 2, cp = u & 3;
+    u32x4 x = st.kx[j], y = st.ky[j];
+    if (rope) {
+      float xf[8], yf[8];
+      unpack8(st.kx[j], xf);
+      unpack8(st.ky[j], yf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float xo, yo;
+        rope_pair(xf[e], yf[e], st.kc[j][e], st.ks[j][e], &xo, &yo);
+        xf[e] = xo;
+        yf[e] = yo;
+      }
+      x = pack8(xf);
+      y = pack8(yf);
+    }
+    *reinterpret_cast<u32x4*>(Kb + r * kRow + 16 * cp) = x;
+    *reinterpret_cast<u32x4*>(Kb + r * kRow + 64 + 16 * cp) = y;
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UV; ++j) {
+    const int u = tid + j * NT;
+    const int rp = u & 31, c = u >> 5;
+    const int col = vt_phys(2 * rp);  // even; the pair (2rp, 2rp+1) stays adjacent
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a0 = st.v0[j][i], a1 = st.v1[j][i];
+      // dims 8c+2i and 8c+2i+1: (key 2rp, key 2rp+1) pairs
+      *reinterpret_cast<uint32_t*>(Vb + (8 * c + 2 * i) * kRow + 2 * col) =
+          (a0 & 0xffffu) | (a1 << 16);
+      *reinterpret_cast<uint32_t*>(Vb + (8 * c + 2 * i + 1) * kRow + 2 * col) =
+          (a0 >> 16) | (a1 & 0xffff0000u);
+    }
+  }
+}
+
+template <int NW, typename TO>
+__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
+                                                               int n_logical) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];
+  constexpr int BM = NW * 32;
+
+  // XCD-aware order: the grid is a multiple of 8 and the dispatcher deals
+  // workgroups round-robin to the 8 XCDs; give each XCD a contiguous run of
+  // query tiles of the same (batch, head) so neighbouring tiles share K/V in
+  // that XCD's L2.
+  const int per_xcd = gridDim.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= n_logical) return;
+  const int qt = logical % n_qtiles;
+  const int bh = logical / n_qtiles;
+  const int h = bh % a.H, b = bh / a.H;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int T = a.T, W = a.W;
+  const size_t rs = (size_t)a.H * kD;
+  const size_t base = (size_t)b * T * rs + (size_t)h * kD;
+  const bf16* __restrict__ q = (const bf16*)a.q + base;
+  const bf16* __restrict__ k = (const bf16*)a.k + base;
+  const bf16* __restrict__ v = (const bf16*)a.v + base;
+  TO* __restrict__ o = (TO*)a.o + base;
+  const bool rope = a.rope;
+
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;
+  const int tq = qw + l32;  // this lane's query
+
+  // ---- Q' fragments (B operand of S^T = K' Q'^T) -------------------------
+  // MFMA step m covers dims 16m .. 16m+15; lane half hh holds dims 16m+8hh+(0..7),
+  // i.e. chunk 2m+hh of 8 dims.  Chunks c and c+4 are RoPE partners.
+  bf16x8 qf[4];
+  if (tq < T) {
+    const bf16* qp = q + (size_t)tq * rs;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int c = 2 * pr + hh;
+      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * c);
+      u32x4 y = *reinterpret_cast<const u32x4*>(qp + kHalf + 8 * c);
+      if (rope) {
+        const float* cs = a.table + (a.table_row0 + tq) * kD + 8 * c;
+        float cc[8], ss[8], xf[8], yf[8];
+        load8(cs, cc);
+        load8(cs + kHalf, ss);
+        unpack8(x, xf);
+        unpack8(y, yf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float xo, yo;
+          rope_pair(xf[e], yf[e], cc[e], ss[e], &xo, &yo);
+          xf[e] = xo;
+          yf[e] = yo;
+        }
+        x = pack8(xf);
+        y = pack8(yf);
+      }
+      qf[pr] = __builtin_bit_cast(bf16x8, x);
+      qf[pr + 2] = __builtin_bit_cast(bf16x8, y);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qf[m] = bf16x8{};
+  }
+
+  f32x16 oacc[2];
+  oacc[0] = f32x16{};
+  oacc[1] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  const int kbeg = max(0, q0 - W + 1);
+  const int klast = min(T, q0 + BM) - 1;
+  const int it0 = kbeg / kBN, it1 = klast / kBN;
+
+  Stage<NW> st;
+  stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
+  stage_commit<NW>(st, lds, lds + kTileBytes, rope, tid);
+  __syncthreads();
+
+  for (int it = it0; it <= it1; ++it) {
+    const int buf = (it - it0) & 1;
+    const bool more = it < it1;
+    if (more) stage_load<NW>(st, k, v, rs, T, (it + 1) * kBN, rope, a.table, a.table_row0, tid);
+
+    const char* Kb = lds + buf * 2 * kTileBytes;
+    const char* Vb = Kb + kTileBytes;
+    const int kt0 = it * kBN;
+
+    bool act[2], msk[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb = kt0 + 32 * sb;
+      act[sb] = (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
+      msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
+    }
+    if (act[0] || act[1]) {
+      float x[2][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (!act[sb]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[sb][r] = -INFINITY;
+          continue;
+        }
+        f32x16 s = f32x16{};
+        const char* kr = Kb + (32 * sb + l32) * kRow + 16 * hh;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * m);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], s, 0, 0, 0);
+        }
+        const int kb = kt0 + 32 * sb + 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float val = s[r] * c2;
+          if (msk[sb]) {
+            const int key = kb + 8 * (r >> 2) + (r & 3);
+            if (key > tq || key < tq - W + 1) val = -INFINITY;
+          }
+          x[sb][r] = val;
+          mx = fmaxf(mx, val);
+        }
+      }
+      mx = fmaxf(mx, xor32(mx));
+      const bool need = mx > m_run + kLazy;
+      if (__any(need)) {
+        const float m_new = need ? mx : m_run;
+        // a lane whose keys were all masked so far has nothing to rescale
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          oacc[0][r] *= alpha;
+          oacc[1][r] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (!act[sb]) continue;
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(x[sb][r] - mu);
+          l_run += pr[r];
+        }
+        bf16x8 pf[2];
+        pf[0] = __builtin_bit_cast(bf16x8, pack8(pr));
+        pf[1] = __builtin_bit_cast(bf16x8, pack8(pr + 8));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+                Vb + (32 * db + l32) * kRow + 64 * sb + 32 * ks + 16 * hh);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (more) stage_commit<NW>(st, lds + (buf ^ 1) * 2 * kTileBytes,
+                               lds + (buf ^ 1) * 2 * kTileBytes + kTileBytes, rope, tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, lane holds query tq, dims 32db + 8g + 4hh + (0..3)
+  const float l_tot = l_run + xor32(l_run);
+  if (tq < T) {
+    const float inv = 1.f / l_tot;
+    TO* op = o + (size_t)tq * rs;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hh;
+        if constexpr (sizeof(TO) == 2) {
+          uint2 w;
+          w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+          w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d0) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(op + d0) = w;
+        }
+      }
+    }
+  }
+}
+
+template <int NW>
+hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
+  constexpr int BM = NW * 32;
+  const int n_qtiles = (a.T + BM - 1) / BM;
+  const int64_t n_logical = (int64_t)n_qtiles * a.H * a.B;
+  const int64_t grid = (n_logical + 7) / 8 * 8;
+  if (out == DT::BF16)
+    hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
+                       a, n_qtiles, (int)n_logical);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<NW, float>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       st, a, n_qtiles, (int)n_logical);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st) {
+  // Four-wave workgroups share each staged (and rotated) K tile among more
+  // queries; two-wave ones keep enough workgroups to cover the 256 CUs when
+  // the problem is small.
+  const int64_t wg4 = (int64_t)((a.T + 127) / 128) * a.H * a.B;
+  if (wg4 >= 256) return launch_nw<4>(a, out, st);
+  return launch_nw<2>(a, out, st);
+}
+
+}  // namespace vx

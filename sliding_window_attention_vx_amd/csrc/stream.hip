@@ -1,0 +1,394 @@
+// Streaming step over a W-slot KV ring, and the ring append.
+//
+// Schedule from the transcribe.cpp "Voxtral" family notes (Streaming
+// schedule): each step brings 4 encoder frames per stream.  A step is HBM
+// bound: every (stream, head) reads its whole ring of rotated keys and
+// values once (2 x W x 128 B in bf16) for only a handful of queries.
+//
+// stream_step_kernel: one workgroup (4 waves) per (stream, head, group of up
+// to 4 new queries).  The keys of the group form one list: ring frames at
+// positions lo .. P-1 (slot = position mod W) followed by new frames
+// 0 .. i1-1 (rotated into LDS first).  The list is processed in blocks of
+// 256 keys, each in two passes so K and V are read exactly once:
+//   scores : 8 lanes per 128-byte key row (one 16-byte load each, fully
+//            coalesced: a wave reads 8 consecutive rows per instruction);
+//            partial dot products for the 4 queries are summed across the
+//            8 lanes with DPP moves; masked scores become -inf; the scores
+//            go to LDS;
+//   softmax: one key per thread, block max/sum per query by wave shuffles,
+//            running max/sum rescale (float32, log2 domain);
+//   P V    : same lane layout over the value rows, p read from LDS.
+// The 8-dim partial outputs are reduced across lanes and waves at the end.
+//
+// ring_append_kernel: one workgroup per stream; rotates the new keys (cos/sin
+// per position computed once into LDS), writes keys and values to slot
+// (pos+i) mod W, then advances pos after a workgroup barrier so that every
+// thread has read the old value.
+#include "vx_launch.h"
+
+namespace vx {
+
+namespace {
+
+constexpr int kQC = 4;    // queries per workgroup
+constexpr int kKB = 256;  // keys per block (one per thread in the softmax pass)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Dynamic LDS layout of stream_step_kernel for i1 new keys.
+struct StepLds {
+  size_t cs, knew, qs, sc, red, total;
+  __host__ __device__ StepLds(int i1, size_t elem) {
+    cs = 0;                                                // [i1][2][32] float
+    knew = align16(cs + (size_t)i1 * kD * sizeof(float));  // [i1][64] TI
+    qs = align16(knew + (size_t)i1 * kD * elem);           // [kQC][64] float
+    sc = align16(qs + (size_t)kQC * kD * sizeof(float));   // [kKB][kQC] float
+    red = align16(sc + (size_t)kKB * kQC * sizeof(float)); // [2][4 waves][kQC] float
+    total = align16(red + 2 * 4 * kQC * sizeof(float));
+  }
+};
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreqs fr) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int H = a.H, W = a.W, n = a.n;
+  const int s = blockIdx.x / H, h = blockIdx.x % H;
+  const int i0 = blockIdx.y * kQC;
+  const int i1 = min(n, i0 + kQC);
+  const int nq = i1 - i0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 7;  // 8-dim chunk handled by this lane
+
+  const StepLds L(i1, sizeof(TI));
+  float* cs = (float*)(smem + L.cs);
+  TI* knew = (TI*)(smem + L.knew);
+  float* qs = (float*)(smem + L.qs);
+  float* sc = (float*)(smem + L.sc);
+  float* red = (float*)(smem + L.red);
+
+  const int64_t P = a.pos[s];
+  const int64_t lo = max((int64_t)0, P + i0 - W + 1);
+  const int nring = (int)max((int64_t)0, P - lo);  // ring keys at positions lo .. P-1
+  const int nk = nring + i1;
+  const int lo_slot = (int)(lo % W);  // ring key kk sits at slot lo_slot + kk (mod W), kk < W
+  const size_t frs = (size_t)H * kD;
+  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
+  const TI* __restrict__ qn = (const TI*)a.q + fbase;
+  const TI* __restrict__ kn = (const TI*)a.k + fbase;
+  const TI* __restrict__ vn = (const TI*)a.v + fbase;
+  const size_t rbase = ((size_t)s * H + h) * (size_t)W * kD;
+  const TI* __restrict__ rk = (const TI*)a.ring_k + rbase;
+  const TI* __restrict__ rv = (const TI*)a.ring_v + rbase;
+
+  // ---- prologue: rotate new keys 0..i1-1 into LDS, queries i0..i1-1 into qs
+  if (a.rope) {
+    for (int u = tid; u < i1 * kHalf; u += blockDim.x) {
+      const int j = u / kHalf, i = u % kHalf;
+      float cc, ss;
+      rope_cs(P + j, fr.f[i], &cc, &ss);
+      cs[j * kD + i] = cc;
+      cs[j * kD + kHalf + i] = ss;
+    }
+    __syncthreads();
+  }
+  for (int u = tid; u < (i1 + kQC) * 4; u += blockDim.x) {
+    const int row = u >> 2, cp = u & 3;
+    const bool isq = row >= i1;
+    const int qi = row - i1;  // query slot when isq
+    if (isq && qi >= nq) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qs[qi * kD + 8 * cp + e] = 0.f;
+        qs[qi * kD + kHalf + 8 * cp + e] = 0.f;
+      }
+      continue;
+    }
+    const int j = isq ? i0 + qi : row;  // new-frame index
+    const TI* src = (isq ? qn : kn) + (size_t)j * frs + 8 * cp;
+    float x[8], y[8];
+    load8(src, x);
+    load8(src + kHalf, y);
+    if (a.rope) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float xo, yo;
+        rope_pair(x[e], y[e], cs[j * kD + 8 * cp + e], cs[j * kD + kHalf + 8 * cp + e], &xo, &yo);
+        x[e] = round_to<TI>(xo);
+        y[e] = round_to<TI>(yo);
+      }
+    }
+    if (isq) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qs[qi * kD + 8 * cp + e] = x[e];
+        qs[qi * kD + kHalf + 8 * cp + e] = y[e];
+      }
+    } else {
+      store8(knew + (size_t)j * kD + 8 * cp, x);
+      store8(knew + (size_t)j * kD + kHalf + 8 * cp, y);
+    }
+  }
+  __syncthreads();
+
+  float qreg[kQC][8];
+#pragma unroll
+  for (int i = 0; i < kQC; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qreg[i][e] = qs[i * kD + 8 * c + e];
+
+  float m_i[kQC], l_i[kQC], op[kQC][8];
+#pragma unroll
+  for (int i = 0; i < kQC; ++i) {
+    m_i[i] = -INFINITY;
+    l_i[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) op[i][e] = 0.f;
+  }
+  const float c2 = a.scale_log2;
+  const int sub = wave * 8 + (lane >> 3);  // row within a 32-row slab
+
+  for (int kb0 = 0; kb0 < nk; kb0 += kKB) {
+    const int nkb = min(kKB, nk - kb0);
+    // -- scores
+    for (int r0 = 0; r0 < nkb; r0 += 32) {
+      const int kr = r0 + sub;  // key within block
+      const int kk = kb0 + kr;  // key within list
+      float part[kQC];
+#pragma unroll
+      for (int i = 0; i < kQC; ++i) part[i] = 0.f;
+      if (kr < nkb) {
+        float kv[8];
+        if (kk < nring) {
+          int slot = lo_slot + kk;
+          if (slot >= W) slot -= W;
+          load8(rk + (size_t)slot * kD + 8 * c, kv);
+        } else {
+          load8(knew + (size_t)(kk - nring) * kD + 8 * c, kv);
+        }
+#pragma unroll
+        for (int i = 0; i < kQC; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[i] = fmaf(qreg[i][e], kv[e], part[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kQC; ++i) part[i] = sum8(part[i]);
+      if (c == 0 && kr < nkb) {
+        const int64_t p = lo + kk;  // absolute position of this key
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < kQC; ++i) {
+          const int64_t pq = P + i0 + i;
+          const bool ok = (i < nq) && (p <= pq) && (p >= pq - W + 1);
+          w[i] = ok ? part[i] * c2 : -INFINITY;
+        }
+        *reinterpret_cast<f32x4*>(sc + kr * kQC) = w;
+      }
+    }
+    __syncthreads();
+    // -- block softmax statistics (thread = key)
+    f32x4 xv;
+    if (tid < nkb) {
+      xv = *reinterpret_cast<const f32x4*>(sc + tid * kQC);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQC; ++i) xv[i] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < kQC; ++i) {
+      const float bm = wave_max(xv[i]);
+      if (lane == 0) red[wave * kQC + i] = bm;
+    }
+    __syncthreads();
+    float alpha[kQC], mu[kQC];
+#pragma unroll
+    for (int i = 0; i < kQC; ++i) {
+      float bm = red[i];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) bm = fmaxf(bm, red[w * kQC + i]);
+      const float mn = fmaxf(m_i[i], bm);
+      alpha[i] = (mn == -INFINITY) ? 1.f : exp2f(m_i[i] - mn);
+      mu[i] = (mn == -INFINITY) ? 0.f : mn;
+      m_i[i] = mn;
+    }
+    f32x4 pv;
+#pragma unroll
+    for (int i = 0; i < kQC; ++i) pv[i] = exp2f(xv[i] - mu[i]);
+    if (tid < nkb) *reinterpret_cast<f32x4*>(sc + tid * kQC) = pv;
+#pragma unroll
+    for (int i = 0; i < kQC; ++i) {
+      const float bs = wave_sum(pv[i]);
+      if (lane == 0) red[4 * kQC + wave * kQC + i] = bs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kQC; ++i) {
+      float bs = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) bs += red[4 * kQC + w * kQC + i];
+      l_i[i] = l_i[i] * alpha[i] + bs;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) op[i][e] *= alpha[i];
+    }
+    // -- P V
+    for (int r0 = 0; r0 < nkb; r0 += 32) {
+      const int kr = r0 + sub;
+      const int kk = kb0 + kr;
+      if (kr < nkb) {
+        float vv[8];
+        if (kk < nring) {
+          int slot = lo_slot + kk;
+          if (slot >= W) slot -= W;
+          load8(rv + (size_t)slot * kD + 8 * c, vv);
+        } else {
+          load8(vn + (size_t)(kk - nring) * frs + 8 * c, vv);
+        }
+        const f32x4 pp = *reinterpret_cast<const f32x4*>(sc + kr * kQC);
+#pragma unroll
+        for (int i = 0; i < kQC; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) op[i][e] = fmaf(pp[i], vv[e], op[i][e]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- reduce the per-lane partial outputs: lanes with equal c, then waves
+#pragma unroll
+  for (int i = 0; i < kQC; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = op[i][e];
+      x += __shfl_xor(x, 8, 64);
+      x += __shfl_xor(x, 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      op[i][e] = x;
+    }
+  float* fin = sc;  // [4 waves][8 chunks][kQC][8]: exactly kKB*kQC floats
+  if (lane < 8) {
+#pragma unroll
+    for (int i = 0; i < kQC; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fin[((wave * 8 + lane) * kQC + i) * 8 + e] = op[i][e];
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 6, d = tid & 63;  // 256 threads = kQC queries x 64 dims
+    if (i < nq) {
+      const int cc = d >> 3, e = d & 7;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += fin[((w * 8 + cc) * kQC + i) * 8 + e];
+      TO* op_ = (TO*)a.o + fbase + (size_t)(i0 + i) * frs + d;
+      *op_ = (TO)(acc / l_i[i]);
+    }
+  }
+}
+
+template <typename TI>
+__global__ __launch_bounds__(256) void ring_append_kernel(AppendArgs a, RopeFreqs fr) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* cs = (float*)smem;  // [n][2][32]
+  const int s = blockIdx.x;
+  const int H = a.H, W = a.W, n = a.n;
+  const int tid = threadIdx.x;
+  const int64_t P = a.pos[s];
+  const int p_slot = (int)(((P % W) + W) % W);  // slot of position P
+  if (a.rope) {
+    for (int u = tid; u < n * kHalf; u += blockDim.x) {
+      const int i = u / kHalf, f = u % kHalf;
+      float cc, ss;
+      rope_cs(P + i, fr.f[f], &cc, &ss);
+      cs[i * kD + f] = cc;
+      cs[i * kD + kHalf + f] = ss;
+    }
+  }
+  __syncthreads();
+  const size_t frs = (size_t)H * kD;
+  const int units = n * H * 4;
+  for (int u = tid; u < units; u += blockDim.x) {
+    const int cp = u & 3;
+    const int ih = u >> 2;
+    const int h = ih % H, i = ih / H;
+    int slot = p_slot + i;  // i < n <= W
+    if (slot >= W) slot -= W;
+    const size_t src = ((size_t)s * n + i) * frs + (size_t)h * kD + 8 * cp;
+    const size_t dst = (((size_t)s * H + h) * W + slot) * kD + 8 * cp;
+    const TI* kp = (const TI*)a.k + src;
+    const TI* vp = (const TI*)a.v + src;
+    float x[8], y[8];
+    load8(kp, x);
+    load8(kp + kHalf, y);
+    if (a.rope) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float xo, yo;
+        rope_pair(x[e], y[e], cs[i * kD + 8 * cp + e], cs[i * kD + kHalf + 8 * cp + e], &xo, &yo);
+        x[e] = xo;
+        y[e] = yo;
+      }
+    }
+    TI* rk = (TI*)a.ring_k + dst;
+    store8(rk, x);
+    store8(rk + kHalf, y);
+    float vx8[8], vy8[8];
+    load8(vp, vx8);
+    load8(vp + kHalf, vy8);
+    TI* rvp = (TI*)a.ring_v + dst;
+    store8(rvp, vx8);
+    store8(rvp + kHalf, vy8);
+  }
+  __syncthreads();
+  if (tid == 0) a.pos[s] = P + n;
+}
+
+}  // namespace
+
+hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreqs& fr,
+                              hipStream_t st) {
+  dim3 grid((unsigned)(a.S * a.H), (unsigned)((a.n + kQC - 1) / kQC));
+  const size_t elem = io == DT::BF16 ? 2 : 4;
+  const size_t smem = StepLds(a.n, elem).total;
+  if (io == DT::F32)
+    hipLaunchKernelGGL((stream_step_kernel<float, float>), grid, dim3(256), smem, st, a, fr);
+  else if (out == DT::BF16)
+    hipLaunchKernelGGL((stream_step_kernel<bf16, bf16>), grid, dim3(256), smem, st, a, fr);
+  else
+    hipLaunchKernelGGL((stream_step_kernel<bf16, float>), grid, dim3(256), smem, st, a, fr);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const AppendArgs& a, DT io, const RopeFreqs& fr, hipStream_t st) {
+  const size_t smem = (size_t)a.n * kD * sizeof(float);
+  if (io == DT::F32)
+    hipLaunchKernelGGL(ring_append_kernel<float>, dim3(a.S), dim3(256), smem, st, a, fr);
+  else
+    hipLaunchKernelGGL(ring_append_kernel<bf16>, dim3(a.S), dim3(256), smem, st, a, fr);
+  return hipGetLastError();
+}
+
+}  // namespace vx

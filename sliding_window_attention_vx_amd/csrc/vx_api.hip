@@ -1,0 +1,291 @@
+// C ABI of the vx library: argument validation on the host, then kernel
+// selection and launch on the caller's stream.  Nothing here allocates,
+// synchronises or keeps state between calls (apart from the thread-local
+// text of the last error).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "vx.h"
+#include "vx_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+vx_status fail(vx_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+vx_status ok() {
+  g_err.clear();
+  return VX_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest sizes accepted: every offset fits comfortably in 64-bit, and every
+// launch stays below 2^32 work-items (at most 4 work-items per frame row of
+// one head in the prefill and rotation kernels).
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int32_t kMaxDim = 1 << 24;
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // B*T*H for prefill and rotation
+
+vx::DT to_dt(int32_t d) { return d == VX_BF16 ? vx::DT::BF16 : vx::DT::F32; }
+size_t elem_size(int32_t d) { return d == VX_BF16 ? 2 : 4; }
+
+vx_status check_cfg(const vx_attn_cfg* cfg) {
+  if (!cfg) return fail(VX_E_NULL, "cfg is NULL");
+  if (cfg->head_dim != vx::kD) return fail(VX_E_SHAPE, "head_dim must be 64 (got %d)", cfg->head_dim);
+  if (cfg->window < 1) return fail(VX_E_RANGE, "window must be >= 1 (got %d)", cfg->window);
+  if (!(cfg->rope_theta > 0.0) || !isfinite(cfg->rope_theta))
+    return fail(VX_E_RANGE, "rope_theta must be finite and > 0");
+  if (!(cfg->softmax_scale >= 0.0f) || !isfinite(cfg->softmax_scale))
+    return fail(VX_E_RANGE, "softmax_scale must be finite and >= 0");
+  const int32_t io = cfg->io_dtype, out = cfg->out_dtype;
+  if ((io != VX_F32 && io != VX_BF16) || (out != VX_F32 && out != VX_BF16))
+    return fail(VX_E_DTYPE, "unknown dtype (io %d, out %d)", io, out);
+  if (io == VX_F32 && out == VX_BF16)
+    return fail(VX_E_DTYPE, "float32 inputs with bfloat16 output is not supported");
+  if (cfg->flags & ~VX_FLAG_VALU_KERNEL) return fail(VX_E_RANGE, "unknown flag bits 0x%x", cfg->flags);
+  return VX_OK;
+}
+
+vx::RopeFreqs rope_freqs(double theta) {
+  vx::RopeFreqs f;
+  for (int i = 0; i < vx::kHalf; ++i) f.f[i] = pow(theta, -2.0 * i / (double)vx::kD);
+  return f;
+}
+
+float scale_log2(const vx_attn_cfg* cfg) {
+  const double s = cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)vx::kD);
+  return (float)(s * 1.4426950408889634073599);  // log2(e)
+}
+
+vx_status check_dims(const char* what, int64_t a, int64_t b, int64_t c) {
+  if (a < 0 || b < 0 || c < 0) return fail(VX_E_SHAPE, "%s: negative size", what);
+  if (a > kMaxDim || b > kMaxDim || c > kMaxDim) return fail(VX_E_SHAPE, "%s: size too large", what);
+  if (a * b * c * vx::kD > kMaxElems) return fail(VX_E_SHAPE, "%s: tensor too large", what);
+  return VX_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+vx_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(VX_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+void vx_default_cfg(vx_attn_cfg* cfg) {
+  if (!cfg) return;
+  cfg->head_dim = 64;
+  cfg->window = 750;
+  cfg->rope_theta = 1e6;
+  cfg->softmax_scale = 0.125f;
+  cfg->io_dtype = VX_BF16;
+  cfg->out_dtype = VX_BF16;
+  cfg->flags = 0;
+}
+
+vx_status vx_rope_table(float* table, int64_t p_begin, int32_t count, const vx_attn_cfg* cfg,
+                        void* stream) {
+  if (!cfg) return fail(VX_E_NULL, "cfg is NULL");
+  if (cfg->head_dim != vx::kD) return fail(VX_E_SHAPE, "head_dim must be 64 (got %d)", cfg->head_dim);
+  if (!(cfg->rope_theta > 0.0) || !isfinite(cfg->rope_theta))
+    return fail(VX_E_RANGE, "rope_theta must be finite and > 0");
+  if (count < 0 || count > kMaxDim) return fail(VX_E_SHAPE, "count out of range (%d)", count);
+  if (p_begin < 0 || p_begin > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "p_begin out of range");
+  if (count == 0) return ok();
+  if (!table) return fail(VX_E_NULL, "table is NULL");
+  if (!aligned16(table)) return fail(VX_E_ALIGN, "table is not 16-byte aligned");
+  (void)hipGetLastError();
+  return launched(vx::launch_rope_table(table, p_begin, count, rope_freqs(cfg->rope_theta),
+                                        (hipStream_t)stream));
+}
+
+vx_status vx_rope_qk(void* q, void* k, int32_t B, int32_t T, int32_t H, int64_t pos0,
+                     const vx_attn_cfg* cfg, void* stream) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_dims("rope_qk", B, T, H))) return st;
+  if (pos0 < 0 || pos0 > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "pos0 out of range");
+  if ((int64_t)B * T == 0) return ok();
+  if (H < 1) return fail(VX_E_SHAPE, "H must be >= 1");
+  if ((int64_t)B * T * H > kMaxRows) return fail(VX_E_SHAPE, "B*T*H too large");
+  if (!q && !k) return fail(VX_E_NULL, "q and k are both NULL");
+  if ((q && !aligned16(q)) || (k && !aligned16(k))) return fail(VX_E_ALIGN, "q/k not 16-byte aligned");
+  const size_t bytes = (size_t)B * T * H * vx::kD * elem_size(cfg->io_dtype);
+  if (q && k && overlap(q, bytes, k, bytes)) return fail(VX_E_RANGE, "q and k overlap");
+  (void)hipGetLastError();
+  return launched(vx::launch_rope_qk(q, k, B, T, H, pos0, to_dt(cfg->io_dtype),
+                                     rope_freqs(cfg->rope_theta), (hipStream_t)stream));
+}
+
+vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t B,
+                              int32_t T, int32_t H, int64_t pos0, int32_t rope_applied,
+                              const float* rope_table, int64_t table_p0, int64_t table_len,
+                              const vx_attn_cfg* cfg, void* stream) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_dims("prefill", B, T, H))) return st;
+  if (pos0 < 0 || pos0 > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "pos0 out of range");
+  if ((int64_t)B * T == 0) return ok();
+  if (H < 1) return fail(VX_E_SHAPE, "H must be >= 1");
+  if (B > 65535 || H > 65535) return fail(VX_E_SHAPE, "B and H must be <= 65535");
+  if ((int64_t)B * T * H > kMaxRows) return fail(VX_E_SHAPE, "B*T*H too large");
+  if (!q || !k || !v || !o) return fail(VX_E_NULL, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "q, k, v and o must be 16-byte aligned");
+  const size_t n = (size_t)B * T * H * vx::kD;
+  const size_t ib = n * elem_size(cfg->io_dtype), ob = n * elem_size(cfg->out_dtype);
+  if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib))
+    return fail(VX_E_RANGE, "o overlaps an input");
+  vx::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.W = cfg->window;
+  a.pos0 = pos0;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  if (a.rope) {
+    if (!rope_table) return fail(VX_E_NULL, "rope_table is NULL and rope_applied == 0");
+    if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "rope_table is not 16-byte aligned");
+    if (table_p0 < 0 || table_len < 0 || pos0 < table_p0 || pos0 + T > table_p0 + table_len)
+      return fail(VX_E_RANGE,
+                  "rope_table covers positions [%lld, %lld) but the chunk needs [%lld, %lld)",
+                  (long long)table_p0, (long long)(table_p0 + table_len), (long long)pos0,
+                  (long long)(pos0 + T));
+    a.table = rope_table;
+    a.table_row0 = pos0 - table_p0;
+  }
+  (void)hipGetLastError();
+  const bool valu = (cfg->flags & VX_FLAG_VALU_KERNEL) || cfg->io_dtype == VX_F32;
+  if (valu)
+    return launched(vx::launch_prefill_valu(a, to_dt(cfg->io_dtype), to_dt(cfg->out_dtype),
+                                            (hipStream_t)stream));
+  return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
+}
+
+static vx_status check_stream_common(const char* what, int32_t S, int32_t n, int32_t H,
+                                     const vx_attn_cfg* cfg) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_dims(what, S, n, H))) return st;
+  if (n < 1 || n > cfg->window)
+    return fail(VX_E_RANGE, "%s: need 1 <= n <= window (n %d, window %d)", what, n, cfg->window);
+  if (n > vx::kStreamMaxNew)
+    return fail(VX_E_RANGE, "%s: at most %d new frames per step (got %d)", what,
+                vx::kStreamMaxNew, n);
+  if (H < 1) return fail(VX_E_SHAPE, "%s: H must be >= 1", what);
+  if ((int64_t)S * H * ((n + 3) / 4) * 256 >= ((int64_t)1 << 32))
+    return fail(VX_E_SHAPE, "%s: S*H*n too large", what);
+  if ((int64_t)S * H * cfg->window * vx::kD > kMaxElems) return fail(VX_E_SHAPE, "%s: ring too large", what);
+  return VX_OK;
+}
+
+vx_status vx_swa_attn_stream_step(const void* q_new, const void* k_new, const void* v_new,
+                                  const void* ring_k, const void* ring_v, const int64_t* pos,
+                                  void* o, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
+                                  const vx_attn_cfg* cfg, void* stream) {
+  vx_status st = check_stream_common("stream_step", S, n, H, cfg);
+  if (st) return st;
+  if (S == 0) return ok();
+  if (!q_new || !k_new || !v_new || !ring_k || !ring_v || !pos || !o)
+    return fail(VX_E_NULL, "stream_step: a tensor pointer is NULL");
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) ||
+      !aligned16(ring_v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "stream_step: tensors must be 16-byte aligned");
+  if (((uintptr_t)pos & 7u) != 0) return fail(VX_E_ALIGN, "stream_step: pos must be 8-byte aligned");
+  const size_t nf = (size_t)S * n * H * vx::kD;
+  const size_t ob = nf * elem_size(cfg->out_dtype), ib = nf * elem_size(cfg->io_dtype);
+  const size_t rb = (size_t)S * H * cfg->window * vx::kD * elem_size(cfg->io_dtype);
+  if (overlap(o, ob, q_new, ib) || overlap(o, ob, k_new, ib) || overlap(o, ob, v_new, ib) ||
+      overlap(o, ob, ring_k, rb) || overlap(o, ob, ring_v, rb))
+    return fail(VX_E_RANGE, "stream_step: o overlaps an input");
+  vx::StreamArgs a{};
+  a.q = q_new;
+  a.k = k_new;
+  a.v = v_new;
+  a.ring_k = ring_k;
+  a.ring_v = ring_v;
+  a.pos = pos;
+  a.o = o;
+  a.S = S;
+  a.n = n;
+  a.H = H;
+  a.W = cfg->window;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  (void)hipGetLastError();
+  return launched(vx::launch_stream_step(a, to_dt(cfg->io_dtype), to_dt(cfg->out_dtype),
+                                         rope_freqs(cfg->rope_theta), (hipStream_t)stream));
+}
+
+vx_status vx_kv_ring_append(void* ring_k, void* ring_v, const void* k_new, const void* v_new,
+                            int64_t* pos, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
+                            const vx_attn_cfg* cfg, void* stream) {
+  vx_status st = check_stream_common("ring_append", S, n, H, cfg);
+  if (st) return st;
+  if (S == 0) return ok();
+  if (!ring_k || !ring_v || !k_new || !v_new || !pos)
+    return fail(VX_E_NULL, "ring_append: a tensor pointer is NULL");
+  if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(VX_E_ALIGN, "ring_append: tensors must be 16-byte aligned");
+  if (((uintptr_t)pos & 7u) != 0) return fail(VX_E_ALIGN, "ring_append: pos must be 8-byte aligned");
+  const size_t rb = (size_t)S * H * cfg->window * vx::kD * elem_size(cfg->io_dtype);
+  if (overlap(ring_k, rb, ring_v, rb)) return fail(VX_E_RANGE, "ring_append: ring_k and ring_v overlap");
+  vx::AppendArgs a{};
+  a.ring_k = ring_k;
+  a.ring_v = ring_v;
+  a.k = k_new;
+  a.v = v_new;
+  a.pos = pos;
+  a.S = S;
+  a.n = n;
+  a.H = H;
+  a.W = cfg->window;
+  a.rope = rope_applied == 0;
+  (void)hipGetLastError();
+  return launched(vx::launch_ring_append(a, to_dt(cfg->io_dtype), rope_freqs(cfg->rope_theta),
+                                         (hipStream_t)stream));
+}
+
+const char* vx_status_string(vx_status s) {
+  switch (s) {
+    case VX_OK: return "ok";
+    case VX_E_NULL: return "null pointer";
+    case VX_E_SHAPE: return "bad shape";
+    case VX_E_DTYPE: return "unsupported dtype";
+    case VX_E_ALIGN: return "misaligned pointer";
+    case VX_E_RANGE: return "value out of range";
+    case VX_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* vx_last_error(void) { return g_err.c_str(); }
+
+int32_t vx_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+Every argument check in libvx runs before any HIP call, so these tests call
+the entry points with host buffers standing in for device pointers and check
+that each invalid argument is rejected with the documented status and that
+no buffer is touched.  They also check that libvx.so exports every function
+include/vx.h declares and that the header compiles as plain C.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import sliding_window_attention_vx_amd as vx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vx.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_RANGE, E_HIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(vx_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vx.LIB_PATH):
+        from sliding_window_attention_vx_amd import build
+        build.build()
+    return vx.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ("vx_rope_qk", "vx_swa_attn_prefill", "vx_swa_attn_stream_step", "vx_kv_ring_append",
+              "vx_rope_table", "vx_status_string", "vx_last_error", "vx_version",
+              "vx_default_cfg"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", vx.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (vx_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_is_plain_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "vx.h"\n#include <stdio.h>\n'
+                   "int main(void){vx_attn_cfg c; vx_default_cfg(&c);\n"
+                   " vx_status s = vx_swa_attn_prefill(0,0,0,0,1,1,1,0,1,0,0,0,&c,0);\n"
+                   ' printf("%d %d %s\\n", c.window, (int)s, vx_status_string(s));\n'
+                   " return s == VX_E_NULL ? 0 : 1;}\n")
+    exe = tmp_path / "use"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe), vx.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(vx.LIB_PATH)}"],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.split()[:2] == ["750", "1"]
+
+
+def test_default_cfg(L):
+    c = vx._Cfg()
+    L.vx_default_cfg(ctypes.byref(c))
+    assert (c.head_dim, c.window, c.rope_theta, c.softmax_scale, c.io_dtype, c.out_dtype, c.flags) \
+        == (64, 750, 1e6, 0.125, vx.VX_BF16, vx.VX_BF16, 0)
+    assert L.vx_version() >= 100
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert L.vx_status_string(code).decode() == vx._STATUS[code]
+
+
+class Bufs:
+    """Host arrays standing in for device buffers (16-byte aligned)."""
+
+    def __init__(self, nbytes=1 << 16):
+        self.arrs = []
+        self.nbytes = nbytes
+
+    def new(self):
+        a = np.full(self.nbytes // 4 + 16, 7.0, dtype=np.float32)
+        off = (-a.ctypes.data) % 16 // 4
+        a = a[off:off + self.nbytes // 4]
+        assert a.ctypes.data % 16 == 0
+        self.arrs.append(a)
+        return ctypes.c_void_p(a.ctypes.data)
+
+    def untouched(self):
+        return all(np.all(a == 7.0) for a in self.arrs)
+
+
+def cfg(**kw):
+    c = vx._Cfg()
+    vx.lib().vx_default_cfg(ctypes.byref(c))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def prefill(L, b, c, q=None, k=None, v=None, o=None, B=1, T=8, H=2, pos0=0, rope_applied=1,
+            table=None, tp0=0, tlen=0):
+    q = q if q is not None else b.new()
+    k = k if k is not None else b.new()
+    v = v if v is not None else b.new()
+    o = o if o is not None else b.new()
+    return L.vx_swa_attn_prefill(q, k, v, o, B, T, H, pos0, rope_applied, table, tp0, tlen,
+                                 None if c is None else ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=32), E_SHAPE), (dict(window=0), E_RANGE), (dict(window=-5), E_RANGE),
+    (dict(rope_theta=0.0), E_RANGE), (dict(rope_theta=float("nan")), E_RANGE),
+    (dict(rope_theta=float("inf")), E_RANGE), (dict(softmax_scale=-1.0), E_RANGE),
+    (dict(softmax_scale=float("nan")), E_RANGE), (dict(io_dtype=vx.VX_F32, out_dtype=vx.VX_BF16), E_DTYPE),
+    (dict(io_dtype=7), E_DTYPE), (dict(out_dtype=-1), E_DTYPE), (dict(flags=2), E_RANGE),
+])
+def test_prefill_rejects_bad_cfg(L, kw, status):
+    b = Bufs()
+    assert prefill(L, b, cfg(**kw)) == status
+    assert L.vx_last_error().decode() != ""
+    assert b.untouched()
+
+
+def test_prefill_argument_errors(L):
+    b = Bufs()
+    c = cfg()
+    assert prefill(L, b, None) == E_NULL
+    assert prefill(L, b, c, B=-1) == E_SHAPE
+    assert prefill(L, b, c, T=-3) == E_SHAPE
+    assert prefill(L, b, c, H=0) == E_SHAPE
+    assert prefill(L, b, c, T=1 << 25) == E_SHAPE
+    assert prefill(L, b, c, q=ctypes.c_void_p(0)) == E_NULL
+    assert prefill(L, b, c, o=ctypes.c_void_p(0)) == E_NULL
+    mis = ctypes.c_void_p(b.new().value + 4)
+    assert prefill(L, b, c, v=mis) == E_ALIGN
+    q = b.new()
+    assert prefill(L, b, c, q=q, o=q) == E_RANGE  # o aliases q
+    assert prefill(L, b, c, pos0=-1) == E_RANGE
+    # rope on load needs a table covering pos0 .. pos0+T-1
+    assert prefill(L, b, c, rope_applied=0) == E_NULL
+    t = b.new()
+    assert prefill(L, b, c, rope_applied=0, table=t, tp0=0, tlen=7) == E_RANGE
+    assert prefill(L, b, c, rope_applied=0, table=t, tp0=5, tlen=100, pos0=4) == E_RANGE
+    assert prefill(L, b, c, rope_applied=0, table=ctypes.c_void_p(t.value + 4), tp0=0,
+                   tlen=100) == E_ALIGN
+    assert b.untouched()
+
+
+def test_prefill_empty_is_ok_without_launch(L):
+    c = cfg()
+    z = ctypes.c_void_p(0)
+    assert L.vx_swa_attn_prefill(z, z, z, z, 0, 10, 4, 0, 1, z, 0, 0, ctypes.byref(c), z) == OK
+    assert L.vx_swa_attn_prefill(z, z, z, z, 3, 0, 4, 0, 1, z, 0, 0, ctypes.byref(c), z) == OK
+    assert L.vx_last_error().decode() == ""
+
+
+def stream_step(L, b, c, S=2, n=4, H=2, **ov):
+    a = dict(q=b.new(), k=b.new(), v=b.new(), rk=b.new(), rv=b.new(), pos=b.new(), o=b.new())
+    a.update(ov)
+    return L.vx_swa_attn_stream_step(a["q"], a["k"], a["v"], a["rk"], a["rv"], a["pos"], a["o"],
+                                     S, n, H, 0, None if c is None else ctypes.byref(c), None)
+
+
+def test_stream_step_argument_errors(L):
+    b = Bufs()
+    c = cfg(window=16)
+    assert stream_step(L, b, None) == E_NULL
+    assert stream_step(L, b, c, n=0) == E_RANGE
+    assert stream_step(L, b, c, n=17) == E_RANGE  # n > W
+    assert stream_step(L, b, cfg(window=750), n=65) == E_RANGE  # above the per-step cap
+    assert stream_step(L, b, c, S=-1) == E_SHAPE
+    assert stream_step(L, b, c, H=0) == E_SHAPE
+    assert stream_step(L, b, c, pos=ctypes.c_void_p(0)) == E_NULL
+    assert stream_step(L, b, c, rk=ctypes.c_void_p(0)) == E_NULL
+    assert stream_step(L, b, c, pos=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    assert stream_step(L, b, c, q=ctypes.c_void_p(b.new().value + 8)) == E_ALIGN
+    rk = b.new()
+    assert stream_step(L, b, c, rk=rk, o=rk) == E_RANGE
+    assert stream_step(L, b, cfg(head_dim=128)) == E_SHAPE
+    assert b.untouched()
+    z = ctypes.c_void_p(0)
+    assert L.vx_swa_attn_stream_step(z, z, z, z, z, z, z, 0, 4, 2, 0, ctypes.byref(c), z) == OK
+
+
+def test_ring_append_argument_errors(L):
+    b = Bufs()
+    c = cfg(window=16)
+
+    def call(S=2, n=4, H=2, **ov):
+        a = dict(rk=b.new(), rv=b.new(), k=b.new(), v=b.new(), pos=b.new())
+        a.update(ov)
+        return L.vx_kv_ring_append(a["rk"], a["rv"], a["k"], a["v"], a["pos"], S, n, H, 0,
+                                   ctypes.byref(c), None)
+    assert call(n=0) == E_RANGE
+    assert call(n=17) == E_RANGE
+    assert call(pos=ctypes.c_void_p(0)) == E_NULL
+    assert call(k=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    r = b.new()
+    assert call(rk=r, rv=r) == E_RANGE
+    assert call(S=-2) == E_SHAPE
+    assert b.untouched()
+
+
+def test_rope_qk_and_table_errors(L):
+    b = Bufs()
+    c = cfg()
+    z = ctypes.c_void_p(0)
+    assert L.vx_rope_qk(z, z, 1, 4, 2, 0, ctypes.byref(c), z) == E_NULL
+    q = b.new()
+    assert L.vx_rope_qk(q, q, 1, 4, 2, 0, ctypes.byref(c), z) == E_RANGE
+    assert L.vx_rope_qk(q, z, 1, 4, 2, -1, ctypes.byref(c), z) == E_RANGE
+    assert L.vx_rope_qk(ctypes.c_void_p(q.value + 4), z, 1, 4, 2, 0, ctypes.byref(c), z) == E_ALIGN
+    assert L.vx_rope_qk(q, z, 1, 4, -2, 0, ctypes.byref(c), z) == E_SHAPE
+    assert L.vx_rope_table(z, 0, 10, ctypes.byref(c), z) == E_NULL
+    assert L.vx_rope_table(q, -1, 10, ctypes.byref(c), z) == E_RANGE
+    assert L.vx_rope_table(q, 0, -1, ctypes.byref(c), z) == E_SHAPE
+    assert L.vx_rope_table(ctypes.c_void_p(q.value + 4), 0, 3, ctypes.byref(c), z) == E_ALIGN
+    assert L.vx_rope_table(q, 0, 3, ctypes.byref(cfg(rope_theta=-1.0)), z) == E_RANGE
+    assert L.vx_rope_table(z, 0, 0, ctypes.byref(c), z) == OK
+    assert b.untouched()
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        vx.prefill(x, x, x)
+    with pytest.raises(ValueError):
+        vx.rope_qk(x, None)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(vx, "_lib", None)
+    monkeypatch.setattr(vx, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        vx.lib()
