@@ -15,17 +15,23 @@
 //   P^T = exp2(S^T * scale*log2e - m)  (lazy max: m moves only when a
 //                    score exceeds it by more than 8, so p <= 256)
 //   O^T += V^T P^T : B = P^T straight from the score registers (bf16);
-//                    A = V^T from LDS, where V was written transposed with
-//                    the key order permuted (bits 2 and 3 of the key index
-//                    swapped) so that each lane's eight keys are one 16-byte
-//                    LDS read matching the score register layout.
+//                    A = V^T read from the row-major V tile with two LDS
+//                    transpose reads (ds_read_b64_tr_b16), each giving a lane
+//                    four consecutive keys of one dimension, exactly the key
+//                    order of the score register layout.
+//   l += P . 1     : row sums from the packed bf16 P (v_dot2c_f32_bf16), so
+//                    the normaliser matches the weights the MFMA multiplies.
 // RoPE is fused into the loads: each lane rotates its own Q' row halves
 // (pairs (i, i+32) are lane-local) and the staging threads rotate each K
 // tile once per workgroup, reading cos/sin from the float32 table; rotated
 // values are rounded to bf16 (the storage type of a rotated tensor).
-// LDS rows are 144 bytes (128 + 16 pad) so that 16-byte reads of 32
-// consecutive rows hit distinct banks.  K/V staging is double buffered:
-// the next tile's global loads are issued before the current tile's MFMAs.
+// LDS rows are padded (K' 144 bytes, V 192 bytes) and the staging threads
+// are mapped to rows so that the MFMA operand reads and the staging writes
+// hit distinct banks.  K/V staging is double buffered: the next tile's global loads are
+// issued before the current tile's MFMAs.  Masks are applied only to the
+// 32-key halves that straddle a band edge, as one unsigned range test per
+// score.  Accumulators stay in VGPRs (the build asks for the VGPR form of
+// MFMA) so the softmax never moves them between register files.
 #include "vx_launch.h"
 
 namespace vx {
@@ -33,27 +39,54 @@ namespace vx {
 namespace {
 
 constexpr int kBN = 64;                    // keys per staged tile
-constexpr int kRow = 144;                  // LDS bytes per row
-constexpr int kTileBytes = 64 * kRow;      // one K' tile or one V^T tile
+constexpr int kRowK = 144;                 // LDS bytes per K' row: 16-byte reads of 32
+                                           // consecutive rows hit distinct banks
+constexpr int kRowV = 192;                 // LDS bytes per V row: the 8-byte transpose
+                                           // reads of 4 rows x 2 dim blocks hit distinct banks
+constexpr int kTileK = 64 * kRowK;         // one K' tile
+constexpr int kTileV = 64 * kRowV;         // one V tile
+constexpr int kStageBytes = kTileK + kTileV;
 constexpr float kLazy = 8.0f;              // log2-domain slack of the running max
 
-__device__ __forceinline__ int vt_phys(int kk) {
-  // key index inside a 64-key tile -> column in the V^T row (bits 2 and 3 swapped)
-  return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// max / sum of x over lanes l and l^32 (v_permlane32_swap)
+__device__ __forceinline__ float partner_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float partner_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// K unit u -> (row, chunk pair): 16 consecutive lanes write rows {0,4,8,12}+.. so
+// that their 16-byte stores at the 144-byte row stride fall in distinct banks.
+__device__ __forceinline__ void k_unit(int u, int& r, int& cp) {
+  cp = u & 3;
+  r = 16 * (u >> 6) + 4 * ((u >> 2) & 3) + ((u >> 4) & 3);
+}
+// V unit u -> (row, 16-byte chunk): 16 consecutive lanes cover rows 0..3 x 4 chunks,
+// conflict-free at the 192-byte row stride; 8 lanes still read each 128-byte row.
+__device__ __forceinline__ void v_unit(int u, int& r, int& c) {
+  r = 8 * (u >> 6) + 4 * ((u >> 5) & 1) + ((u >> 2) & 3);
+  c = 4 * ((u >> 4) & 1) + (u & 3);
 }
 
 template <int NW>
 struct Stage {
   static constexpr int NT = NW * 64;
-  static constexpr int UK = 256 / NT;  // K units per thread (row, chunk pair)
-  static constexpr int UV = 256 / NT;  // V units per thread (row pair, chunk)
+  static constexpr int UK = 256 / NT;  // K units per thread: (row, chunk pair)
+  static constexpr int UV = 512 / NT;  // V units per thread: (row, 16-byte chunk)
   u32x4 kx[UK], ky[UK];
   float kc[UK][8], ks[UK][8];
-  u32x4 v0[UV], v1[UV];
+  u32x4 v[UV];
 };
 
 template <int NW>
@@ -62,10 +95,11 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
                                            bool rope, const float* __restrict__ table,
                                            int64_t row0, int tid) {
   constexpr int NT = Stage<NW>::NT;
+  const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UK; ++j) {
-    const int u = tid + j * NT;
-    const int r = u >> 2, cp = u & 3;
+    int r, cp;
+    k_unit(tid + j * NT, r, cp);
     const int key = kt0 + r;
     if (key < T) {
       const bf16* kp = k + (size_t)key * rs + 8 * cp;
@@ -77,8 +111,8 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
         load8(cs + kHalf, st.ks[j]);
       }
     } else {
-      st.kx[j] = u32x4{0, 0, 0, 0};
-      st.ky[j] = u32x4{0, 0, 0, 0};
+      st.kx[j] = zero;
+      st.ky[j] = zero;
       if (rope) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -90,13 +124,10 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
-    const int u = tid + j * NT;
-    const int rp = u & 31, c = u >> 5;
-    const int key = kt0 + 2 * rp;
-    const u32x4 zero = {0, 0, 0, 0};
-    st.v0[j] = key < T ? *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c) : zero;
-    st.v1[j] = key + 1 < T ? *reinterpret_cast<const u32x4*>(v + (size_t)(key + 1) * rs + 8 * c)
-                           : zero;
+    int r, c;
+    v_unit(tid + j * NT, r, c);
+    const int key = kt0 + r;
+    st.v[j] = key < T ? *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c) : zero;
   }
 }
 
@@ -106,8 +137,8 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
   constexpr int NT = Stage<NW>::NT;
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UK; ++j) {
-    const int u = tid + j * NT;
-    const int r = u >> 2, cp = u & 3;
+    int r, cp;
+    k_unit(tid + j * NT, r, cp);
     u32x4 x = st.kx[j], y = st.ky[j];
     if (rope) {
       float xf[8], yf[8];
@@ -123,30 +154,21 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
       x = pack8(xf);
       y = pack8(yf);
     }
-    *reinterpret_cast<u32x4*>(Kb + r * kRow + 16 * cp) = x;
-    *reinterpret_cast<u32x4*>(Kb + r * kRow + 64 + 16 * cp) = y;
+    *reinterpret_cast<u32x4*>(Kb + r * kRowK + 16 * cp) = x;
+    *reinterpret_cast<u32x4*>(Kb + r * kRowK + 64 + 16 * cp) = y;
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
-    const int u = tid + j * NT;
-    const int rp = u & 31, c = u >> 5;
-    const int col = vt_phys(2 * rp);  // even; the pair (2rp, 2rp+1) stays adjacent
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t a0 = st.v0[j][i], a1 = st.v1[j][i];
-      // dims 8c+2i and 8c+2i+1: (key 2rp, key 2rp+1) pairs
-      *reinterpret_cast<uint32_t*>(Vb + (8 * c + 2 * i) * kRow + 2 * col) =
-          (a0 & 0xffffu) | (a1 << 16);
-      *reinterpret_cast<uint32_t*>(Vb + (8 * c + 2 * i + 1) * kRow + 2 * col) =
-          (a0 >> 16) | (a1 & 0xffff0000u);
-    }
+    int r, c;
+    v_unit(tid + j * NT, r, c);
+    *reinterpret_cast<u32x4*>(Vb + r * kRowV + 16 * c) = st.v[j];
   }
 }
 
 template <int NW, typename TO>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
-                                                               int n_logical) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];
+__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
+                                                                  int n_logical) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   constexpr int BM = NW * 32;
 
   // XCD-aware order: the grid is a multiple of 8 and the dispatcher deals
@@ -213,11 +235,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     for (int m = 0; m < 4; ++m) qf[m] = bf16x8{};
   }
 
+  // per-lane LDS offsets: K' fragment row/col, and the transpose-read address
+  // (lane L of each 16-lane group points at row L/4, dims 4*(L%4) of its block)
+  const int k_off = l32 * kRowK + 16 * hh;
+  const int g = lane >> 4, L = lane & 15;
+  const int v_off = (4 * (g >> 1) + (L >> 2)) * kRowV + (16 * (g & 1) + 4 * (L & 3)) * 2;
+
   f32x16 oacc[2];
   oacc[0] = f32x16{};
   oacc[1] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
+  const unsigned wm1 = (unsigned)(W - 1);
 
   const int kbeg = max(0, q0 - W + 1);
   const int klast = min(T, q0 + BM) - 1;
@@ -225,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
 
   Stage<NW> st;
   stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
-  stage_commit<NW>(st, lds, lds + kTileBytes, rope, tid);
+  stage_commit<NW>(st, lds, lds + kTileK, rope, tid);
   __syncthreads();
 
   for (int it = it0; it <= it1; ++it) {
@@ -233,50 +262,50 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
     const bool more = it < it1;
     if (more) stage_load<NW>(st, k, v, rs, T, (it + 1) * kBN, rope, a.table, a.table_row0, tid);
 
-    const char* Kb = lds + buf * 2 * kTileBytes;
-    const char* Vb = Kb + kTileBytes;
+    const char* Kb = lds + buf * kStageBytes;
+    const char* Vb = Kb + kTileK;
     const int kt0 = it * kBN;
 
-    bool act[2], msk[2];
+    // S^T for one 32-key half: 4 MFMAs over the 64 dims
+    auto s_half = [&](int sb) {
+      f32x16 acc = f32x16{};
+      const char* kr = Kb + 32 * sb * kRowK + k_off;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int kb = kt0 + 32 * sb;
-      act[sb] = (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
-      msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
-    }
-    if (act[0] || act[1]) {
-      float x[2][16];
-      float mx = -INFINITY;
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * m);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], acc, 0, 0, 0);
+      }
+      return acc;
+    };
+    // exp2, bf16 pack, row sum and O^T += V^T P^T for one half
+    auto pv_half = [&](const f32x16& sc, int sb, float mu) {
+      float p[16];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (!act[sb]) {
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -mu));
+      const u32x4 w0 = pack8(p), w1 = pack8(p + 8);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) x[sb][r] = -INFINITY;
-          continue;
-        }
-        f32x16 s = f32x16{};
-        const char* kr = Kb + (32 * sb + l32) * kRow + 16 * hh;
+      for (int i = 0; i < 4; ++i) {
+        l_run = dot2_ones(w0[i], l_run);
+        l_run = dot2_ones(w1[i], l_run);
+      }
+      const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, w0), __builtin_bit_cast(bf16x8, w1)};
+      const char* vr = Vb + 32 * sb * kRowV + v_off;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 32 * m);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], s, 0, 0, 0);
-        }
-        const int kb = kt0 + 32 * sb + 4 * hh;
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float val = s[r] * c2;
-          if (msk[sb]) {
-            const int key = kb + 8 * (r >> 2) + (r & 3);
-            if (key > tq || key < tq - W + 1) val = -INFINITY;
-          }
-          x[sb][r] = val;
-          mx = fmaxf(mx, val);
+        for (int db = 0; db < 2; ++db) {
+          const char* p0 = vr + 16 * ks * kRowV + 64 * db;
+          const bf16x8 vf = lds_tr_pair(p0, p0 + 8 * kRowV);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
         }
       }
-      mx = fmaxf(mx, xor32(mx));
-      const bool need = mx > m_run + kLazy;
+    };
+    // lazy running max: move it only when a score exceeds it by more than kLazy
+    auto update_max = [&](float mx) {
+      const float mxs = partner_max(mx) * c2;  // log2 domain
+      const bool need = mxs > m_run + kLazy;
       if (__any(need)) {
-        const float m_new = need ? mx : m_run;
+        const float m_new = need ? mxs : m_run;
         // a lane whose keys were all masked so far has nothing to rescale
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
@@ -287,55 +316,66 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillArgs a, in
         }
         m_run = m_new;
       }
-      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    };
+
+    bool act[2], msk[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kb = kt0 + 32 * sb;
+      act[sb] = (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
+      msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
+    }
+    if (act[0] || act[1]) {
+      f32x16 sc[2];
+      float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         if (!act[sb]) continue;
-        float pr[16];
+        f32x16 acc = s_half(sb);
+        if (msk[sb]) {
+          // key of register r: kb + 4hh + 8(r/4) + r%4; keep iff 0 <= tq - key <= W-1
+          const int d0 = tq - (kt0 + 32 * sb + 4 * hh);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(x[sb][r] - mu);
-          l_run += pr[r];
-        }
-        bf16x8 pf[2];
-        pf[0] = __builtin_bit_cast(bf16x8, pack8(pr));
-        pf[1] = __builtin_bit_cast(bf16x8, pack8(pr + 8));
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                Vb + (32 * db + l32) * kRow + 64 * sb + 32 * ks + 16 * hh);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            acc[r] = ((unsigned)(d0 - off) <= wm1) ? acc[r] : -INFINITY;
           }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        sc[sb] = acc;
       }
+      update_max(mx);
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+        if (act[sb]) pv_half(sc[sb], sb, mu);
     }
 
-    if (more) stage_commit<NW>(st, lds + (buf ^ 1) * 2 * kTileBytes,
-                               lds + (buf ^ 1) * 2 * kTileBytes + kTileBytes, rope, tid);
+    if (more) stage_commit<NW>(st, lds + (buf ^ 1) * kStageBytes,
+                               lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid);
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, lane holds query tq, dims 32db + 8g + 4hh + (0..3)
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = partner_sum(l_run);
   if (tq < T) {
     const float inv = 1.f / l_tot;
     TO* op = o + (size_t)tq * rs;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * hh;
+      for (int gg = 0; gg < 4; ++gg) {
+        const int d0 = 32 * db + 8 * gg + 4 * hh;
         if constexpr (sizeof(TO) == 2) {
           uint2 w;
-          w.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-          w.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+          w.x = pack_bf16x2(oacc[db][4 * gg] * inv, oacc[db][4 * gg + 1] * inv);
+          w.y = pack_bf16x2(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv);
           *reinterpret_cast<uint2*>(op + d0) = w;
         } else {
           f32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * g + e] * inv;
+          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * gg + e] * inv;
           *reinterpret_cast<f32x4*>(op + d0) = w;
         }
       }

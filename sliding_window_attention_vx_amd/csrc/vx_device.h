@@ -57,6 +57,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[1] = (bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
 }
+// acc + lo(w) + hi(w) for a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+// The word is taken by value: bit-casting an element of a vector expression
+// directly in the builtin's argument has been miscompiled (every element read
+// as element 0), a copy into a scalar avoids that.
+__device__ __forceinline__ float dot2_ones(uint32_t w, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  bf16x2 x;
+  __builtin_memcpy(&x, &w, sizeof x);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+
 __device__ __forceinline__ void unpack8(const u32x4 w, float v[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

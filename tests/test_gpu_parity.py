@@ -336,3 +336,21 @@ def test_stream_snapshot_resume_bitwise():
                                    vd[:, sl].contiguous(), a, b, p, window=W))
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("T,W", [(1, 750), (5, 750), (97, 33), (300, 64), (1500, 750)])
+def test_prefill_uniform_scores_closed_form(T, W):
+    # q = k = 0 makes every score 0, so o[t] is the plain mean of v[t-W+1..t]:
+    # exact for small-integer values (bf16 weights 1, integer sums in fp32).
+    import torch
+    say(f"uniform scores T{T} W{W}")
+    H = 2
+    v = (np.arange(T)[None, :, None, None] % 7 * 3 + np.arange(64)[None, None, None, :] % 5
+         + np.arange(H)[None, None, :, None]).astype(np.float32) * np.ones((1, T, H, 64), np.float32)
+    z = torch.zeros((1, T, H, 64), dtype=torch.bfloat16, device="cuda")
+    o = host(vx.prefill(z, z, dev(v, "bf16"), window=W, out_dtype="f32"))
+    c = np.cumsum(np.concatenate([np.zeros((1, 1, H, 64)), v], axis=1), axis=1)
+    t = np.arange(T)
+    lo = np.maximum(0, t - W + 1)
+    want = (c[:, t + 1] - c[:, lo]) / (t - lo + 1)[None, :, None, None]
+    np.testing.assert_allclose(o, want, rtol=0, atol=1e-5)
