@@ -233,7 +233,7 @@ def main():
             "traffic": None,
         },
         "roofline_stream": {
-            "kernel": "stream_step_kernel",
+            "kernel": "stream_step_mfma_kernel",
             "bound": "hbm",
             "achieved": round(stream_gbs, 1),
             "peak": PEAK_HBM_GBS,

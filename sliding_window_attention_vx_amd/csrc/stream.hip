@@ -309,6 +309,254 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreq
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 streaming step on matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// One wave per (stream, head, chunk of up to 16 new queries): the 16 query
+// columns of the MFMA hold the chunk (4 in the Voxtral schedule; the rest are
+// zero).  Keys are processed in blocks of 32:
+//   S^T = K' Q'^T  two 16-key MFMA pairs; the A operand (16 keys x 8 dims per
+//                  lane) is loaded straight from the ring in HBM; new keys are
+//                  rotated in registers (dims d and d+32 sit in the same lane).
+//   softmax        lane (q, g) holds query q's scores for keys 4g..4g+3 and
+//                  16+4g..16+4g+3; the row max/sum reduce over the four lanes
+//                  of q with v_permlane16_swap / v_permlane32_swap; lazy
+//                  running max as in the prefill.
+//   O^T += V^T P^T V goes HBM -> VGPR -> this wave's LDS (160-byte rows) and
+//                  comes back through ds_read_b64_tr_b16, which hands a lane
+//                  four consecutive keys of one dim: exactly the key order
+//                  of the score registers.
+// The next block's K and V loads are issued before the current block's math,
+// so each wave keeps 16 KB of ring reads in flight.
+constexpr int kSQ = 16;                    // query columns per wave
+constexpr int kSRowV = 160;                // LDS bytes per staged V row (conflict-free)
+constexpr int kSBufV = 32 * kSRowV;        // one 32-key V block
+
+__device__ __forceinline__ float max16x(float x) {  // max over lanes l, l^16
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max32x(float x) {  // max over lanes l, l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum16x(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32x(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 s_lds_bf16x4;
+
+template <typename TO>
+__global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, RopeFreqs fr) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* cs = (float*)smem;                                  // [i1][2][32] cos/sin
+  char* vbuf = smem + align16((size_t)a.n * kD * sizeof(float));  // 2 x 32 V rows
+  const int H = a.H, W = a.W, n = a.n;
+  const int s = blockIdx.x / H, h = blockIdx.x % H;
+  const int i0 = blockIdx.y * kSQ;
+  const int i1 = min(n, i0 + kSQ);
+  const int nq = i1 - i0;
+  const int lane = threadIdx.x;
+  const int q = lane & 15, g = lane >> 4;
+
+  const int64_t P = a.pos[s];
+  const int64_t lo = max((int64_t)0, P + i0 - W + 1);
+  const int nring = (int)max((int64_t)0, P - lo);  // ring keys at positions lo .. P-1
+  const int nk = nring + i1;                       // then new frames 0 .. i1-1
+  const int lo_slot = (int)(lo % W);
+  const size_t frs = (size_t)H * kD;
+  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
+  const bf16* __restrict__ qn = (const bf16*)a.q + fbase;
+  const bf16* __restrict__ kn = (const bf16*)a.k + fbase;
+  const bf16* __restrict__ vn = (const bf16*)a.v + fbase;
+  const size_t rbase = ((size_t)s * H + h) * (size_t)W * kD;
+  const bf16* __restrict__ rk = (const bf16*)a.ring_k + rbase;
+  const bf16* __restrict__ rv = (const bf16*)a.ring_v + rbase;
+  const bool rope = a.rope;
+
+  // cos/sin of the new positions P .. P+i1-1 (float64 angle, as everywhere)
+  if (rope) {
+    for (int u = lane; u < i1 * kHalf; u += 64) {
+      const int j = u / kHalf, f = u % kHalf;
+      float cc, ss;
+      rope_cs(P + j, fr.f[f], &cc, &ss);
+      cs[j * kD + f] = cc;
+      cs[j * kD + kHalf + f] = ss;
+    }
+  }
+  __syncthreads();
+
+  // rotated new row j (dims 8g..8g+7 and 32+8g..32+8g+7) as two bf16x8 words
+  auto new_row = [&](const bf16* base, int j, u32x4& x, u32x4& y) {
+    x = *reinterpret_cast<const u32x4*>(base + (size_t)j * frs + 8 * g);
+    y = *reinterpret_cast<const u32x4*>(base + (size_t)j * frs + kHalf + 8 * g);
+    if (rope) {
+      float xf[8], yf[8];
+      unpack8(x, xf);
+      unpack8(y, yf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float xo, yo;
+        rope_pair(xf[e], yf[e], cs[j * kD + 8 * g + e], cs[j * kD + kHalf + 8 * g + e], &xo, &yo);
+        xf[e] = xo;
+        yf[e] = yo;
+      }
+      x = pack8(xf);
+      y = pack8(yf);
+    }
+  };
+
+  // Q' (B operand): lane (q, g) holds query i0+q, dims 8g.. (m=0) and 32+8g.. (m=1)
+  bf16x8 qf[2];
+  {
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+    if (q < nq) new_row(qn, i0 + q, x, y);
+    qf[0] = __builtin_bit_cast(bf16x8, x);
+    qf[1] = __builtin_bit_cast(bf16x8, y);
+  }
+
+  // per-block loads: K A-operand rows (2 sub-blocks x 2 dim halves) and V rows
+  struct Blk {
+    u32x4 k[2][2];  // [sub-block][dim half]
+    u32x4 v[4];     // 4 x (8 rows x 16 bytes) of the 32 V rows
+  };
+  auto load_blk = [&](int kb, Blk& B) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int kk = kb + 16 * sb + q;  // key of this lane's A row
+      if (kk < nring) {
+        int slot = lo_slot + kk;
+        if (slot >= W) slot -= W;
+        const bf16* kr = rk + (size_t)slot * kD + 8 * g;
+        B.k[sb][0] = *reinterpret_cast<const u32x4*>(kr);
+        B.k[sb][1] = *reinterpret_cast<const u32x4*>(kr + kHalf);
+      } else if (kk < nk) {
+        new_row(kn, kk - nring, B.k[sb][0], B.k[sb][1]);
+      } else {
+        B.k[sb][0] = u32x4{0, 0, 0, 0};
+        B.k[sb][1] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * j + (lane >> 3), c = lane & 7;
+      const int kk = kb + row;
+      if (kk < nring) {
+        int slot = lo_slot + kk;
+        if (slot >= W) slot -= W;
+        B.v[j] = *reinterpret_cast<const u32x4*>(rv + (size_t)slot * kD + 8 * c);
+      } else if (kk < nk) {
+        B.v[j] = *reinterpret_cast<const u32x4*>(vn + (size_t)(kk - nring) * frs + 8 * c);
+      } else {
+        B.v[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  // tr16 read address: lane L of group g points at row 4g + L/4, dims 4*(L%4)
+  const int v_off = (4 * g + (q >> 2)) * kSRowV + 4 * (q & 3) * 2;
+  const float c2 = a.scale_log2;
+  const int64_t pq = P + i0 + q;  // this lane's query position
+  f32x4 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int nblk = (nk + 31) / 32;
+  Blk cur, nxt;
+  load_blk(0, cur);
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int kb = 32 * bi;
+    if (bi + 1 < nblk) load_blk(kb + 32, nxt);
+    char* vb = vbuf + (bi & 1) * kSBufV;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(vb + (8 * j + (lane >> 3)) * kSRowV + 16 * (lane & 7)) = cur.v[j];
+
+    f32x4 sc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[sb][0]),
+                                                    qf[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[sb][1]),
+                                                    qf[1], acc, 0, 0, 0);
+      sc[sb] = acc;
+    }
+    // mask: key kb+16sb+4g+r sits at position lo+kk (ring) or P+(kk-nring) (new)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kb + 16 * sb + 4 * g + r;
+        const int64_t pk = kk < nring ? lo + kk : P + (kk - nring);
+        const bool ok = (q < nq) && (kk < nk) && (pk <= pq) && (pk > pq - W);
+        sc[sb][r] = ok ? sc[sb][r] : -INFINITY;
+        mx = fmaxf(mx, sc[sb][r]);
+      }
+    mx = max32x(max16x(mx)) * c2;
+    const bool need = mx > m_run + 8.0f;
+    if (__any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float p[8];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[4 * sb + r] = __builtin_amdgcn_exp2f(fmaf(sc[sb][r], c2, -mu));
+    const u32x4 pw = pack8(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_run = dot2_ones(pw[i], l_run);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+    __syncthreads();  // V rows of this block are in LDS
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const char* p0 = vb + v_off + 32 * db;
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((s_lds_bf16x4*)p0);
+      const bf16x4 vb2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((s_lds_bf16x4*)(p0 + 16 * kSRowV));
+      const bf16x8 vf = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+
+  // O^T[d = 16db + 4g + r][q]; the row sum is spread over the four lanes of q
+  const float l_tot = sum32x(sum16x(l_run));
+  if (q < nq) {
+    const float inv = 1.f / l_tot;
+    TO* op = (TO*)a.o + fbase + (size_t)(i0 + q) * frs;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      if constexpr (sizeof(TO) == 2) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+        w.y = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
+        *reinterpret_cast<uint2*>(op + d0) = w;
+      } else {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[db][e] * inv;
+        *reinterpret_cast<f32x4*>(op + d0) = w;
+      }
+    }
+  }
+}
+
 template <typename TI>
 __global__ __launch_bounds__(256) void ring_append_kernel(AppendArgs a, RopeFreqs fr) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -373,12 +621,17 @@ hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreq
   dim3 grid((unsigned)(a.S * a.H), (unsigned)((a.n + kQC - 1) / kQC));
   const size_t elem = io == DT::BF16 ? 2 : 4;
   const size_t smem = StepLds(a.n, elem).total;
-  if (io == DT::F32)
+  if (io == DT::F32) {
     hipLaunchKernelGGL((stream_step_kernel<float, float>), grid, dim3(256), smem, st, a, fr);
-  else if (out == DT::BF16)
-    hipLaunchKernelGGL((stream_step_kernel<bf16, bf16>), grid, dim3(256), smem, st, a, fr);
+    return hipGetLastError();
+  }
+  // bf16: matrix-core kernel, one wave per (stream, head, 16-query chunk)
+  dim3 grid16((unsigned)(a.S * a.H), (unsigned)((a.n + kSQ - 1) / kSQ));
+  const size_t smem16 = align16((size_t)a.n * kD * sizeof(float)) + 2 * kSBufV;
+  if (out == DT::BF16)
+    hipLaunchKernelGGL((stream_step_mfma_kernel<bf16>), grid16, dim3(64), smem16, st, a, fr);
   else
-    hipLaunchKernelGGL((stream_step_kernel<bf16, float>), grid, dim3(256), smem, st, a, fr);
+    hipLaunchKernelGGL((stream_step_mfma_kernel<float>), grid16, dim3(64), smem16, st, a, fr);
   return hipGetLastError();
 }
 
