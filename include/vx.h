@@ -132,6 +132,20 @@ vx_status vx_kv_ring_append(void *ring_k, void *ring_v, const void *k_new, const
                             int64_t *pos, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
                             const vx_attn_cfg *cfg, void *stream);
 
+/* One streaming step and its ring append in one call (one launch for bf16):
+ * the attention of vx_swa_attn_stream_step, then the rotated new keys and the
+ * new values are written to slots (pos_in[s] + i) mod W of the rings, and
+ * pos_out[s] = pos_in[s] + n.  Same shapes and dtypes as the two separate
+ * calls, and the same results bit for bit.  Requires 1 <= n <= min(W, 16)
+ * (one workgroup per ring, which writes it only after all its reads).
+ * pos_in and pos_out must be distinct arrays: some workgroups still read
+ * pos_in while another writes pos_out; swap the two for the next step. */
+vx_status vx_swa_attn_stream_step_append(const void *q_new, const void *k_new, const void *v_new,
+                                         void *ring_k, void *ring_v, const int64_t *pos_in,
+                                         int64_t *pos_out, void *o, int32_t S, int32_t n,
+                                         int32_t H, int32_t rope_applied, const vx_attn_cfg *cfg,
+                                         void *stream);
+
 /* Static description of a status code. */
 const char *vx_status_string(vx_status s);
 

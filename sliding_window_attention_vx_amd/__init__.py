@@ -15,6 +15,7 @@ import os
 
 __all__ = [
     "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
+    "stream_step_append",
     "WINDOW", "THETA", "HEAD_DIM",
 ]
 
@@ -57,6 +58,9 @@ _SIGS = {
                                                _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
     "vx_kv_ring_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                          ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_stream_step_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _i32, _i32, _i32, _i32,
+                                                      ctypes.POINTER(_Cfg), _vp]),
     "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vx_last_error": (ctypes.c_char_p, []),
     "vx_version": (_i32, []),
@@ -247,3 +251,31 @@ def ring_append(ring_k, ring_v, k_new, v_new, pos, window=WINDOW, theta=THETA, r
     _check(lib().vx_kv_ring_append(_ptr(ring_k), _ptr(ring_v), _ptr(k_new), _ptr(v_new), _ptr(pos),
                                    S, n, H, int(bool(rope_applied)), ctypes.byref(cfg),
                                    _stream(k_new)), "vx_kv_ring_append")
+
+
+def stream_step_append(q_new, k_new, v_new, ring_k, ring_v, pos_in, pos_out, window=WINDOW,
+                       theta=THETA, scale=0.0, rope_applied=False, out=None, out_dtype=None):
+    """Streaming step plus ring append in one call; pos_out[s] = pos_in[s] + n (distinct arrays)."""
+    import torch
+    for name, x in (("q_new", q_new), ("k_new", k_new), ("v_new", v_new), ("ring_k", ring_k),
+                    ("ring_v", ring_v), ("pos_in", pos_in), ("pos_out", pos_out)):
+        _dev_tensor(x, name)
+    S, n, H = _stream_shapes(q_new, ring_k, ring_v, pos_in, window)
+    if pos_out.shape != pos_in.shape or pos_out.dtype != pos_in.dtype:
+        raise ValueError("pos_out must be int64 [S]")
+    if k_new.shape != q_new.shape or v_new.shape != q_new.shape:
+        raise ValueError("q_new, k_new, v_new must have the same shape")
+    io = _dt(q_new)
+    if any(_dt(x) != io for x in (k_new, v_new, ring_k, ring_v)):
+        raise ValueError("new frames and rings must share a dtype")
+    od = out_dtype or (_dt(out) if out is not None else io)
+    if out is None:
+        out = torch.empty(q_new.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q_new.device)
+    _dev_tensor(out, "out")
+    cfg = Config(window, theta, scale, io, od).c()
+    _check(lib().vx_swa_attn_stream_step_append(
+        _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos_in),
+        _ptr(pos_out), _ptr(out), S, n, H, int(bool(rope_applied)), ctypes.byref(cfg),
+        _stream(q_new)), "vx_swa_attn_stream_step_append")
+    return out

@@ -534,6 +534,27 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
     cur = nxt;
   }
 
+  if (a.append) {
+    // fused append (one chunk per (stream, head), so every ring read of this
+    // ring is done): rotated new keys and raw values go to slot (P+j) mod W.
+    const int j = q;
+    if (j < n) {
+      int slot = (int)(((P % W) + W) % W) + j;
+      if (slot >= W) slot -= W;
+      u32x4 x, y;
+      new_row(kn, j, x, y);
+      bf16* wk = (bf16*)a.ring_k_w + rbase + (size_t)slot * kD;
+      bf16* wv = (bf16*)a.ring_v_w + rbase + (size_t)slot * kD;
+      *reinterpret_cast<u32x4*>(wk + 8 * g) = x;
+      *reinterpret_cast<u32x4*>(wk + kHalf + 8 * g) = y;
+      *reinterpret_cast<u32x4*>(wv + 8 * g) =
+          *reinterpret_cast<const u32x4*>(vn + (size_t)j * frs + 8 * g);
+      *reinterpret_cast<u32x4*>(wv + kHalf + 8 * g) =
+          *reinterpret_cast<const u32x4*>(vn + (size_t)j * frs + kHalf + 8 * g);
+    }
+    if (h == 0 && lane == 0) a.pos_out[s] = P + n;
+  }
+
   // O^T[d = 16db + 4g + r][q]; the row sum is spread over the four lanes of q
   const float l_tot = sum32x(sum16x(l_run));
   if (q < nq) {
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(256) void ring_append_kernel(AppendArgs a, RopeFreq
     store8(rvp + kHalf, vy8);
   }
   __syncthreads();
-  if (tid == 0) a.pos[s] = P + n;
+  if (tid == 0) a.pos_out[s] = P + n;
 }
 
 }  // namespace

@@ -261,6 +261,7 @@ vx_status vx_kv_ring_append(void* ring_k, void* ring_v, const void* k_new, const
   a.k = k_new;
   a.v = v_new;
   a.pos = pos;
+  a.pos_out = pos;
   a.S = S;
   a.n = n;
   a.H = H;
@@ -269,6 +270,77 @@ vx_status vx_kv_ring_append(void* ring_k, void* ring_v, const void* k_new, const
   (void)hipGetLastError();
   return launched(vx::launch_ring_append(a, to_dt(cfg->io_dtype), rope_freqs(cfg->rope_theta),
                                          (hipStream_t)stream));
+}
+
+vx_status vx_swa_attn_stream_step_append(const void* q_new, const void* k_new, const void* v_new,
+                                         void* ring_k, void* ring_v, const int64_t* pos_in,
+                                         int64_t* pos_out, void* o, int32_t S, int32_t n,
+                                         int32_t H, int32_t rope_applied, const vx_attn_cfg* cfg,
+                                         void* stream) {
+  vx_status st = check_stream_common("stream_step_append", S, n, H, cfg);
+  if (st) return st;
+  if (n > vx::kStreamFusedMaxNew)
+    return fail(VX_E_RANGE, "stream_step_append: at most %d new frames per step (got %d)",
+                vx::kStreamFusedMaxNew, n);
+  if (S == 0) return ok();
+  if (!q_new || !k_new || !v_new || !ring_k || !ring_v || !pos_in || !pos_out || !o)
+    return fail(VX_E_NULL, "stream_step_append: a tensor pointer is NULL");
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) ||
+      !aligned16(ring_v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "stream_step_append: tensors must be 16-byte aligned");
+  if (((uintptr_t)pos_in & 7u) != 0 || ((uintptr_t)pos_out & 7u) != 0)
+    return fail(VX_E_ALIGN, "stream_step_append: pos_in/pos_out must be 8-byte aligned");
+  const size_t nf = (size_t)S * n * H * vx::kD;
+  const size_t ob = nf * elem_size(cfg->out_dtype), ib = nf * elem_size(cfg->io_dtype);
+  const size_t rb = (size_t)S * H * cfg->window * vx::kD * elem_size(cfg->io_dtype);
+  const size_t pb = (size_t)S * sizeof(int64_t);
+  if (overlap(pos_in, pb, pos_out, pb))
+    return fail(VX_E_RANGE, "stream_step_append: pos_in and pos_out must not overlap");
+  if (overlap(ring_k, rb, ring_v, rb))
+    return fail(VX_E_RANGE, "stream_step_append: ring_k and ring_v overlap");
+  if (overlap(o, ob, q_new, ib) || overlap(o, ob, k_new, ib) || overlap(o, ob, v_new, ib) ||
+      overlap(o, ob, ring_k, rb) || overlap(o, ob, ring_v, rb))
+    return fail(VX_E_RANGE, "stream_step_append: o overlaps an input");
+  vx::StreamArgs a{};
+  a.q = q_new;
+  a.k = k_new;
+  a.v = v_new;
+  a.ring_k = ring_k;
+  a.ring_v = ring_v;
+  a.pos = pos_in;
+  a.o = o;
+  a.S = S;
+  a.n = n;
+  a.H = H;
+  a.W = cfg->window;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  const vx::RopeFreqs fr = rope_freqs(cfg->rope_theta);
+  (void)hipGetLastError();
+  if (cfg->io_dtype == VX_BF16) {
+    a.append = true;
+    a.ring_k_w = ring_k;
+    a.ring_v_w = ring_v;
+    a.pos_out = pos_out;
+    return launched(vx::launch_stream_step(a, vx::DT::BF16, to_dt(cfg->out_dtype), fr,
+                                           (hipStream_t)stream));
+  }
+  // float32: the two kernels back to back on the same stream
+  vx_status s1 = launched(vx::launch_stream_step(a, vx::DT::F32, vx::DT::F32, fr, (hipStream_t)stream));
+  if (s1) return s1;
+  vx::AppendArgs b{};
+  b.ring_k = ring_k;
+  b.ring_v = ring_v;
+  b.k = k_new;
+  b.v = v_new;
+  b.pos = pos_in;
+  b.pos_out = pos_out;
+  b.S = S;
+  b.n = n;
+  b.H = H;
+  b.W = cfg->window;
+  b.rope = a.rope;
+  return launched(vx::launch_ring_append(b, vx::DT::F32, fr, (hipStream_t)stream));
 }
 
 const char* vx_status_string(vx_status s) {

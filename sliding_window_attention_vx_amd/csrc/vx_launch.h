@@ -35,6 +35,12 @@ struct StreamArgs {
   int S, n, H, W;
   bool rope;
   float scale_log2;
+  // fused append (n <= 16): write rotated new keys/values into the ring after
+  // all reads and set pos_out[s] = pos[s] + n (pos_out != pos)
+  bool append;
+  void* ring_k_w;
+  void* ring_v_w;
+  int64_t* pos_out;
 };
 
 struct AppendArgs {
@@ -42,7 +48,8 @@ struct AppendArgs {
   void* ring_v;
   const void* k;
   const void* v;
-  int64_t* pos;
+  const int64_t* pos;  // read
+  int64_t* pos_out;    // written: pos_out[s] = pos[s] + n (may equal pos)
   int S, n, H, W;
   bool rope;
 };
@@ -58,5 +65,6 @@ hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreq
 hipError_t launch_ring_append(const AppendArgs& a, DT io, const RopeFreqs& fr, hipStream_t st);
 
 constexpr int kStreamMaxNew = 64;  // largest n accepted by the streaming kernels (LDS use)
+constexpr int kStreamFusedMaxNew = 16;  // largest n of the fused step + append
 
 }  // namespace vx

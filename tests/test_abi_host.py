@@ -39,8 +39,8 @@ def L():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for f in ("vx_rope_qk", "vx_swa_attn_prefill", "vx_swa_attn_stream_step", "vx_kv_ring_append",
-              "vx_rope_table", "vx_status_string", "vx_last_error", "vx_version",
-              "vx_default_cfg"):
+              "vx_swa_attn_stream_step_append", "vx_rope_table", "vx_status_string",
+              "vx_last_error", "vx_version", "vx_default_cfg"):
         assert f in names
 
 
@@ -210,6 +210,27 @@ def test_ring_append_argument_errors(L):
     r = b.new()
     assert call(rk=r, rv=r) == E_RANGE
     assert call(S=-2) == E_SHAPE
+    assert b.untouched()
+
+
+def test_stream_step_append_errors(L):
+    b = Bufs()
+    c = cfg(window=750)
+
+    def call(S=2, n=4, H=2, **ov):
+        a = dict(q=b.new(), k=b.new(), v=b.new(), rk=b.new(), rv=b.new(), pin=b.new(),
+                 pout=b.new(), o=b.new())
+        a.update(ov)
+        return L.vx_swa_attn_stream_step_append(a["q"], a["k"], a["v"], a["rk"], a["rv"], a["pin"],
+                                                a["pout"], a["o"], S, n, H, 0, ctypes.byref(c), None)
+    assert call(n=17) == E_RANGE  # above the fused cap
+    assert call(n=0) == E_RANGE
+    p = b.new()
+    assert call(pin=p, pout=p) == E_RANGE  # pos_in and pos_out must differ
+    assert call(pout=ctypes.c_void_p(0)) == E_NULL
+    assert call(pout=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    r = b.new()
+    assert call(rk=r, o=r) == E_RANGE
     assert b.untouched()
 
 

@@ -354,3 +354,46 @@ def test_prefill_uniform_scores_closed_form(T, W):
     lo = np.maximum(0, t - W + 1)
     want = (c[:, t + 1] - c[:, lo]) / (t - lo + 1)[None, :, None, None]
     np.testing.assert_allclose(o, want, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("io,n", [("bf16", 1), ("bf16", 4), ("bf16", 16), ("f32", 4)])
+def test_fused_step_append_equals_two_calls(io, n):
+    # vx_swa_attn_stream_step_append == vx_swa_attn_stream_step + vx_kv_ring_append, bit for bit
+    import torch
+    S, H, W = 6, 4, 750
+    say(f"fused step+append io {io} n {n}")
+    st = synth.make_stream_state(S, H, W, seed=21, pos_lo=0 + W, pos_hi=20000, dtype=io)
+    fr = synth.make_stream_frames(S, n, H, seed=21, step=0, dtype=io)
+    rk, rv, pos = _stream_state_dev(st, io)
+    qn, kn, vn = (dev(fr[x], io) for x in ("q", "k", "v"))
+    rk2, rv2, pos_in = rk.clone(), rv.clone(), pos.clone()
+    o1 = vx.stream_step(qn, kn, vn, rk, rv, pos, window=W)
+    vx.ring_append(rk, rv, kn, vn, pos, window=W)
+    pos_out = torch.full_like(pos_in, -1)
+    o2 = vx.stream_step_append(qn, kn, vn, rk2, rv2, pos_in, pos_out, window=W)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(rk, rk2) and torch.equal(rv, rv2)
+    assert torch.equal(pos, pos_out)
+    assert torch.equal(pos_in, torch.from_numpy(st["pos"]).cuda())  # pos_in untouched
+
+
+def test_fused_stream_equals_prefill():
+    import torch
+    W, T = 64, 200
+    x = synth.make_prefill(3, T, 2, seed=303, dtype="bf16", scale=0.5)
+    qd, kd, vd = (dev(x[n], "bf16") for n in ("q", "k", "v"))
+    rk = torch.full((3, 2, W, 64), float("nan"), device="cuda").bfloat16()
+    rv = rk.clone()
+    pa = torch.zeros(3, dtype=torch.int64, device="cuda")
+    pb = torch.empty_like(pa)
+    outs = []
+    for t in range(0, T, 4):
+        sl = slice(t, t + 4)
+        outs.append(vx.stream_step_append(qd[:, sl].contiguous(), kd[:, sl].contiguous(),
+                                          vd[:, sl].contiguous(), rk, rv, pa, pb, window=W,
+                                          out_dtype="f32"))
+        pa, pb = pb, pa
+    got = host(torch.cat(outs, dim=1))
+    assert np.all(host(pa.double()) == T)
+    check_bf16(got, oracle.prefill(x["q"], x["k"], x["v"], W, bf16=True), "fused stream vs oracle")
