@@ -89,45 +89,38 @@ struct Stage {
   u32x4 v[UV];
 };
 
+// Global loads of the next tile into registers.  Rows at or past T are
+// clamped to T-1 instead of being skipped: their keys lie after every stored
+// query, so causality masks them, and the clamped values are finite.  The
+// loads are unconditional on purpose: conditional loads merged with zero fills
+// made the compiler copy the landing registers right after issuing them, which
+// waited for the loads and serialized the double buffering.
 template <int NW>
 __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
                                            const bf16* __restrict__ v, size_t rs, int T, int kt0,
                                            bool rope, const float* __restrict__ table,
                                            int64_t row0, int tid) {
   constexpr int NT = Stage<NW>::NT;
-  const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UK; ++j) {
     int r, cp;
     k_unit(tid + j * NT, r, cp);
-    const int key = kt0 + r;
-    if (key < T) {
-      const bf16* kp = k + (size_t)key * rs + 8 * cp;
-      st.kx[j] = *reinterpret_cast<const u32x4*>(kp);
-      st.ky[j] = *reinterpret_cast<const u32x4*>(kp + kHalf);
-      if (rope) {
-        const float* cs = table + (row0 + key) * kD + 8 * cp;
-        load8(cs, st.kc[j]);
-        load8(cs + kHalf, st.ks[j]);
-      }
-    } else {
-      st.kx[j] = zero;
-      st.ky[j] = zero;
-      if (rope) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          st.kc[j][e] = 1.f;
-          st.ks[j][e] = 0.f;
-        }
-      }
+    const int key = min(kt0 + r, T - 1);
+    const bf16* kp = k + (size_t)key * rs + 8 * cp;
+    st.kx[j] = *reinterpret_cast<const u32x4*>(kp);
+    st.ky[j] = *reinterpret_cast<const u32x4*>(kp + kHalf);
+    if (rope) {
+      const float* cs = table + (row0 + key) * kD + 8 * cp;
+      load8(cs, st.kc[j]);
+      load8(cs + kHalf, st.ks[j]);
     }
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
     int r, c;
     v_unit(tid + j * NT, r, c);
-    const int key = kt0 + r;
-    st.v[j] = key < T ? *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c) : zero;
+    const int key = min(kt0 + r, T - 1);
+    st.v[j] = *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c);
   }
 }
 
@@ -326,30 +319,32 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
     }
     if (act[0] || act[1]) {
-      f32x16 sc[2];
-      float mx = -INFINITY;
+      // Software pipeline over the two 32-key halves: the second half's score
+      // MFMAs are issued before the first half's softmax, so the matrix core
+      // runs while the VALU computes exponentials.
+      f32x16 s_cur = act[0] ? s_half(0) : s_half(1);
+      f32x16 s_nxt = f32x16{};
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         if (!act[sb]) continue;
-        f32x16 acc = s_half(sb);
         if (msk[sb]) {
           // key of register r: kb + 4hh + 8(r/4) + r%4; keep iff 0 <= tq - key <= W-1
           const int d0 = tq - (kt0 + 32 * sb + 4 * hh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 8 * (r >> 2) + (r & 3);
-            acc[r] = ((unsigned)(d0 - off) <= wm1) ? acc[r] : -INFINITY;
+            s_cur[r] = ((unsigned)(d0 - off) <= wm1) ? s_cur[r] : -INFINITY;
           }
         }
+        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-        sc[sb] = acc;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+        if (sb == 0 && act[1]) s_nxt = s_half(1);
+        update_max(mx);
+        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+        pv_half(s_cur, sb, mu);
+        s_cur = s_nxt;
       }
-      update_max(mx);
-      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-        if (act[sb]) pv_half(sc[sb], sb, mu);
     }
 
     if (more) stage_commit<NW>(st, lds + (buf ^ 1) * kStageBytes,
