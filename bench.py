@@ -58,7 +58,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=10,
+    ap.add_argument("--cpu-reps", type=int, default=60,
                     help="oracle repetitions of the prefill workload for the CPU baseline")
     ap.add_argument("--only", choices=["prefill", "stream", "copy"], default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
