@@ -171,8 +171,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const int per_xcd = gridDim.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (logical >= n_logical) return;
-  const int qt = logical % n_qtiles;
-  const int bh = logical / n_qtiles;
+  // Longest work first: within each chunk of kGroup (batch, head) pairs the
+  // dispatch order is query tile descending, then head.  The first query
+  // tiles of a sequence have short key ranges (their band is cut at key 0),
+  // so they are dispatched last and land on CUs that already hold a long
+  // workgroup, instead of two long workgroups sharing one CU.
+  constexpr int kGroup = 4;
+  const int n_bh = a.B * a.H;
+  const int chunk = logical / (kGroup * n_qtiles);
+  const int in_chunk = logical - chunk * kGroup * n_qtiles;
+  const int gc = min(kGroup, n_bh - chunk * kGroup);  // pairs in this chunk
+  const int qt = n_qtiles - 1 - in_chunk / gc;
+  const int bh = chunk * kGroup + in_chunk % gc;
   const int h = bh % a.H, b = bh / a.H;
 
   const int tid = threadIdx.x;
