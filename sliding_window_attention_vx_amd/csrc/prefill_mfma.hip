@@ -160,29 +160,40 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
 
 template <int NW, typename TO>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
-                                                                  int n_logical) {
+                                                                  int n_short, int hx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   constexpr int BM = NW * 32;
 
-  // XCD-aware order: the grid is a multiple of 8 and the dispatcher deals
-  // workgroups round-robin to the 8 XCDs; give each XCD a contiguous run of
-  // query tiles of the same (batch, head) so neighbouring tiles share K/V in
-  // that XCD's L2.
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (logical >= n_logical) return;
-  // Longest work first: within each chunk of kGroup (batch, head) pairs the
-  // dispatch order is query tile descending, then head.  The first query
-  // tiles of a sequence have short key ranges (their band is cut at key 0),
-  // so they are dispatched last and land on CUs that already hold a long
-  // workgroup, instead of two long workgroups sharing one CU.
-  constexpr int kGroup = 4;
+  // Work order.  The dispatcher deals workgroups round-robin to the 8 XCDs
+  // (workgroup id mod 8), and each XCD has its own L2.  With at least 8
+  // (batch, head) pairs, XCD x owns pairs [x*hx, (x+1)*hx) and runs first
+  // their full-length query tiles, pair by pair so that neighbouring tiles
+  // share K/V in its L2, then the n_short leading query tiles, whose band is
+  // cut at key 0, longest first.  The short ones thus arrive last and pair up
+  // with a long workgroup on a CU that still has room, instead of two long
+  // workgroups sharing one CU.  With fewer pairs every XCD takes query tiles
+  // of every pair, in the same longest-first order.
   const int n_bh = a.B * a.H;
-  const int chunk = logical / (kGroup * n_qtiles);
-  const int in_chunk = logical - chunk * kGroup * n_qtiles;
-  const int gc = min(kGroup, n_bh - chunk * kGroup);  // pairs in this chunk
-  const int qt = n_qtiles - 1 - in_chunk / gc;
-  const int bh = chunk * kGroup + in_chunk % gc;
+  int bh, qt;
+  if (hx > 0) {
+    const int i = blockIdx.x >> 3;
+    const int n_long = n_qtiles - n_short;
+    int bl;
+    if (i < hx * n_long) {
+      bl = i / n_long;
+      qt = n_short + i % n_long;
+    } else {
+      const int j = i - hx * n_long;
+      qt = n_short - 1 - j / hx;
+      bl = j % hx;
+    }
+    bh = (blockIdx.x & 7) * hx + bl;
+    if (bh >= n_bh) return;
+  } else {
+    const int i = blockIdx.x;
+    qt = n_qtiles - 1 - i / n_bh;
+    bh = i % n_bh;
+  }
   const int h = bh % a.H, b = bh / a.H;
 
   const int tid = threadIdx.x;
@@ -392,14 +403,16 @@ template <int NW>
 hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   constexpr int BM = NW * 32;
   const int n_qtiles = (a.T + BM - 1) / BM;
-  const int64_t n_logical = (int64_t)n_qtiles * a.H * a.B;
-  const int64_t grid = (n_logical + 7) / 8 * 8;
+  const int n_short = min(n_qtiles, (a.W - 1 + BM - 1) / BM);  // tiles with q0 < W-1
+  const int n_bh = a.B * a.H;
+  const int hx = n_bh >= 8 ? (n_bh + 7) / 8 : 0;
+  const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
   if (out == DT::BF16)
     hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
-                       a, n_qtiles, (int)n_logical);
+                       a, n_qtiles, n_short, hx);
   else
     hipLaunchKernelGGL((prefill_mfma_kernel<NW, float>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       st, a, n_qtiles, (int)n_logical);
+                       st, a, n_qtiles, n_short, hx);
   return hipGetLastError();
 }
 
