@@ -216,6 +216,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   // ---- Q' fragments (B operand of S^T = K' Q'^T) -------------------------
   // MFMA step m covers dims 16m .. 16m+15; lane half hh holds dims 16m+8hh+(0..7),
   // i.e. chunk 2m+hh of 8 dims.  Chunks c and c+4 are RoPE partners.
+  // The workgroup's rows of the cos/sin table are staged through LDS first:
+  // each load instruction then reads 1 KB of consecutive table bytes, where
+  // per-lane reads of a lane's own row would touch one 256-byte row per lane.
+  // Rows are padded to kRowQT bytes so the per-lane LDS reads below hit
+  // distinct banks.  The region is reused by the first K/V tile afterwards.
+  constexpr int kRowQT = 4 * kD + 16;
+  static_assert(BM * kRowQT <= 2 * kStageBytes, "Q table rows must fit in LDS");
+  if (rope) {
+    constexpr int NT = NW * 64;
+#pragma unroll
+    for (int j = 0; j < BM * 16 / NT; ++j) {
+      const int i = tid + j * NT;
+      const int r = i >> 4, c = i & 15;
+      const int row = min(q0 + r, T - 1);
+      const u32x4 val =
+          *reinterpret_cast<const u32x4*>(a.table + (a.table_row0 + row) * kD + 4 * c);
+      *reinterpret_cast<u32x4*>(lds + r * kRowQT + 16 * c) = val;
+    }
+    __syncthreads();
+  }
   bf16x8 qf[4];
   if (tq < T) {
     const bf16* qp = q + (size_t)tq * rs;
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * c);
       u32x4 y = *reinterpret_cast<const u32x4*>(qp + kHalf + 8 * c);
       if (rope) {
-        const float* cs = a.table + (a.table_row0 + tq) * kD + 8 * c;
+        const float* cs = reinterpret_cast<const float*>(lds + (tq - q0) * kRowQT) + 8 * c;
         float cc[8], ss[8], xf[8], yf[8];
         load8(cs, cc);
         load8(cs + kHalf, ss);
@@ -268,6 +288,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
 
   Stage<NW> st;
   stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
+  if (rope) __syncthreads();  // every wave has read its Q table rows
   stage_commit<NW>(st, lds, lds + kTileK, rope, tid);
   __syncthreads();
 
