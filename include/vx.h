@@ -106,6 +106,37 @@ vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void 
                               const float *rope_table, int64_t table_p0, int64_t table_len,
                               const vx_attn_cfg *cfg, void *stream);
 
+/* Batched first-chunk prefill over streams of different lengths, which can
+ * also seed each stream's KV ring for the streaming step (Voxtral Mini 4B
+ * Realtime Core AI page: the batched first-chunk encoder, one call for the
+ * whole first chunk, then the streaming encoder for later chunks).
+ * Stream s has T_s = cu_seqlens[s+1] - cu_seqlens[s] frames at positions
+ * 0 .. T_s - 1, packed along the frame axis: q, k, v and o are
+ * [total, H, D] with stream s at rows cu_seqlens[s] .. cu_seqlens[s+1]-1;
+ * each frame attends as in vx_swa_attn_prefill, within its own stream only.
+ * total: the number of packed rows (the host size of q, k, v and o).
+ * cu_seqlens: device int32 [S+1], cu_seqlens[0] = 0, non-decreasing, with
+ *   cu_seqlens[S] = total.  The kernel clamps every offset to [0, total] and
+ *   a negative length counts as 0, so a wrong array cannot reach outside
+ *   the buffers.
+ * max_T: host bound with T_s <= max_T for every s (rows of a longer stream
+ *   past max_T are not computed); max_T <= W is the full-causal case.
+ * bf16 input only (VX_E_DTYPE otherwise); o is bf16 or float32.
+ * RoPE as in vx_swa_attn_prefill with pos0 = 0: the table must cover
+ *   positions 0 .. max_T - 1 unless rope_applied != 0.
+ * ring_k, ring_v: [S, H, W, D] bf16 rings, or both NULL for no seeding.
+ *   When given, the rotated keys and the values of frames
+ *   t >= T_s - W are written to slot t mod W of stream s (other slots keep
+ *   their contents) and pos[s] (device int64 [S], required) is set to T_s:
+ *   the state after appending the whole first chunk, ready for
+ *   vx_swa_attn_stream_step at position T_s.  Seeding needs max_T >= 1. */
+vx_status vx_swa_attn_prefill_varlen(const void *q, const void *k, const void *v, void *o,
+                                     const int32_t *cu_seqlens, int32_t S, int32_t total,
+                                     int32_t max_T, int32_t H, int32_t rope_applied, const float *rope_table,
+                                     int64_t table_p0, int64_t table_len, void *ring_k,
+                                     void *ring_v, int64_t *pos, const vx_attn_cfg *cfg,
+                                     void *stream);
+
 /* One streaming step for S independent streams with n new frames each
  * (1 <= n <= min(W, 64); a longer first chunk goes through the prefill).
  * q_new, k_new, v_new, o: [S,n,H,D]; ring_k (rotated keys) and ring_v: [S,H,W,D] in cfg->io_dtype; slot j of a ring holds the frame at

@@ -132,6 +132,36 @@ def prefill(q, k, v, W, pos=None, theta=1e6, scale=None, bf16=False, rope_applie
     return o
 
 
+def prefill_varlen(q, k, v, cu, W, ring_k=None, ring_v=None, pos=None, theta=1e6, bf16=False,
+                   rope_applied=False):
+    """Batched first-chunk prefill (Voxtral Mini 4B Realtime Core AI page: the
+    batched first-chunk encoder runs a stream's whole first chunk in one call,
+    the streaming encoder then continues from it).
+
+    q, k, v: [total, H, D]; stream s is rows cu[s] .. cu[s+1]-1, an independent
+    chunk at positions 0 .. T_s-1, attended exactly as prefill() does.  With
+    rings ([S,H,W,D] float64, modified in place) and pos (int64 [S]), the chunk
+    is then appended to stream s's ring from position 0 exactly as
+    ring_append() does, so pos[s] = T_s and the last W frames sit in their
+    slots.  A composition of prefill() and ring_append(); no new arithmetic.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(c) for c in cu]
+    o = np.zeros_like(q)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b > a:
+            o[a:b] = prefill(q[None, a:b], k[None, a:b], v[None, a:b], W, theta=theta, bf16=bf16,
+                             rope_applied=rope_applied)[0]
+        if ring_k is not None:
+            pos[s] = 0
+            for c in range(a, b, int(W)):  # ring_append takes at most W frames per call
+                e = min(b, c + int(W))
+                ring_append(ring_k[s:s + 1], ring_v[s:s + 1], k[None, c:e], v[None, c:e],
+                            pos[s:s + 1], W, theta=theta, bf16=bf16, rope_applied=rope_applied)
+    return o
+
+
 def stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, W, theta=1e6, scale=None, bf16=False,
                 rope_applied=False, nthreads=0):
     """One streaming step; q/k/v_new [S,n,H,D], rings [S,H,W,D], pos [S] -> o [S,n,H,D]."""

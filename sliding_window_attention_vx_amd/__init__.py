@@ -61,6 +61,9 @@ _SIGS = {
     "vx_swa_attn_stream_step_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                       _i32, _i32, _i32, _i32,
                                                       ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_prefill_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                  _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp,
+                                                  _vp, ctypes.POINTER(_Cfg), _vp]),
     "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vx_last_error": (ctypes.c_char_p, []),
     "vx_version": (_i32, []),
@@ -197,6 +200,56 @@ def prefill(q, k, v, window=WINDOW, pos0=0, theta=THETA, scale=0.0, rope_applied
     _check(lib().vx_swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, int(pos0),
                                      int(bool(rope_applied)), _ptr(table), int(table_p0), int(tlen),
                                      ctypes.byref(cfg), _stream(q)), "vx_swa_attn_prefill")
+    return out
+
+
+def prefill_varlen(q, k, v, cu_seqlens, max_T, window=WINDOW, theta=THETA, scale=0.0,
+                   rope_applied=False, table=None, ring_k=None, ring_v=None, pos=None, out=None,
+                   out_dtype=None):
+    """Batched first-chunk prefill: streams packed along the frame axis.
+
+    q, k, v: bf16 [total, H, 64]; stream s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1
+    (cu_seqlens: int32 device tensor [S+1]), at positions 0 .. T_s-1, T_s <= max_T.
+    With ring_k, ring_v ([S, H, W, 64] bf16) and pos (int64 [S]) the rings are
+    seeded with the chunk's last W rotated keys and values and pos[s] = T_s.
+    """
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        _dev_tensor(x, name)
+    if not (q.shape == k.shape == v.shape) or q.dim() != 3 or q.shape[-1] != HEAD_DIM:
+        raise ValueError("q, k, v must all be [total, H, 64]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [S+1]")
+    S = cu_seqlens.numel() - 1
+    H = q.shape[1]
+    io = _dt(q)
+    od = out_dtype or (_dt(out) if out is not None else io)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q.device)
+    _dev_tensor(out, "out")
+    if out.shape != q.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
+    tlen = 0
+    if not rope_applied:
+        if table is None:
+            table = rope_table(0, max(int(max_T), 1), theta, device=q.device)
+        _dev_tensor(table, "table")
+        tlen = table.shape[0]
+    if ring_k is not None:
+        for name, x in (("ring_k", ring_k), ("ring_v", ring_v), ("pos", pos)):
+            if x is None:
+                raise ValueError("ring seeding needs ring_k, ring_v and pos")
+            _dev_tensor(x, name)
+        if ring_k.shape != (S, H, window, HEAD_DIM) or ring_v.shape != ring_k.shape:
+            raise ValueError(f"rings must be [S, H, W, 64] = {(S, H, window, HEAD_DIM)}")
+        if pos.dtype != torch.int64 or pos.shape != (S,):
+            raise ValueError("pos must be int64 [S]")
+    cfg = Config(window, theta, scale, io, od).c()
+    _check(lib().vx_swa_attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), S, q.shape[0], int(max_T), H,
+        int(bool(rope_applied)), _ptr(table), 0, int(tlen), _ptr(ring_k), _ptr(ring_v), _ptr(pos),
+        ctypes.byref(cfg), _stream(q)), "vx_swa_attn_prefill_varlen")
     return out
 
 

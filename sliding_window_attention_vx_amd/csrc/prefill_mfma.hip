@@ -124,9 +124,23 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
   }
 }
 
-template <int NW>
+// Ring seeding by the staging threads: the rotated key rows and value rows of
+// frames in [s_lo, s_hi) go to slot (frame mod W) of the stream's rings.
+struct Seed {
+  bf16* ring_k;  // this (stream, head)'s [W, 64] ring slice
+  bf16* ring_v;
+  int kt0;       // first frame of the tile being committed
+  int s_lo, s_hi, W;
+  __device__ __forceinline__ bool take(int r, int& slot) const {
+    const int t = kt0 + r;
+    slot = t % max(W, 1);
+    return t >= s_lo && t < s_hi;
+  }
+};
+
+template <int NW, bool SEED = false>
 __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char* Vb, bool rope,
-                                             int tid) {
+                                             int tid, const Seed& sd = Seed{}) {
   constexpr int NT = Stage<NW>::NT;
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UK; ++j) {
@@ -149,16 +163,25 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
     }
     *reinterpret_cast<u32x4*>(Kb + r * kRowK + 16 * cp) = x;
     *reinterpret_cast<u32x4*>(Kb + r * kRowK + 64 + 16 * cp) = y;
+    int slot;
+    if (SEED && sd.take(r, slot)) {
+      bf16* kr = sd.ring_k + (size_t)slot * kD + 8 * cp;
+      *reinterpret_cast<u32x4*>(kr) = x;
+      *reinterpret_cast<u32x4*>(kr + kHalf) = y;
+    }
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
     int r, c;
     v_unit(tid + j * NT, r, c);
     *reinterpret_cast<u32x4*>(Vb + r * kRowV + 16 * c) = st.v[j];
+    int slot;
+    if (SEED && sd.take(r, slot))
+      *reinterpret_cast<u32x4*>(sd.ring_v + (size_t)slot * kD + 8 * c) = st.v[j];
   }
 }
 
-template <int NW, typename TO>
+template <int NW, typename TO, bool SEED>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
                                                                   int n_short, int hx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
@@ -200,9 +223,20 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int T = a.T, W = a.W;
+  // fixed batch: stream b at rows b*T ..; varlen: rows cu[b] .. cu[b+1]-1
+  int T = a.T;
+  size_t row0 = (size_t)b * a.T;
+  if (a.cu) {
+    const int c0 = min(max(a.cu[b], 0), a.total);
+    const int c1 = min(max(a.cu[b + 1], c0), a.total);
+    row0 = (size_t)c0;
+    T = min(c1 - c0, a.T);
+    if (SEED && h == 0 && qt == 0 && threadIdx.x == 0) a.pos_out[b] = T;
+    if (qt * NW * 32 >= T) return;
+  }
+  const int W = a.W;
   const size_t rs = (size_t)a.H * kD;
-  const size_t base = (size_t)b * T * rs + (size_t)h * kD;
+  const size_t base = row0 * rs + (size_t)h * kD;
   const bf16* __restrict__ q = (const bf16*)a.q + base;
   const bf16* __restrict__ k = (const bf16*)a.k + base;
   const bf16* __restrict__ v = (const bf16*)a.v + base;
@@ -289,7 +323,23 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   Stage<NW> st;
   stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
   if (rope) __syncthreads();  // every wave has read its Q table rows
-  stage_commit<NW>(st, lds, lds + kTileK, rope, tid);
+  // ring seeding: this workgroup writes its own query rows, as keys, for
+  // frames in the stream's last W
+  Seed sd0{};
+  if (SEED) {
+    const size_t ring = ((size_t)b * a.H + h) * (size_t)W * kD;
+    sd0.ring_k = (bf16*)a.ring_k + ring;
+    sd0.ring_v = (bf16*)a.ring_v + ring;
+    sd0.s_lo = max(q0, T - W);
+    sd0.s_hi = min(q0 + BM, T);
+    sd0.W = W;
+  }
+  auto seed_for = [&](int kt0) {
+    Seed sd = sd0;
+    sd.kt0 = kt0;
+    return sd;
+  };
+  stage_commit<NW, SEED>(st, lds, lds + kTileK, rope, tid, seed_for(it0 * kBN));
   __syncthreads();
 
   for (int it = it0; it <= it1; ++it) {
@@ -389,8 +439,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       }
     }
 
-    if (more) stage_commit<NW>(st, lds + (buf ^ 1) * kStageBytes,
-                               lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid);
+    if (more) stage_commit<NW, SEED>(st, lds + (buf ^ 1) * kStageBytes,
+                               lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid, seed_for((it + 1) * kBN));
     __syncthreads();
   }
 
@@ -428,12 +478,18 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   const int n_bh = a.B * a.H;
   const int hx = n_bh >= 8 ? (n_bh + 7) / 8 : 0;
   const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
-  if (out == DT::BF16)
-    hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16>), dim3((unsigned)grid), dim3(NW * 64), 0, st,
-                       a, n_qtiles, n_short, hx);
-  else
-    hipLaunchKernelGGL((prefill_mfma_kernel<NW, float>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       st, a, n_qtiles, n_short, hx);
+  const dim3 g((unsigned)grid), blk(NW * 64);
+  if (a.ring_k) {
+    if (out == DT::BF16)
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, true>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, true>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+  } else {
+    if (out == DT::BF16)
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, false>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+    else
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, false>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+  }
   return hipGetLastError();
 }
 

@@ -187,6 +187,81 @@ vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void*
   return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
 }
 
+vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                                     const int32_t* cu_seqlens, int32_t S, int32_t total,
+                                     int32_t max_T, int32_t H, int32_t rope_applied,
+                                     const float* rope_table,
+                                     int64_t table_p0, int64_t table_len, void* ring_k,
+                                     void* ring_v, int64_t* pos, const vx_attn_cfg* cfg,
+                                     void* stream) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_dims("prefill_varlen", S, max_T, H))) return st;
+  if (total < 0 || (int64_t)total > (int64_t)S * max_T)
+    return fail(VX_E_SHAPE, "prefill_varlen: total must be in [0, S*max_T]");
+  if (cfg->io_dtype != VX_BF16)
+    return fail(VX_E_DTYPE, "prefill_varlen: only bf16 input is supported");
+  const bool seed = ring_k || ring_v;
+  if (S == 0 || ((max_T == 0 || total == 0) && !seed)) return ok();
+  if (seed && max_T == 0) return fail(VX_E_SHAPE, "prefill_varlen: seeding needs max_T >= 1");
+  if (H < 1) return fail(VX_E_SHAPE, "H must be >= 1");
+  if (S > 65535 || H > 65535) return fail(VX_E_SHAPE, "S and H must be <= 65535");
+  if ((int64_t)S * max_T * H > kMaxRows) return fail(VX_E_SHAPE, "S*max_T*H too large");
+  if (!q || !k || !v || !o || !cu_seqlens)
+    return fail(VX_E_NULL, "q, k, v, o and cu_seqlens must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (((uintptr_t)cu_seqlens & 3u) != 0) return fail(VX_E_ALIGN, "cu_seqlens is not 4-byte aligned");
+  const size_t n = (size_t)total * H * vx::kD;
+  const size_t ib = n * elem_size(cfg->io_dtype), ob = n * elem_size(cfg->out_dtype);
+  if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib))
+    return fail(VX_E_RANGE, "o overlaps an input");
+  if (seed) {
+    if (!ring_k || !ring_v || !pos)
+      return fail(VX_E_NULL, "ring seeding needs ring_k, ring_v and pos");
+    if (!aligned16(ring_k) || !aligned16(ring_v))
+      return fail(VX_E_ALIGN, "ring_k and ring_v must be 16-byte aligned");
+    if (((uintptr_t)pos & 7u) != 0) return fail(VX_E_ALIGN, "pos is not 8-byte aligned");
+    if ((int64_t)S * H * cfg->window * vx::kD > kMaxElems)
+      return fail(VX_E_SHAPE, "prefill_varlen: ring too large");
+    const size_t rb = (size_t)S * H * cfg->window * vx::kD * elem_size(cfg->io_dtype);
+    if (overlap(ring_k, rb, ring_v, rb)) return fail(VX_E_RANGE, "ring_k and ring_v overlap");
+    if (overlap(o, ob, ring_k, rb) || overlap(o, ob, ring_v, rb))
+      return fail(VX_E_RANGE, "o overlaps a ring");
+  }
+  vx::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = S;
+  a.T = max_T;
+  a.H = H;
+  a.W = cfg->window;
+  a.pos0 = 0;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  a.cu = cu_seqlens;
+  a.total = total;
+  if (seed) {
+    a.ring_k = ring_k;
+    a.ring_v = ring_v;
+    a.pos_out = pos;
+  }
+  if (a.rope) {
+    if (!rope_table) return fail(VX_E_NULL, "rope_table is NULL and rope_applied == 0");
+    if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "rope_table is not 16-byte aligned");
+    if (table_p0 < 0 || table_len < 0 || table_p0 > 0 || max_T > table_p0 + table_len)
+      return fail(VX_E_RANGE,
+                  "rope_table covers positions [%lld, %lld) but the chunks need [0, %d)",
+                  (long long)table_p0, (long long)(table_p0 + table_len), max_T);
+    a.table = rope_table;
+    a.table_row0 = -table_p0;
+  }
+  (void)hipGetLastError();
+  return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
+}
+
 static vx_status check_stream_common(const char* what, int32_t S, int32_t n, int32_t H,
                                      const vx_attn_cfg* cfg) {
   vx_status st = check_cfg(cfg);

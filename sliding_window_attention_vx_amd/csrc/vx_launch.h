@@ -22,6 +22,16 @@ struct PrefillArgs {
   const float* table;   // [.., 2, 32] cos/sin rows
   int64_t table_row0;   // table row of position pos0 (= pos0 - table_p0)
   float scale_log2;     // softmax scale * log2(e)
+  // Varlen batch (cu != nullptr): B streams packed along the frame axis,
+  // stream b at rows cu[b] .. cu[b+1]-1 (length at most T), each at positions
+  // pos0 .. pos0 + length - 1.  Ring seeding (ring_k != nullptr): the rotated
+  // keys and the values of frames t >= length - W go to slot t mod W of the
+  // stream's [H, W, 64] rings, and pos_out[b] = length.
+  const int32_t* cu = nullptr;
+  int total = 0;        // packed rows (offsets are clamped to [0, total])
+  void* ring_k = nullptr;
+  void* ring_v = nullptr;
+  int64_t* pos_out = nullptr;
 };
 
 struct StreamArgs {

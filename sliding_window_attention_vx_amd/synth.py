@@ -196,6 +196,32 @@ def make_stream_config(name: str = "stream"):
                              dtype=c.dtype, D=c.D)
 
 
+# Batched first chunks: 64 streams whose first chunks hold 120..156 encoder
+# frames (156 = the 312-mel first chunk after the stride-2 stem), 32 heads.
+FIRST_CHUNK = dict(S=64, t_lo=120, t_hi=156, H=32, W=750, dtype="bf16", scale=0.5, seed=6)
+
+
+def make_first_chunks(S: int, H: int, lengths, *, seed, dtype: str = "bf16", scale: float = 0.5,
+                      D: int = HEAD_DIM):
+    """Packed first chunks: q, k, v [total, H, D] with stream s at rows cu[s] .. cu[s+1]-1.
+
+    Draws Q, K, V for all frames at once (order Q, K, V, as make_prefill).
+    Returns dict(q, k, v, cu) with cu an int32 array of S+1 offsets.
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    assert lengths.shape == (S,) and np.all(lengths >= 0)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    x = make_prefill(1, int(cu[-1]), H, seed=seed, dtype=dtype, scale=scale, D=D)
+    return dict(q=x["q"][0], k=x["k"][0], v=x["v"][0], cu=cu)
+
+
+def first_chunk_lengths(S: int, t_lo: int, t_hi: int, *, seed) -> np.ndarray:
+    """Chunk lengths drawn uniformly from t_lo..t_hi (inclusive)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    return rng.integers(t_lo, t_hi + 1, size=S).astype(np.int64)
+
+
 def band_pairs(T: int, W: int) -> int:
     """Number of (query, key) pairs with 0 <= t-j < W, 0 <= j <= t < T (counting only)."""
     if T <= W:

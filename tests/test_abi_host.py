@@ -166,6 +166,56 @@ def test_prefill_empty_is_ok_without_launch(L):
     assert L.vx_last_error().decode() == ""
 
 
+def prefill_varlen(L, b, c, S=2, max_T=8, H=2, rope_applied=1, table=None, tp0=0, tlen=0,
+                   seed=False, total=10, **ov):
+    a = dict(q=b.new(), k=b.new(), v=b.new(), o=b.new(), cu=b.new())
+    if seed:
+        a.update(rk=b.new(), rv=b.new(), pos=b.new())
+    a.update(ov)
+    return L.vx_swa_attn_prefill_varlen(a["q"], a["k"], a["v"], a["o"], a["cu"], S, total, max_T, H,
+                                        rope_applied, table, tp0, tlen, a.get("rk"), a.get("rv"),
+                                        a.get("pos"), None if c is None else ctypes.byref(c), None)
+
+
+def test_prefill_varlen_argument_errors(L):
+    b = Bufs()
+    c = cfg()
+    assert prefill_varlen(L, b, None) == E_NULL
+    assert prefill_varlen(L, b, cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
+    assert prefill_varlen(L, b, c, S=-1) == E_SHAPE
+    assert prefill_varlen(L, b, c, max_T=-2) == E_SHAPE
+    assert prefill_varlen(L, b, c, H=0) == E_SHAPE
+    assert prefill_varlen(L, b, c, total=-1) == E_SHAPE
+    assert prefill_varlen(L, b, c, total=17) == E_SHAPE  # more than S*max_T
+    assert prefill_varlen(L, b, c, cu=ctypes.c_void_p(0)) == E_NULL
+    assert prefill_varlen(L, b, c, q=ctypes.c_void_p(0)) == E_NULL
+    assert prefill_varlen(L, b, c, cu=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    q = b.new()
+    assert prefill_varlen(L, b, c, q=q, o=q) == E_RANGE
+    # seeding needs both rings and pos
+    assert prefill_varlen(L, b, c, seed=True, pos=ctypes.c_void_p(0)) == E_NULL
+    assert prefill_varlen(L, b, c, seed=True, rv=ctypes.c_void_p(0)) == E_NULL
+    r = b.new()
+    assert prefill_varlen(L, b, c, seed=True, rk=r, rv=r) == E_RANGE
+    assert prefill_varlen(L, b, c, seed=True, pos=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    assert prefill_varlen(L, b, c, seed=True, max_T=0, total=0) == E_SHAPE
+    # the table must start at position 0 and cover max_T positions
+    t = b.new()
+    assert prefill_varlen(L, b, c, rope_applied=0) == E_NULL
+    assert prefill_varlen(L, b, c, rope_applied=0, table=t, tp0=0, tlen=7) == E_RANGE
+    assert prefill_varlen(L, b, c, rope_applied=0, table=t, tp0=1, tlen=100) == E_RANGE
+    assert b.untouched()
+
+
+def test_prefill_varlen_empty_is_ok_without_launch(L):
+    c = cfg()
+    z = ctypes.c_void_p(0)
+    assert L.vx_swa_attn_prefill_varlen(z, z, z, z, z, 0, 0, 8, 4, 1, z, 0, 0, z, z, z,
+                                        ctypes.byref(c), z) == OK
+    assert L.vx_swa_attn_prefill_varlen(z, z, z, z, z, 3, 0, 0, 4, 1, z, 0, 0, z, z, z,
+                                        ctypes.byref(c), z) == OK
+
+
 def stream_step(L, b, c, S=2, n=4, H=2, **ov):
     a = dict(q=b.new(), k=b.new(), v=b.new(), rk=b.new(), rv=b.new(), pos=b.new(), o=b.new())
     a.update(ov)

@@ -376,3 +376,33 @@ def test_oracle_regression_record_tiny():
     for key, val in rec["samples"].items():
         t, h, d = map(int, key.split(","))
         assert abs(o[0, t, h, d] - val) < 1e-12
+
+
+def test_prefill_varlen_is_per_stream_prefill_plus_ring_seed():
+    """The batched first-chunk composition: each packed stream equals its own
+    prefill, and its ring holds the last W frames (value rows exactly, key rows
+    rotated at their own positions) in slot t mod W; an empty stream leaves
+    its ring untouched."""
+    from sliding_window_attention_vx_amd import synth
+    lengths = [5, 0, 9]
+    x = synth.make_first_chunks(3, 2, lengths, seed=11, dtype="f32", scale=1.0)
+    W = 4
+    rk = np.full((3, 2, W, 64), 5.0)
+    rv = rk.copy()
+    pos = np.full(3, -1, dtype=np.int64)
+    o = oracle.prefill_varlen(x["q"], x["k"], x["v"], x["cu"], W, ring_k=rk, ring_v=rv, pos=pos)
+    assert list(pos) == lengths
+    cu = x["cu"]
+    for s, T in enumerate(lengths):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if T == 0:
+            assert np.all(rk[s] == 5.0) and np.all(rv[s] == 5.0)
+            continue
+        want = oracle.prefill(x["q"][None, a:b], x["k"][None, a:b], x["v"][None, a:b], W)[0]
+        np.testing.assert_array_equal(o[a:b], want)
+        krot = oracle.rope(x["k"][None, a:b])[0]  # positions 0 .. T-1
+        for t in range(max(0, T - W), T):
+            np.testing.assert_array_equal(rv[s][:, t % W], x["v"][a + t])
+            np.testing.assert_array_equal(rk[s][:, t % W], krot[t])
+        if T < W:  # slots past the chunk keep their contents
+            assert np.all(rk[s][:, T:] == 5.0)
