@@ -60,7 +60,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=60,
                     help="oracle repetitions of the prefill workload for the CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "stream", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "copy"], default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
                          "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
     ap.add_argument("--copy-mib", type=int, default=1024)
@@ -126,6 +126,20 @@ def main():
     so = torch.empty_like(frames[0][0])
     sbytes = stream_bytes(sc.S, sc.n, sc.H, sc.W)
 
+    # ---- batched first chunks (varlen prefill seeding the rings)
+    fc = synth.FIRST_CHUNK
+    fc_len = synth.first_chunk_lengths(fc["S"], fc["t_lo"], fc["t_hi"], seed=fc["seed"])
+    xf = synth.make_first_chunks(fc["S"], fc["H"], fc_len, seed=fc["seed"], scale=fc["scale"])
+    fq, fk, fv = to(xf["q"]), to(xf["k"]), to(xf["v"])
+    fcu = torch.from_numpy(xf["cu"]).to(dev)
+    fo = torch.empty_like(fq)
+    frk = torch.zeros((fc["S"], fc["H"], fc["W"], 64), dtype=torch.bfloat16, device=dev)
+    frv = torch.zeros_like(frk)
+    fpos = torch.zeros(fc["S"], dtype=torch.int64, device=dev)
+    ftab = vx.rope_table(0, fc["t_hi"])
+    fc_flops = sum(4.0 * 64 * synth.band_pairs(int(t), fc["W"]) * fc["H"] for t in fc_len)
+    fc_slices = [(int(xf["cu"][i]), int(xf["cu"][i + 1])) for i in range(fc["S"])]
+
     def prefill():
         vx.prefill(q, k, v, window=pc.W, table=table, out=o)
 
@@ -153,7 +167,10 @@ def main():
         stream_fused(i)
 
     if args.only is not None:
-        fn = (lambda j: prefill()) if args.only == "prefill" else stream_fused
+        fn = {"prefill": lambda j: prefill(), "stream": stream_fused,
+              "first_chunk": lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"],
+                                                         window=fc["W"], table=ftab, ring_k=frk,
+                                                         ring_v=frv, pos=fpos, out=fo)}[args.only]
         for j in range(args.warmup):
             fn(j)
         torch.cuda.synchronize()
@@ -200,6 +217,15 @@ def main():
         return s.elapsed_time(e) * 1e3 / reps
 
     reps = max(K, 20)
+    fc_us = per_launch_us(lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"], window=fc["W"],
+                                                      table=ftab, ring_k=frk, ring_v=frv,
+                                                      pos=fpos, out=fo), reps)
+
+    def serial_first_chunks(j):
+        for a_, b_ in fc_slices:
+            vx.prefill(fq[a_:b_][None], fk[a_:b_][None], fv[a_:b_][None], window=fc["W"],
+                       table=ftab, out=fo[a_:b_][None])
+    fc_serial_us = per_launch_us(serial_first_chunks, max(K // 4, 5))
     pre_us = per_launch_us(lambda j: prefill(), reps)
     step_us = per_launch_us(stream_fused, reps)
     attend_us = per_launch_us(lambda j: stream(j), reps)
@@ -251,6 +277,20 @@ def main():
             "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
             "traffic": None,
         },
+    }
+
+    out["first_chunk"] = {
+        "workload": f"{fc['S']} streams x first chunks of {fc['t_lo']}..{fc['t_hi']} frames "
+                    f"(varlen, {int(xf['cu'][-1])} frames), H{fc['H']} D64 W{fc['W']} bf16, RoPE "
+                    "fused, rings seeded",
+        "us_per_call": round(fc_us, 3),
+        "tflops": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
+        "serialized_us": round(fc_serial_us, 3),
+        "batching_speedup": round(fc_serial_us / fc_us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fc_flops / (fc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
     }
 
     if not args.no_cpu_baseline:
