@@ -33,6 +33,33 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, calibrated
+# against a 1 GiB device copy: read = FETCH_SIZE x 2, written = WRITE_SIZE x 1), for the kernel
+# sources whose SHA-256 is given.  A changed source reports null until it is measured again.
+CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
+MEASURED_TRAFFIC = {
+    "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
+                "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
+                21_649_408 + 6_144_000),
+    "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
+               "e05bc039dade29edacef14b7022e2959c543d4baf0479d16eb70c2a23daa31e0",
+               396_048_794 + 3_146_240),
+    "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
+                    "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
+                    156_001_485 + 107_364_352),
+}
+
+
+def measured_traffic(kind):
+    """Bytes per launch from the counters if the kernel source is the one measured, else None."""
+    import hashlib
+    files, digest, nbytes = MEASURED_TRAFFIC[kind]
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
+    return nbytes if m.hexdigest() == digest else None
+
 
 def band_flops(B, T, H, W, D=64):
     from sliding_window_attention_vx_amd.synth import band_pairs
@@ -266,7 +293,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill"),
         },
         "roofline_stream": {
             "kernel": "stream_step_mfma_kernel",
@@ -275,7 +302,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(stream_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("stream"),
         },
     }
 
@@ -290,7 +317,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fc_flops / (fc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("first_chunk")},
     }
 
     if not args.no_cpu_baseline:
