@@ -68,6 +68,14 @@ def _configure(lib):
     lib.oracle_ring_append.restype = ctypes.c_int
     lib.oracle_ring_append.argtypes = [_dp, _dp, _dp, _dp, _i64p, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gqa_prefill.restype = ctypes.c_int
+    lib.oracle_gqa_prefill.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       _i64p, ctypes.c_double, ctypes.c_double, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int]
+    lib.oracle_gqa_stream_step.restype = ctypes.c_int
+    lib.oracle_gqa_stream_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64p, _dp, _i64, _i64, _i64,
+                                           _i64, _i64, _i64, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -194,3 +202,62 @@ def ring_append(ring_k, ring_v, k_new, v_new, pos, W, theta=1e6, bf16=False, rop
                                     int(bool(bf16)), int(bool(rope_applied)))
     if rc != 0:
         raise ValueError("oracle_ring_append rejected its arguments")
+
+
+def gqa_prefill(q, k, v, W, pos=None, theta=1e6, scale=None, bf16=False, rope_applied=False,
+                nthreads=0):
+    """Grouped-query causal sliding-window attention over whole chunks.
+
+    Voxtral Realtime 2602 text decoder (transcribe.cpp "Voxtral" family notes,
+    Architecture: 32 query heads over 8 key/value heads, head_dim 128, window
+    8192).  q [B,T,Hq,D], k,v [B,T,Hkv,D] -> o [B,T,Hq,D] float64; query head
+    h reads key/value head h // (Hq // Hkv).  pos as in prefill().
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, T, Hkv, D) and v.shape == k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    p = None
+    if pos is not None:
+        if np.isscalar(pos):
+            p = (np.int64(pos) + np.arange(T, dtype=np.int64))[None, :].repeat(B, 0)
+        else:
+            p = np.broadcast_to(np.asarray(pos, dtype=np.int64), (B, T))
+        p = np.ascontiguousarray(p, dtype=np.int64)
+    o = np.zeros_like(q)
+    rc = _load().oracle_gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, D, int(W),
+                                    None if p is None else _ptr(p, _i64p), float(theta),
+                                    float(scale), int(bool(bf16)), int(bool(rope_applied)),
+                                    int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gqa_prefill rejected its arguments")
+    return o
+
+
+def gqa_stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, W, theta=1e6, scale=None,
+                    bf16=False, rope_applied=False, nthreads=0):
+    """One grouped-query streaming (decode) step.
+
+    q_new [S,n,Hq,D], k_new/v_new [S,n,Hkv,D], rings [S,Hkv,W,D], pos [S]
+    -> o [S,n,Hq,D].  Reads the rings only; ring_append() with the key/value
+    heads appends the step's frames.
+    """
+    q_new, k_new, v_new = _f64(q_new), _f64(k_new), _f64(v_new)
+    ring_k, ring_v = _f64(ring_k), _f64(ring_v)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    S, n, Hq, D = q_new.shape
+    Hkv = k_new.shape[2]
+    assert k_new.shape == (S, n, Hkv, D) and v_new.shape == k_new.shape
+    assert ring_k.shape == (S, Hkv, W, D) and ring_v.shape == (S, Hkv, W, D)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.zeros_like(q_new)
+    rc = _load().oracle_gqa_stream_step(_ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k),
+                                        _ptr(ring_v), _ptr(pos, _i64p), _ptr(o), S, n, Hq, Hkv,
+                                        D, int(W), float(theta), float(scale), int(bool(bf16)),
+                                        int(bool(rope_applied)), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gqa_stream_step rejected its arguments")
+    return o

@@ -15,11 +15,21 @@
  * form (same page, "Streaming schedule": 4 encoder frames per step) appends
  * frames to a W-slot ring of rotated keys and values.
  *
+ * The text decoder of the same model (same page and section) uses the same
+ * attention with grouped queries: 32 query heads over 8 key/value heads,
+ * head_dim 128, a sliding window of 8192 tokens and RoPE theta 1e6, decoded
+ * one token at a time over a ring of the same kind.  The functions below
+ * take the grouped form as the general one (oracle_gqa_*); the multi-head
+ * entry points are that form with as many key/value heads as query heads.
+ *
  * Readings where the pages are silent:
  *   - window: keys j with t-W+1 <= j <= t (W keys including the query);
  *   - RoPE: half-split pairing (i, i+D/2), frequency f_i = theta^(-2i/D),
  *     angle = position * f_i, computed in float64;
  *   - scale: 1/sqrt(D) unless given;
+ *   - grouping: query head h reads key/value head h / (Hq/Hkv), i.e. each
+ *     key/value head serves Hq/Hkv consecutive query heads (the
+ *     repeat_interleave layout the Core AI page names for its decoder);
  *   - bf16 contract: in bf16 mode the rotated q and k are rounded to bfloat16
  *     (nearest, ties to even) before the scores, as the storage dtype of a
  *     rotated tensor is bf16; everything after that is exact float64.
@@ -127,32 +137,40 @@ static int set_threads(int nthreads) {
 #endif
 }
 
-/* Whole-chunk prefill.
- * q,k,v,o: [B,T,H,D] float64.  pos: [B*T] absolute positions or NULL (= t).
- * Query t attends to keys j = max(0,t-W+1) .. t of the same (b,h).
+/* Whole-chunk prefill, grouped-query form.
+ * q,o: [B,T,Hq,D]; k,v: [B,T,Hkv,D] float64.  pos: [B*T] absolute positions
+ * or NULL (= t).  Query t of query head h attends to keys j = max(0,t-W+1)
+ * .. t of key/value head h / (Hq/Hkv), same b.  With Hkv == Hq this is plain
+ * multi-head attention (the audio encoder); the text decoder of the same
+ * model groups 32 query heads over 8 key/value heads (transcribe.cpp
+ * "Voxtral" family notes, Architecture), each key/value head serving Hq/Hkv
+ * consecutive query heads.
  * rope_applied != 0: q and k are already rotated (no rotation, no rounding).
- * Returns 0, or -1 on bad arguments / allocation failure. */
-int oracle_prefill(const double *q, const double *k, const double *v, double *o,
-                   int64_t B, int64_t T, int64_t H, int64_t D, int64_t W,
-                   const int64_t *pos, double theta, double scale, int bf16,
-                   int rope_applied, int nthreads) {
-  if (B < 0 || T < 0 || H < 1 || D < 2 || (D & 1) || W < 1) return -1;
+ * Returns 0, or -1 on bad arguments (Hq % Hkv != 0 included) or allocation
+ * failure. */
+int oracle_gqa_prefill(const double *q, const double *k, const double *v, double *o,
+                       int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t W,
+                       const int64_t *pos, double theta, double scale, int bf16,
+                       int rope_applied, int nthreads) {
+  if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 2 || (D & 1) || W < 1) return -1;
   if (B == 0 || T == 0) return 0;
-  size_t n = (size_t)(B * T * H * D);
-  double *qr = (double *)malloc(n * sizeof(double));
-  double *kr = (double *)malloc(n * sizeof(double));
+  const int64_t G = Hq / Hkv;
+  size_t nq = (size_t)(B * T * Hq * D), nkv = (size_t)(B * T * Hkv * D);
+  double *qr = (double *)malloc(nq * sizeof(double));
+  double *kr = (double *)malloc(nkv * sizeof(double));
   if (!qr || !kr) { free(qr); free(kr); return -1; }
-  memcpy(qr, q, n * sizeof(double));
-  memcpy(kr, k, n * sizeof(double));
+  memcpy(qr, q, nq * sizeof(double));
+  memcpy(kr, k, nkv * sizeof(double));
   if (!rope_applied) {
-    oracle_rope(qr, B, T, H, D, pos, theta, bf16);
-    oracle_rope(kr, B, T, H, D, pos, theta, bf16);
+    oracle_rope(qr, B, T, Hq, D, pos, theta, bf16);
+    oracle_rope(kr, B, T, Hkv, D, pos, theta, bf16);
   }
   int nt = set_threads(nthreads);
   int err = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nt) reduction(| : err)
   for (int64_t b = 0; b < B; ++b)
-    for (int64_t h = 0; h < H; ++h) {
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t hk = h / G;
       int64_t cap = W < T ? W : T;
       double *s = (double *)malloc((size_t)cap * sizeof(double));
       const double **kp = (const double **)malloc((size_t)cap * sizeof(double *));
@@ -162,11 +180,11 @@ int oracle_prefill(const double *q, const double *k, const double *v, double *o,
         int64_t j0 = t - W + 1 < 0 ? 0 : t - W + 1;
         int64_t nk = 0;
         for (int64_t j = j0; j <= t; ++j, ++nk) {
-          kp[nk] = kr + ((b * T + j) * H + h) * D;
-          vp[nk] = v + ((b * T + j) * H + h) * D;
+          kp[nk] = kr + ((b * T + j) * Hkv + hk) * D;
+          vp[nk] = v + ((b * T + j) * Hkv + hk) * D;
         }
-        attend(qr + ((b * T + t) * H + h) * D, kp, vp, nk, D, scale, s,
-               o + ((b * T + t) * H + h) * D);
+        attend(qr + ((b * T + t) * Hq + h) * D, kp, vp, nk, D, scale, s,
+               o + ((b * T + t) * Hq + h) * D);
       }
       free(s); free(kp); free(vp);
     }
@@ -175,37 +193,52 @@ int oracle_prefill(const double *q, const double *k, const double *v, double *o,
   return err ? -1 : 0;
 }
 
-/* One streaming step for S streams with n new frames each.
- * q_new,k_new,v_new,o: [S,n,H,D].  ring_k (rotated keys), ring_v: [S,H,W,D];
- * slot j of a ring holds the frame at position p with p mod W == j.
- * pos[S]: absolute position of the first new frame (= frames seen so far).
- * New query i (position P+i) attends to ring frames at positions
- * max(0, P+i-W+1) .. P-1 and to new frames P .. P+i.  Reads the ring only.
- * Requires 1 <= n <= W.  Returns 0 or -1. */
-int oracle_stream_step(const double *q_new, const double *k_new, const double *v_new,
-                       const double *ring_k, const double *ring_v, const int64_t *pos,
-                       double *o, int64_t S, int64_t n, int64_t H, int64_t D, int64_t W,
-                       double theta, double scale, int bf16, int rope_applied, int nthreads) {
-  if (S < 0 || n < 1 || n > W || H < 1 || D < 2 || (D & 1) || W < 1) return -1;
+/* Multi-head prefill: q,k,v,o [B,T,H,D]; oracle_gqa_prefill with Hkv = H. */
+int oracle_prefill(const double *q, const double *k, const double *v, double *o,
+                   int64_t B, int64_t T, int64_t H, int64_t D, int64_t W,
+                   const int64_t *pos, double theta, double scale, int bf16,
+                   int rope_applied, int nthreads) {
+  return oracle_gqa_prefill(q, k, v, o, B, T, H, H, D, W, pos, theta, scale, bf16,
+                            rope_applied, nthreads);
+}
+
+/* One streaming step for S streams with n new frames each, grouped-query form.
+ * q_new,o: [S,n,Hq,D]; k_new,v_new: [S,n,Hkv,D].  ring_k (rotated keys),
+ * ring_v: [S,Hkv,W,D]; slot j of a ring holds the frame at position p with
+ * p mod W == j.  pos[S]: absolute position of the first new frame (= frames
+ * seen so far).  New query i (position P+i) of query head h attends, on
+ * key/value head h / (Hq/Hkv), to ring frames at positions max(0, P+i-W+1)
+ * .. P-1 and to new frames P .. P+i.  Reads the rings only.  With n = 1 this
+ * is one decode step of the text decoder.  Requires 1 <= n <= W and
+ * Hq % Hkv == 0.  Returns 0 or -1. */
+int oracle_gqa_stream_step(const double *q_new, const double *k_new, const double *v_new,
+                           const double *ring_k, const double *ring_v, const int64_t *pos,
+                           double *o, int64_t S, int64_t n, int64_t Hq, int64_t Hkv, int64_t D,
+                           int64_t W, double theta, double scale, int bf16, int rope_applied,
+                           int nthreads) {
+  if (S < 0 || n < 1 || n > W || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 2 || (D & 1) || W < 1)
+    return -1;
   if (S == 0) return 0;
-  size_t cnt = (size_t)(S * n * H * D);
-  double *qr = (double *)malloc(cnt * sizeof(double));
-  double *kr = (double *)malloc(cnt * sizeof(double));
+  const int64_t G = Hq / Hkv;
+  size_t cq = (size_t)(S * n * Hq * D), ck = (size_t)(S * n * Hkv * D);
+  double *qr = (double *)malloc(cq * sizeof(double));
+  double *kr = (double *)malloc(ck * sizeof(double));
   int64_t *p = (int64_t *)malloc((size_t)(S * n) * sizeof(int64_t));
   if (!qr || !kr || !p) { free(qr); free(kr); free(p); return -1; }
-  memcpy(qr, q_new, cnt * sizeof(double));
-  memcpy(kr, k_new, cnt * sizeof(double));
+  memcpy(qr, q_new, cq * sizeof(double));
+  memcpy(kr, k_new, ck * sizeof(double));
   for (int64_t s = 0; s < S; ++s)
     for (int64_t i = 0; i < n; ++i) p[s * n + i] = pos[s] + i;
   if (!rope_applied) {
-    oracle_rope(qr, S, n, H, D, p, theta, bf16);
-    oracle_rope(kr, S, n, H, D, p, theta, bf16);
+    oracle_rope(qr, S, n, Hq, D, p, theta, bf16);
+    oracle_rope(kr, S, n, Hkv, D, p, theta, bf16);
   }
   int nt = set_threads(nthreads);
   int err = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nt) reduction(| : err)
   for (int64_t s = 0; s < S; ++s)
-    for (int64_t h = 0; h < H; ++h) {
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t kvh = h / G;
       int64_t cap = W + n;
       double *sc = (double *)malloc((size_t)cap * sizeof(double));
       const double **kp = (const double **)malloc((size_t)cap * sizeof(double *));
@@ -217,21 +250,31 @@ int oracle_stream_step(const double *q_new, const double *k_new, const double *v
         int64_t nk = 0;
         for (int64_t pp = lo; pp < P; ++pp, ++nk) { /* history from the ring */
           int64_t slot = pp % W;
-          kp[nk] = ring_k + ((s * H + h) * W + slot) * D;
-          vp[nk] = ring_v + ((s * H + h) * W + slot) * D;
+          kp[nk] = ring_k + ((s * Hkv + kvh) * W + slot) * D;
+          vp[nk] = ring_v + ((s * Hkv + kvh) * W + slot) * D;
         }
         /* new frames P .. P+i: all inside the window because n <= W */
         for (int64_t jj = 0; jj <= i; ++jj, ++nk) {
-          kp[nk] = kr + ((s * n + jj) * H + h) * D;
-          vp[nk] = v_new + ((s * n + jj) * H + h) * D;
+          kp[nk] = kr + ((s * n + jj) * Hkv + kvh) * D;
+          vp[nk] = v_new + ((s * n + jj) * Hkv + kvh) * D;
         }
-        attend(qr + ((s * n + i) * H + h) * D, kp, vp, nk, D, scale, sc,
-               o + ((s * n + i) * H + h) * D);
+        attend(qr + ((s * n + i) * Hq + h) * D, kp, vp, nk, D, scale, sc,
+               o + ((s * n + i) * Hq + h) * D);
       }
       free(sc); free(kp); free(vp);
     }
   free(qr); free(kr); free(p);
   return err ? -1 : 0;
+}
+
+/* Multi-head streaming step: all tensors with H heads; oracle_gqa_stream_step
+ * with Hkv = H. */
+int oracle_stream_step(const double *q_new, const double *k_new, const double *v_new,
+                       const double *ring_k, const double *ring_v, const int64_t *pos,
+                       double *o, int64_t S, int64_t n, int64_t H, int64_t D, int64_t W,
+                       double theta, double scale, int bf16, int rope_applied, int nthreads) {
+  return oracle_gqa_stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, o, S, n, H, H, D, W,
+                                theta, scale, bf16, rope_applied, nthreads);
 }
 
 /* Append n new frames per stream: rotate k_new (unless rope_applied; bf16

@@ -227,3 +227,80 @@ def band_pairs(T: int, W: int) -> int:
     if T <= W:
         return T * (T + 1) // 2
     return W * (W + 1) // 2 + (T - W) * W
+
+
+# ---------------------------------------------------------------------------
+# text-decoder sets (grouped-query attention)
+# ---------------------------------------------------------------------------
+# The Voxtral Realtime 2602 text decoder (transcribe.cpp "Voxtral" family
+# notes, Architecture): 32 query heads over 8 key/value heads, head_dim 128,
+# sliding window 8192, RoPE theta 1e6.
+#
+#   dec_tiny     prefill B2 T200 Hq8 Hkv2 W64 bf16, N(0,1)
+#   dec_prefill  prefill B1 T16384 Hq32 Hkv8 W8192 bf16, N(0,1): a prompt two
+#                windows long
+#   dec_decode   64 streams x 1 new token, Hq32 Hkv8 W8192 bf16, rings
+#                pre-filled N(0,1), next position per stream ~ U{8192..65536}
+
+@dataclasses.dataclass(frozen=True)
+class GqaConfig:
+    name: str
+    kind: str  # "prefill" or "decode"
+    B: int     # batch (prefill) or streams (decode)
+    T: int     # prompt length (prefill) or new tokens per step (decode)
+    Hq: int
+    Hkv: int
+    W: int
+    dtype: str
+    seed: int
+    scale: float = 1.0
+    pos_lo: int = 0
+    pos_hi: int = 0
+    theta: float = 1e6
+    D: int = 128
+
+
+GQA_CONFIGS = {
+    "dec_tiny": GqaConfig("dec_tiny", "prefill", B=2, T=200, Hq=8, Hkv=2, W=64, dtype="bf16",
+                          seed=21),
+    "dec_prefill": GqaConfig("dec_prefill", "prefill", B=1, T=16384, Hq=32, Hkv=8, W=8192,
+                             dtype="bf16", seed=22),
+    "dec_decode": GqaConfig("dec_decode", "decode", B=64, T=1, Hq=32, Hkv=8, W=8192,
+                            dtype="bf16", seed=23, pos_lo=8192, pos_hi=65536),
+}
+
+
+def make_gqa_prefill(B: int, T: int, Hq: int, Hkv: int, *, seed, dtype: str = "bf16",
+                     scale: float = 1.0, D: int = 128):
+    """Q [B,T,Hq,D], then K and V [B,T,Hkv,D], as float32 arrays of storage values."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    out = {}
+    for name, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        x = rng.standard_normal((B, T, H, D), dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        out[name] = _store(x, dtype)
+    return out
+
+
+def make_gqa_frames(S: int, n: int, Hq: int, Hkv: int, *, seed, step: int,
+                    dtype: str = "bf16", D: int = 128):
+    """New-token q [S,n,Hq,D], k and v [S,n,Hkv,D] for decode step `step`."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1000003, step])))
+    return {name: _store(rng.standard_normal((S, n, H, D), dtype=np.float32), dtype)
+            for name, H in (("q", Hq), ("k", Hkv), ("v", Hkv))}
+
+
+def make_gqa_config(name: str):
+    c = GQA_CONFIGS[name]
+    assert c.kind == "prefill"
+    return make_gqa_prefill(c.B, c.T, c.Hq, c.Hkv, seed=c.seed, dtype=c.dtype, scale=c.scale,
+                            D=c.D)
+
+
+def make_gqa_decode_state(name: str = "dec_decode"):
+    """Full rings [S,Hkv,W,D] and next positions for a decode workload."""
+    c = GQA_CONFIGS[name]
+    assert c.kind == "decode"
+    return make_stream_state(c.B, c.Hkv, c.W, seed=c.seed, pos_lo=c.pos_lo, pos_hi=c.pos_hi,
+                             dtype=c.dtype, D=c.D)

@@ -31,6 +31,9 @@ PIN_CHECKS = [
     pins.test_streaming_equals_prefill_bf16_contract,
     pins.test_ring_holds_rotated_keys_at_position_mod_w,
     pins.test_stream_step_from_absolute_positions_matches_prefill_slice,
+    lambda: pins.test_gqa_prefill_matches_dense_brute_force(48, 16, 8, 2, 128),
+    pins.test_gqa_key_value_head_touches_only_its_group,
+    lambda: pins.test_gqa_decode_equals_prefill_across_ring_wraps(1),
 ]
 
 MUTATIONS = [
@@ -47,6 +50,8 @@ MUTATIONS = [
     ("append rotates at the chunk start", "int64_t p = pos[s] + i;\n      int64_t slot", "int64_t p = pos[s];\n      int64_t slot"),
     ("bf16 ties away from zero", "double n = nearbyint(scaled);", "double n = round(scaled);"),
     ("bf16 truncates", "double n = nearbyint(scaled);", "double n = trunc(scaled);"),
+    ("prefill key/value heads interleaved", "const int64_t hk = h / G;", "const int64_t hk = h % Hkv;"),
+    ("decode key/value heads interleaved", "const int64_t kvh = h / G;", "const int64_t kvh = h % Hkv;"),
     ("new frames see the future", "for (int64_t jj = 0; jj <= i; ++jj, ++nk)", "for (int64_t jj = 0; jj < n; ++jj, ++nk)"),
 ]
 

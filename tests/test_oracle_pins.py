@@ -406,3 +406,139 @@ def test_prefill_varlen_is_per_stream_prefill_plus_ring_seed():
             np.testing.assert_array_equal(rk[s][:, t % W], krot[t])
         if T < W:  # slots past the chunk keep their contents
             assert np.all(rk[s][:, T:] == 5.0)
+
+
+# --------------------------------------------------------------------------
+# grouped-query attention (text decoder: 32 query heads over 8 key/value
+# heads, head_dim 128, window 8192, RoPE theta 1e6)
+# --------------------------------------------------------------------------
+
+def _expand_kv(x, G):
+    """Copy each key/value head to G consecutive query heads (the
+    repeat_interleave form of GQA the Core AI page compares against a
+    broadcast form); axis 2 is the head axis of [B,T,H,D]."""
+    return np.repeat(x, G, axis=2)
+
+
+@pytest.mark.parametrize("T,W,Hq,Hkv,D", [(40, 7, 4, 2, 16), (48, 16, 8, 2, 128),
+                                           (33, 40, 4, 1, 8), (20, 5, 3, 3, 8)])
+def test_gqa_prefill_matches_dense_brute_force(T, W, Hq, Hkv, D):
+    q = rnd((1, T, Hq, D), 80)
+    k, v = rnd((1, T, Hkv, D), 81), rnd((1, T, Hkv, D), 82)
+    pos = np.arange(T)
+    G = Hq // Hkv
+    kr = _expand_kv(complex_rope(k[0], pos)[None], G)[0]
+    want = dense_band_attention(complex_rope(q[0], pos), kr, _expand_kv(v, G)[0], W)
+    np.testing.assert_allclose(oracle.gqa_prefill(q, k, v, W)[0], want, rtol=0, atol=1e-12)
+
+
+def test_gqa_prefill_matches_sdpa_grouped_mode():
+    # torch SDPA's own grouped mode (enable_gqa: query head h reads key/value
+    # head h // (Hq/Hkv)) with a band mask, at the decoder's head_dim 128.
+    import torch
+    import torch.nn.functional as F
+    from tests.refimpl import band_mask
+    B, T, Hq, Hkv, D, W = 2, 80, 8, 2, 128, 30
+    q, k, v = rnd((B, T, Hq, D), 83), rnd((B, T, Hkv, D), 84), rnd((B, T, Hkv, D), 85)
+    pos = np.arange(T)
+    qr = np.stack([complex_rope(q[b], pos) for b in range(B)])
+    kr = np.stack([complex_rope(k[b], pos) for b in range(B)])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    want = F.scaled_dot_product_attention(t(qr), t(kr), t(v),
+                                          attn_mask=torch.from_numpy(band_mask(T, W)),
+                                          enable_gqa=True).numpy().transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(oracle.gqa_prefill(q, k, v, W), want, rtol=0, atol=1e-12)
+
+
+def test_gqa_with_one_group_is_multi_head():
+    q, k, v = (rnd((2, 30, 4, 16), s) for s in (86, 87, 88))
+    np.testing.assert_array_equal(oracle.gqa_prefill(q, k, v, 9), oracle.prefill(q, k, v, 9))
+
+
+def test_gqa_key_value_head_touches_only_its_group():
+    # Changing key/value head j changes the outputs of query heads jG .. jG+G-1 only.
+    T, Hq, Hkv, D, W = 24, 8, 4, 16, 10
+    G = Hq // Hkv
+    q, k, v = rnd((1, T, Hq, D), 89), rnd((1, T, Hkv, D), 90), rnd((1, T, Hkv, D), 91)
+    base = oracle.gqa_prefill(q, k, v, W)
+    for j in range(Hkv):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, j] += 1.0
+        v2[:, :, j] *= -2.0
+        o = oracle.gqa_prefill(q, k2, v2, W)
+        changed = np.any(o != base, axis=(0, 1, 3))
+        assert list(np.nonzero(changed)[0]) == list(range(j * G, (j + 1) * G)), j
+
+
+def test_gqa_rope_frequencies_closed_form_head_dim_128():
+    # theta = 1e6, D = 128: f_i = 1e6^(-2i/128) = 10^(-3i/32); the basis vector
+    # e_i at position 1 turns by f_i radians into dims (i, i+64).
+    D = 128
+    for i in (0, 1, 32, 63):
+        f = 10.0 ** (-3.0 * i / 32.0)
+        x = np.zeros((1, 1, 1, D))
+        x[0, 0, 0, i] = 1.0
+        r = oracle.rope(x, pos=np.array([[1]]), theta=1e6)[0, 0, 0]
+        assert abs(math.atan2(r[i + 64], r[i]) - f) < 1e-15 * max(1.0, f) + 1e-18, i
+        assert np.all(np.delete(r, [i, i + 64]) == 0.0)
+
+
+def run_gqa_decode(q, k, v, W, n=1, bf16=False, prefix=0):
+    """Feed q [1,T,Hq,D], k/v [1,T,Hkv,D] through gqa_stream_step + ring_append,
+    n tokens per step, over garbage-filled W-slot rings.  The first `prefix`
+    tokens are only appended (no attention), so decoding starts at that
+    position with a full history; returns the outputs of the decoded tokens."""
+    _, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    ring_k = np.full((1, Hkv, W, D), 1e3)
+    ring_v = np.full((1, Hkv, W, D), -1e3)
+    pos = np.array([0], dtype=np.int64)
+    for t in range(0, prefix, W):
+        sl = slice(t, min(prefix, t + W))
+        oracle.ring_append(ring_k, ring_v, k[:, sl], v[:, sl], pos, W, bf16=bf16)
+    out = np.zeros_like(q[:, prefix:])
+    for t in range(prefix, T, n):
+        sl = slice(t, min(T, t + n))
+        out[:, t - prefix:sl.stop - prefix] = oracle.gqa_stream_step(
+            q[:, sl], k[:, sl], v[:, sl], ring_k, ring_v, pos, W, bf16=bf16)
+        oracle.ring_append(ring_k, ring_v, k[:, sl], v[:, sl], pos, W, bf16=bf16)
+    return out
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_gqa_decode_equals_prefill_across_ring_wraps(n):
+    # Token-by-token decode over a W-slot ring equals whole-prompt prefill.
+    W, T, Hq, Hkv, D = 16, 53, 8, 2, 128
+    q, k, v = rnd((1, T, Hq, D), 92), rnd((1, T, Hkv, D), 93), rnd((1, T, Hkv, D), 94)
+    got = run_gqa_decode(q, k, v, W, n=n)
+    np.testing.assert_allclose(got, oracle.gqa_prefill(q, k, v, W), rtol=0, atol=1e-12)
+
+
+def test_gqa_decode_equals_prefill_bf16_contract_past_the_window():
+    # Decode from position 8190 (rings wrapped many times) in the bf16
+    # contract: the decoded tail equals the tail of one prefill over all tokens.
+    W, p0, T, Hq, Hkv, D = 12, 8190, 8230, 4, 1, 32
+    q, k, v = rnd((1, T, Hq, D), 95), rnd((1, T, Hkv, D), 96), rnd((1, T, Hkv, D), 97)
+    got = run_gqa_decode(q, k, v, W, bf16=True, prefix=p0)
+    want = oracle.gqa_prefill(q, k, v, W, bf16=True)[:, p0:]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_gqa_rejects_indivisible_heads():
+    x6, x4 = np.zeros((1, 3, 6, 8)), np.zeros((1, 3, 4, 8))
+    with pytest.raises(ValueError):
+        oracle.gqa_prefill(x6, x4, x4, 2)
+    with pytest.raises(ValueError):
+        oracle.gqa_stream_step(x6, x4, x4, np.zeros((1, 4, 2, 8)), np.zeros((1, 4, 2, 8)),
+                               np.array([0], np.int64), 2)
+
+
+def test_decoder_constants_match_pages():
+    c = json.load(open(os.path.join(GOLDEN, "voxtral_realtime_constants.json")))
+    for name in ("dec_prefill", "dec_decode"):
+        cfg = synth.GQA_CONFIGS[name]
+        assert cfg.Hq == c["text_decoder_heads_q"]["value"]
+        assert cfg.Hkv == c["text_decoder_heads_kv"]["value"]
+        assert cfg.D == c["text_decoder_head_dim"]["value"]
+        assert cfg.W == c["text_decoder_window"]["value"]
+        assert cfg.theta == c["text_decoder_rope_theta"]["value"]
