@@ -23,7 +23,8 @@
  *     Calls only enqueue work on it and never synchronise; a fault in a
  *     kernel surfaces at the caller's next synchronising HIP call.
  *   - Layouts are dense row-major: activations [B,T,H,D] (D fastest), rings
- *     [S,H,W,D].  D (head_dim) must be 64.
+ *     [S,H,W,D].  D (head_dim) must be 64, except for the grouped-query
+ *     entry points at the end of this file, which take 128.
  *   - Every argument is checked on the host before anything is launched.  On
  *     any error nothing is launched and no buffer is touched; the status
  *     says why and vx_last_error() gives a message (thread-local).  A failed
@@ -76,7 +77,8 @@ typedef struct {
 void vx_default_cfg(vx_attn_cfg *cfg);
 
 /* RoPE cosine/sine table for `count` consecutive positions starting at
- * `p_begin` (>= 0).  table: device float32 [count][2][head_dim/2]:
+ * `p_begin` (>= 0), for head_dim 64 or 128.  table: device float32
+ * [count][2][head_dim/2]:
  * table[j][0][i] = cos((p_begin+j) * theta^(-2i/D)), table[j][1][i] = sin(...).
  * Only cfg->head_dim and cfg->rope_theta are read.  The table depends on
  * nothing else, so one table serves every layer and call that uses these
@@ -176,6 +178,59 @@ vx_status vx_swa_attn_stream_step_append(const void *q_new, const void *k_new, c
                                          int64_t *pos_out, void *o, int32_t S, int32_t n,
                                          int32_t H, int32_t rope_applied, const vx_attn_cfg *cfg,
                                          void *stream);
+
+/* ---- Grouped-query attention, head_dim 128 ---------------------------------
+ * The text decoder of Voxtral Realtime 2602 (transcribe.cpp "Voxtral" family
+ * notes, Architecture: 32 query heads over 8 key/value heads, head_dim 128,
+ * sliding window 8192, RoPE theta 1e6): the same causal sliding-window
+ * attention with RoPE, where query head h reads key/value head h / G,
+ * G = Hq / Hkv (each key/value head serves G consecutive query heads).
+ * These entry points take cfg->head_dim == 128, bf16 input (VX_E_DTYPE
+ * otherwise), a bf16 or float32 output and no flags; RoPE pairs dimension i
+ * with i + 64.  q and o have Hq heads, k, v and the rings Hkv heads. */
+
+/* Fills `cfg` with the Voxtral Realtime text-decoder defaults: head_dim 128,
+ * window 8192, theta 1e6, scale 1/sqrt(128) (softmax_scale 0), bf16 in and
+ * out, no flags. */
+void vx_default_gqa_cfg(vx_attn_cfg *cfg);
+
+/* Prompt prefill:
+ *   o[b,t,h] = sum_j softmax_j(scale * q'[b,t,h] . k'[b,j,h/G]) v[b,j,h/G],
+ *   j = max(0, t-W+1) .. t,
+ * q', k' rotated at positions pos0 + t.  q, o: [B,T,Hq,128]; k, v:
+ * [B,T,Hkv,128].  Hq must be a multiple of Hkv with G in {1, 2, 4, 8}
+ * (VX_E_SHAPE otherwise).  RoPE arguments as in vx_swa_attn_prefill, with a
+ * table made by vx_rope_table at head_dim 128.
+ * ring_k, ring_v: [B,Hkv,W,128] bf16 rings, or both NULL.  When given
+ * (needs pos0 == 0), the rotated keys and the values of frames t >= T - W
+ * go to slot t mod W of batch entry b's rings (other slots keep their
+ * contents) and pos[b] (device int64 [B], required) is set to T: the state
+ * from which vx_gqa_attn_decode continues at position T. */
+vx_status vx_gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
+                              int32_t T, int32_t Hq, int32_t Hkv, int64_t pos0,
+                              int32_t rope_applied, const float *rope_table, int64_t table_p0,
+                              int64_t table_len, void *ring_k, void *ring_v, int64_t *pos,
+                              const vx_attn_cfg *cfg, void *stream);
+
+/* One decode step of S independent streams with n new tokens each, and its
+ * ring append, in one launch.  q_new, o: [S,n,Hq,128]; k_new, v_new:
+ * [S,n,Hkv,128]; ring_k (rotated keys) and ring_v: [S,Hkv,W,128], slot j
+ * holding the token at position p with p mod W == j.  pos_in[s] (device
+ * int64) is the position of the first new token (= tokens appended so far;
+ * a stream starts at 0 with any ring contents).  New token i of stream s
+ * (position P = pos_in[s] + i) of query head h attends, on key/value head
+ * h/G, to ring tokens at positions max(0, P-W+1) .. pos_in[s]-1 and to new
+ * tokens pos_in[s] .. P.  q_new and k_new are rotated here unless
+ * rope_applied != 0.  After every read of its ring the call writes the
+ * rotated new keys and the new values to slots (pos_in[s] + i) mod W and
+ * sets pos_out[s] = pos_in[s] + n; pos_in and pos_out must be distinct
+ * arrays (swap them for the next step).  Requires 1 <= n <= W and
+ * n * Hq/Hkv <= 16 (one token of a 32/8 decoder uses 4 of the 16 query
+ * columns of a workgroup). */
+vx_status vx_gqa_attn_decode(const void *q_new, const void *k_new, const void *v_new,
+                             void *ring_k, void *ring_v, const int64_t *pos_in, int64_t *pos_out,
+                             void *o, int32_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                             int32_t rope_applied, const vx_attn_cfg *cfg, void *stream);
 
 /* Static description of a status code. */
 const char *vx_status_string(vx_status s);

@@ -15,13 +15,16 @@ import os
 
 __all__ = [
     "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
-    "stream_step_append",
-    "WINDOW", "THETA", "HEAD_DIM",
+    "stream_step_append", "gqa_prefill", "gqa_decode",
+    "WINDOW", "THETA", "HEAD_DIM", "DEC_WINDOW", "DEC_HEAD_DIM",
 ]
 
 WINDOW = 750
 THETA = 1e6
 HEAD_DIM = 64
+# text decoder (grouped-query attention): 32 query / 8 key-value heads
+DEC_WINDOW = 8192
+DEC_HEAD_DIM = 128
 
 VX_F32, VX_BF16 = 0, 1
 VX_FLAG_VALU_KERNEL = 1
@@ -64,6 +67,12 @@ _SIGS = {
     "vx_swa_attn_prefill_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                   _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp,
                                                   _vp, ctypes.POINTER(_Cfg), _vp]),
+    "vx_default_gqa_cfg": (None, [ctypes.POINTER(_Cfg)]),
+    "vx_gqa_attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32,
+                                           _vp, _i64, _i64, _vp, _vp, _vp, ctypes.POINTER(_Cfg),
+                                           _vp]),
+    "vx_gqa_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                          _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
     "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vx_last_error": (ctypes.c_char_p, []),
     "vx_version": (_i32, []),
@@ -91,7 +100,8 @@ class Config:
     """Attention parameters (mirrors vx_attn_cfg)."""
 
     def __init__(self, window=WINDOW, theta=THETA, scale=0.0, io_dtype="bf16", out_dtype=None,
-                 valu=False):
+                 valu=False, head_dim=HEAD_DIM):
+        self.head_dim = int(head_dim)
         self.window = int(window)
         self.theta = float(theta)
         self.scale = float(scale)
@@ -101,7 +111,7 @@ class Config:
 
     def c(self):
         d = {"bf16": VX_BF16, "f32": VX_F32}
-        return _Cfg(HEAD_DIM, self.window, self.theta, self.scale, d[self.io_dtype],
+        return _Cfg(self.head_dim, self.window, self.theta, self.scale, d[self.io_dtype],
                     d[self.out_dtype], VX_FLAG_VALU_KERNEL if self.valu else 0)
 
 
@@ -137,13 +147,13 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def rope_table(p_begin, count, theta=THETA, device="cuda", out=None):
-    """cos/sin table [count, 2, 32] float32 for positions p_begin .. p_begin+count-1."""
+def rope_table(p_begin, count, theta=THETA, device="cuda", out=None, head_dim=HEAD_DIM):
+    """cos/sin table [count, 2, head_dim/2] float32 for positions p_begin .. p_begin+count-1."""
     import torch
     if out is None:
-        out = torch.empty((count, 2, HEAD_DIM // 2), dtype=torch.float32, device=device)
+        out = torch.empty((count, 2, head_dim // 2), dtype=torch.float32, device=device)
     _dev_tensor(out, "out")
-    cfg = Config(theta=theta).c()
+    cfg = Config(theta=theta, head_dim=head_dim).c()
     _check(lib().vx_rope_table(_ptr(out), int(p_begin), int(count), ctypes.byref(cfg),
                                _stream(out)), "vx_rope_table")
     return out
@@ -331,4 +341,100 @@ def stream_step_append(q_new, k_new, v_new, ring_k, ring_v, pos_in, pos_out, win
         _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos_in),
         _ptr(pos_out), _ptr(out), S, n, H, int(bool(rope_applied)), ctypes.byref(cfg),
         _stream(q_new)), "vx_swa_attn_stream_step_append")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention, head_dim 128 (the text decoder)
+# ---------------------------------------------------------------------------
+
+def gqa_prefill(q, k, v, window=DEC_WINDOW, pos0=0, theta=THETA, scale=0.0, rope_applied=False,
+                table=None, table_p0=0, ring_k=None, ring_v=None, pos=None, out=None,
+                out_dtype=None):
+    """Grouped-query prompt prefill: q [B,T,Hq,128], k, v [B,T,Hkv,128] bf16 -> o [B,T,Hq,128].
+
+    Query head h reads key/value head h // (Hq // Hkv).  With ring_k, ring_v
+    ([B, Hkv, W, 128] bf16) and pos (int64 [B]) the rings are seeded with the
+    prompt's last W rotated keys and values and pos[b] = T (needs pos0 = 0).
+    """
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(x, name)
+    if q.dim() != 4 or q.shape[-1] != DEC_HEAD_DIM or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, T, Hq, 128] and k, v [B, T, Hkv, 128]")
+    B, T, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, DEC_HEAD_DIM):
+        raise ValueError("k and v must be [B, T, Hkv, 128] with q's B and T")
+    if any(_dt(x) != "bf16" for x in (q, k, v)):
+        raise ValueError("q, k, v must be bfloat16")
+    od = out_dtype or (_dt(out) if out is not None else "bf16")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q.device)
+    _dev_tensor(out, "out")
+    if out.shape != q.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
+    tlen = 0
+    if not rope_applied:
+        if table is None:
+            table = rope_table(pos0, max(T, 1), theta, device=q.device, head_dim=DEC_HEAD_DIM)
+            table_p0 = pos0
+        _dev_tensor(table, "table")
+        tlen = table.shape[0]
+    if ring_k is not None or ring_v is not None:
+        for name, x in (("ring_k", ring_k), ("ring_v", ring_v), ("pos", pos)):
+            if x is None:
+                raise ValueError("ring seeding needs ring_k, ring_v and pos")
+            _dev_tensor(x, name)
+        want = (B, Hkv, window, DEC_HEAD_DIM)
+        if ring_k.shape != want or ring_v.shape != want:
+            raise ValueError(f"rings must be [B, Hkv, W, 128] = {want}")
+        if pos.dtype != torch.int64 or pos.shape != (B,):
+            raise ValueError("pos must be int64 [B]")
+    cfg = Config(window, theta, scale, "bf16", od, head_dim=DEC_HEAD_DIM).c()
+    _check(lib().vx_gqa_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, Hq, Hkv, int(pos0), int(bool(rope_applied)),
+        _ptr(table), int(table_p0), int(tlen), _ptr(ring_k), _ptr(ring_v), _ptr(pos),
+        ctypes.byref(cfg), _stream(q)), "vx_gqa_attn_prefill")
+    return out
+
+
+def gqa_decode(q_new, k_new, v_new, ring_k, ring_v, pos_in, pos_out, window=DEC_WINDOW,
+               theta=THETA, scale=0.0, rope_applied=False, out=None, out_dtype=None):
+    """One grouped-query decode step with its ring append.
+
+    q_new [S,n,Hq,128], k_new/v_new [S,n,Hkv,128] bf16; rings [S,Hkv,W,128]
+    bf16; pos_in/pos_out int64 [S], distinct (pos_out = pos_in + n).
+    """
+    import torch
+    for name, x in (("q_new", q_new), ("k_new", k_new), ("v_new", v_new), ("ring_k", ring_k),
+                    ("ring_v", ring_v), ("pos_in", pos_in), ("pos_out", pos_out)):
+        _dev_tensor(x, name)
+    if q_new.dim() != 4 or q_new.shape[-1] != DEC_HEAD_DIM:
+        raise ValueError("q_new must be [S, n, Hq, 128]")
+    S, n, Hq, _ = q_new.shape
+    Hkv = k_new.shape[2] if k_new.dim() == 4 else -1
+    if k_new.shape != (S, n, Hkv, DEC_HEAD_DIM) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [S, n, Hkv, 128]")
+    want = (S, Hkv, window, DEC_HEAD_DIM)
+    if ring_k.shape != want or ring_v.shape != want:
+        raise ValueError(f"rings must be [S, Hkv, W, 128] = {want}")
+    for x in (pos_in, pos_out):
+        if x.dtype != torch.int64 or x.shape != (S,):
+            raise ValueError("pos_in and pos_out must be int64 [S]")
+    if any(_dt(x) != "bf16" for x in (q_new, k_new, v_new, ring_k, ring_v)):
+        raise ValueError("new tokens and rings must be bfloat16")
+    od = out_dtype or (_dt(out) if out is not None else "bf16")
+    if out is None:
+        out = torch.empty(q_new.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q_new.device)
+    _dev_tensor(out, "out")
+    if out.shape != q_new.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
+    cfg = Config(window, theta, scale, "bf16", od, head_dim=DEC_HEAD_DIM).c()
+    _check(lib().vx_gqa_attn_decode(
+        _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos_in),
+        _ptr(pos_out), _ptr(out), S, n, Hq, Hkv, int(bool(rope_applied)), ctypes.byref(cfg),
+        _stream(q_new)), "vx_gqa_attn_decode")
     return out

@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvx.so")
-SOURCES = ["vx_api.hip", "rope.hip", "prefill_valu.hip", "prefill_mfma.hip", "stream.hip"]
+SOURCES = ["vx_api.hip", "rope.hip", "prefill_valu.hip", "prefill_mfma.hip", "stream.hip",
+           "gqa_prefill.hip", "gqa_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -9,6 +9,7 @@
 
 #include <string>
 
+#include "gqa_launch.h"
 #include "vx.h"
 #include "vx_launch.h"
 
@@ -67,8 +68,40 @@ vx::RopeFreqs rope_freqs(double theta) {
 }
 
 float scale_log2(const vx_attn_cfg* cfg) {
-  const double s = cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)vx::kD);
+  const double s = cfg->softmax_scale > 0.0f ? (double)cfg->softmax_scale
+                                             : 1.0 / sqrt((double)cfg->head_dim);
   return (float)(s * 1.4426950408889634073599);  // log2(e)
+}
+
+// Grouped-query entry points: head_dim 128, bf16 input, no flags.
+vx_status check_gqa_cfg(const char* what, const vx_attn_cfg* cfg) {
+  if (!cfg) return fail(VX_E_NULL, "%s: cfg is NULL", what);
+  if (cfg->head_dim != vx::kGD)
+    return fail(VX_E_SHAPE, "%s: head_dim must be 128 (got %d)", what, cfg->head_dim);
+  if (cfg->window < 1) return fail(VX_E_RANGE, "%s: window must be >= 1 (got %d)", what, cfg->window);
+  if (!(cfg->rope_theta > 0.0) || !isfinite(cfg->rope_theta))
+    return fail(VX_E_RANGE, "%s: rope_theta must be finite and > 0", what);
+  if (!(cfg->softmax_scale >= 0.0f) || !isfinite(cfg->softmax_scale))
+    return fail(VX_E_RANGE, "%s: softmax_scale must be finite and >= 0", what);
+  if (cfg->io_dtype != VX_BF16) return fail(VX_E_DTYPE, "%s: only bf16 input is supported", what);
+  if (cfg->out_dtype != VX_BF16 && cfg->out_dtype != VX_F32)
+    return fail(VX_E_DTYPE, "%s: unknown output dtype %d", what, cfg->out_dtype);
+  if (cfg->flags != 0) return fail(VX_E_RANGE, "%s: no flags are defined (got 0x%x)", what, cfg->flags);
+  return VX_OK;
+}
+
+vx::RopeFreqs128 rope_freqs128(double theta) {
+  vx::RopeFreqs128 f;
+  for (int i = 0; i < vx::kGHalf; ++i) f.f[i] = pow(theta, -2.0 * i / (double)vx::kGD);
+  return f;
+}
+
+vx_status check_heads(const char* what, int32_t Hq, int32_t Hkv) {
+  if (Hq < 1 || Hkv < 1) return fail(VX_E_SHAPE, "%s: Hq and Hkv must be >= 1", what);
+  if (Hq > 65535) return fail(VX_E_SHAPE, "%s: Hq must be <= 65535", what);
+  if (Hq % Hkv != 0)
+    return fail(VX_E_SHAPE, "%s: Hq (%d) must be a multiple of Hkv (%d)", what, Hq, Hkv);
+  return VX_OK;
 }
 
 vx_status check_dims(const char* what, int64_t a, int64_t b, int64_t c) {
@@ -103,10 +136,22 @@ void vx_default_cfg(vx_attn_cfg* cfg) {
   cfg->flags = 0;
 }
 
+void vx_default_gqa_cfg(vx_attn_cfg* cfg) {
+  if (!cfg) return;
+  cfg->head_dim = 128;
+  cfg->window = 8192;
+  cfg->rope_theta = 1e6;
+  cfg->softmax_scale = 0.0f;  // 1/sqrt(128)
+  cfg->io_dtype = VX_BF16;
+  cfg->out_dtype = VX_BF16;
+  cfg->flags = 0;
+}
+
 vx_status vx_rope_table(float* table, int64_t p_begin, int32_t count, const vx_attn_cfg* cfg,
                         void* stream) {
   if (!cfg) return fail(VX_E_NULL, "cfg is NULL");
-  if (cfg->head_dim != vx::kD) return fail(VX_E_SHAPE, "head_dim must be 64 (got %d)", cfg->head_dim);
+  if (cfg->head_dim != vx::kD && cfg->head_dim != vx::kGD)
+    return fail(VX_E_SHAPE, "head_dim must be 64 or 128 (got %d)", cfg->head_dim);
   if (!(cfg->rope_theta > 0.0) || !isfinite(cfg->rope_theta))
     return fail(VX_E_RANGE, "rope_theta must be finite and > 0");
   if (count < 0 || count > kMaxDim) return fail(VX_E_SHAPE, "count out of range (%d)", count);
@@ -115,6 +160,9 @@ vx_status vx_rope_table(float* table, int64_t p_begin, int32_t count, const vx_a
   if (!table) return fail(VX_E_NULL, "table is NULL");
   if (!aligned16(table)) return fail(VX_E_ALIGN, "table is not 16-byte aligned");
   (void)hipGetLastError();
+  if (cfg->head_dim == vx::kGD)
+    return launched(vx::launch_gqa_rope_table(table, p_begin, count,
+                                              rope_freqs128(cfg->rope_theta), (hipStream_t)stream));
   return launched(vx::launch_rope_table(table, p_begin, count, rope_freqs(cfg->rope_theta),
                                         (hipStream_t)stream));
 }
@@ -416,6 +464,134 @@ vx_status vx_swa_attn_stream_step_append(const void* q_new, const void* k_new, c
   b.W = cfg->window;
   b.rope = a.rope;
   return launched(vx::launch_ring_append(b, vx::DT::F32, fr, (hipStream_t)stream));
+}
+
+vx_status vx_gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t B,
+                              int32_t T, int32_t Hq, int32_t Hkv, int64_t pos0,
+                              int32_t rope_applied, const float* rope_table, int64_t table_p0,
+                              int64_t table_len, void* ring_k, void* ring_v, int64_t* pos,
+                              const vx_attn_cfg* cfg, void* stream) {
+  const char* what = "gqa_prefill";
+  vx_status st = check_gqa_cfg(what, cfg);
+  if (st) return st;
+  if (B < 0 || T < 0) return fail(VX_E_SHAPE, "%s: negative size", what);
+  if ((st = check_heads(what, Hq, Hkv))) return st;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(VX_E_SHAPE, "%s: Hq/Hkv must be 1, 2, 4 or 8 (got %d)", what, G);
+  if (pos0 < 0 || pos0 > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "%s: pos0 out of range", what);
+  const bool seed = ring_k || ring_v;
+  if (seed && pos0 != 0) return fail(VX_E_RANGE, "%s: ring seeding needs pos0 == 0", what);
+  if ((int64_t)B * T == 0) return ok();
+  if (B > 65535 || T > kMaxDim) return fail(VX_E_SHAPE, "%s: B or T too large", what);
+  if ((int64_t)B * T * Hq * vx::kGD > kMaxElems) return fail(VX_E_SHAPE, "%s: tensor too large", what);
+  if (!q || !k || !v || !o) return fail(VX_E_NULL, "%s: q, k, v and o must be non-NULL", what);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "%s: q, k, v and o must be 16-byte aligned", what);
+  const size_t qb = (size_t)B * T * Hq * vx::kGD * 2, kb = (size_t)B * T * Hkv * vx::kGD * 2;
+  const size_t ob = (size_t)B * T * Hq * vx::kGD * elem_size(cfg->out_dtype);
+  if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, kb))
+    return fail(VX_E_RANGE, "%s: o overlaps an input", what);
+  vx::GqaPrefillArgs a{};
+  a.q = (const vx::bf16*)q;
+  a.k = (const vx::bf16*)k;
+  a.v = (const vx::bf16*)v;
+  a.o = o;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.W = cfg->window;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  if (seed) {
+    if (!ring_k || !ring_v || !pos) return fail(VX_E_NULL, "%s: seeding needs ring_k, ring_v and pos", what);
+    if (!aligned16(ring_k) || !aligned16(ring_v))
+      return fail(VX_E_ALIGN, "%s: ring_k and ring_v must be 16-byte aligned", what);
+    if (((uintptr_t)pos & 7u) != 0) return fail(VX_E_ALIGN, "%s: pos is not 8-byte aligned", what);
+    if ((int64_t)B * Hkv * cfg->window * vx::kGD > kMaxElems)
+      return fail(VX_E_SHAPE, "%s: ring too large", what);
+    const size_t rb = (size_t)B * Hkv * cfg->window * vx::kGD * 2;
+    if (overlap(ring_k, rb, ring_v, rb)) return fail(VX_E_RANGE, "%s: ring_k and ring_v overlap", what);
+    if (overlap(o, ob, ring_k, rb) || overlap(o, ob, ring_v, rb))
+      return fail(VX_E_RANGE, "%s: o overlaps a ring", what);
+    a.ring_k = (vx::bf16*)ring_k;
+    a.ring_v = (vx::bf16*)ring_v;
+    a.pos_out = pos;
+  }
+  if (a.rope) {
+    if (!rope_table) return fail(VX_E_NULL, "%s: rope_table is NULL and rope_applied == 0", what);
+    if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "%s: rope_table is not 16-byte aligned", what);
+    if (table_p0 < 0 || table_len < 0 || pos0 < table_p0 || pos0 + T > table_p0 + table_len)
+      return fail(VX_E_RANGE,
+                  "%s: rope_table covers positions [%lld, %lld) but the prompt needs [%lld, %lld)",
+                  what, (long long)table_p0, (long long)(table_p0 + table_len), (long long)pos0,
+                  (long long)(pos0 + T));
+    a.table = rope_table;
+    a.table_row0 = pos0 - table_p0;
+  }
+  (void)hipGetLastError();
+  return launched(vx::launch_gqa_prefill(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
+}
+
+vx_status vx_gqa_attn_decode(const void* q_new, const void* k_new, const void* v_new,
+                             void* ring_k, void* ring_v, const int64_t* pos_in, int64_t* pos_out,
+                             void* o, int32_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                             int32_t rope_applied, const vx_attn_cfg* cfg, void* stream) {
+  const char* what = "gqa_decode";
+  vx_status st = check_gqa_cfg(what, cfg);
+  if (st) return st;
+  if (S < 0 || S > kMaxDim) return fail(VX_E_SHAPE, "%s: S out of range", what);
+  if ((st = check_heads(what, Hq, Hkv))) return st;
+  const int32_t G = Hq / Hkv;
+  if (n < 1 || n > cfg->window)
+    return fail(VX_E_RANGE, "%s: need 1 <= n <= window (n %d, window %d)", what, n, cfg->window);
+  if ((int64_t)n * G > vx::kGqaMaxCols)
+    return fail(VX_E_RANGE, "%s: n * Hq/Hkv must be <= %d (got %lld)", what, vx::kGqaMaxCols,
+                (long long)n * G);
+  if ((int64_t)S * Hkv >= ((int64_t)1 << 31)) return fail(VX_E_SHAPE, "%s: S*Hkv too large", what);
+  if ((int64_t)S * Hkv * cfg->window * vx::kGD > kMaxElems)
+    return fail(VX_E_SHAPE, "%s: ring too large", what);
+  if (S == 0) return ok();
+  if (!q_new || !k_new || !v_new || !ring_k || !ring_v || !pos_in || !pos_out || !o)
+    return fail(VX_E_NULL, "%s: a tensor pointer is NULL", what);
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(ring_k) ||
+      !aligned16(ring_v) || !aligned16(o))
+    return fail(VX_E_ALIGN, "%s: tensors must be 16-byte aligned", what);
+  if (((uintptr_t)pos_in & 7u) != 0 || ((uintptr_t)pos_out & 7u) != 0)
+    return fail(VX_E_ALIGN, "%s: pos_in/pos_out must be 8-byte aligned", what);
+  const size_t qb = (size_t)S * n * Hq * vx::kGD * 2, kb = (size_t)S * n * Hkv * vx::kGD * 2;
+  const size_t ob = (size_t)S * n * Hq * vx::kGD * elem_size(cfg->out_dtype);
+  const size_t rb = (size_t)S * Hkv * cfg->window * vx::kGD * 2;
+  const size_t pb = (size_t)S * sizeof(int64_t);
+  if (overlap(pos_in, pb, pos_out, pb))
+    return fail(VX_E_RANGE, "%s: pos_in and pos_out must not overlap", what);
+  if (overlap(ring_k, rb, ring_v, rb)) return fail(VX_E_RANGE, "%s: ring_k and ring_v overlap", what);
+  if (overlap(o, ob, q_new, qb) || overlap(o, ob, k_new, kb) || overlap(o, ob, v_new, kb) ||
+      overlap(o, ob, ring_k, rb) || overlap(o, ob, ring_v, rb))
+    return fail(VX_E_RANGE, "%s: o overlaps an input", what);
+  if (overlap(ring_k, rb, k_new, kb) || overlap(ring_k, rb, v_new, kb) ||
+      overlap(ring_v, rb, k_new, kb) || overlap(ring_v, rb, v_new, kb))
+    return fail(VX_E_RANGE, "%s: a ring overlaps the new keys or values", what);
+  vx::GqaDecodeArgs a{};
+  a.q = (const vx::bf16*)q_new;
+  a.k = (const vx::bf16*)k_new;
+  a.v = (const vx::bf16*)v_new;
+  a.ring_k = (vx::bf16*)ring_k;
+  a.ring_v = (vx::bf16*)ring_v;
+  a.pos_in = pos_in;
+  a.pos_out = pos_out;
+  a.o = o;
+  a.S = S;
+  a.n = n;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.W = cfg->window;
+  a.rope = rope_applied == 0;
+  a.scale_log2 = scale_log2(cfg);
+  (void)hipGetLastError();
+  return launched(vx::launch_gqa_decode(a, to_dt(cfg->out_dtype), rope_freqs128(cfg->rope_theta),
+                                        (hipStream_t)stream));
 }
 
 const char* vx_status_string(vx_status s) {

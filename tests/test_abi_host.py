@@ -40,7 +40,8 @@ def test_header_declares_the_four_calls():
     names = declared_functions()
     for f in ("vx_rope_qk", "vx_swa_attn_prefill", "vx_swa_attn_stream_step", "vx_kv_ring_append",
               "vx_swa_attn_stream_step_append", "vx_rope_table", "vx_status_string",
-              "vx_last_error", "vx_version", "vx_default_cfg"):
+              "vx_last_error", "vx_version", "vx_default_cfg", "vx_swa_attn_prefill_varlen",
+              "vx_default_gqa_cfg", "vx_gqa_attn_prefill", "vx_gqa_attn_decode"):
         assert f in names
 
 
@@ -317,3 +318,100 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(vx, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         vx.lib()
+
+
+# ---------------------------------------------------------------------------
+# grouped-query entry points (head_dim 128)
+# ---------------------------------------------------------------------------
+
+def gqa_cfg(**kw):
+    c = vx._Cfg()
+    vx.lib().vx_default_gqa_cfg(ctypes.byref(c))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_default_gqa_cfg(L):
+    c = gqa_cfg()
+    assert (c.head_dim, c.window, c.rope_theta, c.softmax_scale) == (128, 8192, 1e6, 0.0)
+    assert (c.io_dtype, c.out_dtype, c.flags) == (vx.VX_BF16, vx.VX_BF16, 0)
+
+
+def test_gqa_prefill_argument_errors(L):
+    b = Bufs()
+    z = ctypes.c_void_p(0)
+    c64 = gqa_cfg(window=64)
+
+    def call(B=1, T=8, Hq=4, Hkv=1, pos0=0, rope_applied=1, c=c64, tlen=0, **ov):
+        a = dict(q=b.new(), k=b.new(), v=b.new(), o=b.new(), table=z, rk=z, rv=z, pos=z)
+        a.update(ov)
+        return L.vx_gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], B, T, Hq, Hkv, pos0,
+                                     rope_applied, a["table"], 0, tlen, a["rk"], a["rv"], a["pos"],
+                                     ctypes.byref(c), None)
+    assert call(c=gqa_cfg(head_dim=64)) == E_SHAPE
+    assert call(c=gqa_cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
+    assert call(c=gqa_cfg(out_dtype=5)) == E_DTYPE
+    assert call(c=gqa_cfg(flags=1)) == E_RANGE
+    assert call(c=gqa_cfg(window=0)) == E_RANGE
+    assert call(c=gqa_cfg(softmax_scale=-1.0)) == E_RANGE
+    assert call(Hq=6, Hkv=4) == E_SHAPE     # not a multiple
+    assert call(Hq=12, Hkv=1) == E_SHAPE    # group of 12 not supported
+    assert call(Hkv=0) == E_SHAPE
+    assert call(B=-1) == E_SHAPE
+    assert call(pos0=-1) == E_RANGE
+    assert call(q=z) == E_NULL
+    assert call(o=ctypes.c_void_p(b.new().value + 8)) == E_ALIGN
+    r = b.new()
+    assert call(q=r, o=r) == E_RANGE
+    assert call(rope_applied=0) == E_NULL           # no table
+    assert call(rope_applied=0, table=b.new(), tlen=4) == E_RANGE  # covers 4 of 8 positions
+    assert call(rk=b.new()) == E_NULL                # seeding needs both rings and pos
+    assert call(rk=b.new(), rv=b.new(), pos=b.new(), pos0=2) == E_RANGE
+    assert call(rk=b.new(), rv=b.new(), pos=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    assert call(B=0) == OK and call(T=0) == OK
+    assert L.vx_last_error().decode() == ""
+    assert b.untouched()
+
+
+def test_gqa_decode_argument_errors(L):
+    b = Bufs()
+    z = ctypes.c_void_p(0)
+    c64 = gqa_cfg(window=64)
+
+    def call(S=2, n=1, Hq=4, Hkv=1, c=c64, **ov):
+        a = dict(q=b.new(), k=b.new(), v=b.new(), rk=b.new(), rv=b.new(), pin=b.new(),
+                 pout=b.new(), o=b.new())
+        a.update(ov)
+        return L.vx_gqa_attn_decode(a["q"], a["k"], a["v"], a["rk"], a["rv"], a["pin"], a["pout"],
+                                    a["o"], S, n, Hq, Hkv, 0, ctypes.byref(c), None)
+    assert call(c=gqa_cfg(head_dim=64)) == E_SHAPE
+    assert call(c=gqa_cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
+    assert call(n=0) == E_RANGE
+    assert call(n=65) == E_RANGE                 # more than the window
+    assert call(n=5) == E_RANGE                  # 5 tokens x 4 heads > 16 columns
+    assert call(Hq=16, Hkv=1, n=2) == E_RANGE    # 32 columns
+    assert call(Hq=6, Hkv=4) == E_SHAPE
+    assert call(S=-1) == E_SHAPE
+    p = b.new()
+    assert call(pin=p, pout=p) == E_RANGE
+    assert call(pout=z) == E_NULL
+    assert call(pin=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    assert call(q=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    r = b.new()
+    assert call(rk=r, o=r) == E_RANGE
+    r = b.new()
+    assert call(rk=r, rv=r) == E_RANGE
+    r = b.new()
+    assert call(rv=r, k=r) == E_RANGE            # ring overlaps the new keys
+    assert call(S=0) == OK
+    assert b.untouched()
+
+
+def test_rope_table_head_dims(L):
+    b = Bufs()
+    q = b.new()
+    assert L.vx_rope_table(q, 0, 3, ctypes.byref(cfg(head_dim=96)), None) == E_SHAPE
+    assert L.vx_rope_table(q, -1, 3, ctypes.byref(gqa_cfg()), None) == E_RANGE
+    assert L.vx_rope_table(ctypes.c_void_p(0), 0, 0, ctypes.byref(gqa_cfg()), None) == OK
+    assert b.untouched()
