@@ -47,6 +47,8 @@ MEASURED_TRAFFIC = {
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
                     "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
                     156_001_485 + 107_364_352),
+    "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"), None, None),
+    "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"), None, None),
 }
 
 
@@ -54,6 +56,8 @@ def measured_traffic(kind):
     """Bytes per launch from the counters if the kernel source is the one measured, else None."""
     import hashlib
     files, digest, nbytes = MEASURED_TRAFFIC[kind]
+    if digest is None:
+        return None
     m = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -79,6 +83,20 @@ def stream_bytes(S, n, H, W, D=64, elem=2):
     return S * H * per_sh + S * 16
 
 
+def gqa_decode_bytes(S, n, Hq, Hkv, W, D=128, elem=2):
+    """Algorithmic HBM bytes of one grouped-query decode step (attend + append).
+
+    Per (stream, key/value head): the W-1 ring keys and values the new
+    tokens need, the G*n query rows and G*n output rows (G = Hq/Hkv), the n
+    new key and value rows read and the same rows appended; plus pos read
+    and written per stream.
+    """
+    row = D * elem
+    G = Hq // Hkv
+    per = 2 * (W - 1) * row + G * n * row + 2 * n * row + G * n * row + 2 * n * row
+    return S * Hkv * per + S * 16
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,7 +105,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=60,
                     help="oracle repetitions of the prefill workload for the CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "gqa_prefill",
+                                       "gqa_decode", "copy"], default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
                          "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
     ap.add_argument("--copy-mib", type=int, default=1024)
@@ -167,6 +186,36 @@ def main():
     fc_flops = sum(4.0 * 64 * synth.band_pairs(int(t), fc["W"]) * fc["H"] for t in fc_len)
     fc_slices = [(int(xf["cu"][i]), int(xf["cu"][i + 1])) for i in range(fc["S"])]
 
+    # ---- text decoder (grouped-query attention, head_dim 128)
+    dc = synth.GQA_CONFIGS["dec_decode"]
+    dst = synth.make_gqa_decode_state("dec_decode")
+    dring = {"k": to(dst["ring_k"]), "v": to(dst["ring_v"]), "c": 0,
+             "pos": [torch.from_numpy(dst["pos"].copy()).to(dev)]}
+    dring["pos"].append(dring["pos"][0].clone())
+    del dst
+    dframes = []
+    for i in range(8):
+        fr = synth.make_gqa_frames(dc.B, dc.T, dc.Hq, dc.Hkv, seed=dc.seed, step=i)
+        dframes.append((to(fr["q"]), to(fr["k"]), to(fr["v"])))
+    do = torch.empty_like(dframes[0][0])
+    dbytes = gqa_decode_bytes(dc.B, dc.T, dc.Hq, dc.Hkv, dc.W)
+    gc = synth.GQA_CONFIGS["dec_prefill"]
+    xg = synth.make_gqa_config("dec_prefill")
+    gq, gk, gv = to(xg["q"]), to(xg["k"]), to(xg["v"])
+    go = torch.empty_like(gq)
+    gtab = vx.rope_table(0, gc.T, head_dim=vx.DEC_HEAD_DIM)
+    g_flops = band_flops(gc.B, gc.T, gc.Hq, gc.W, D=gc.D)
+
+    def gqa_decode(i):
+        qn, kn, vn = dframes[i % 8]
+        c = dring["c"]
+        vx.gqa_decode(qn, kn, vn, dring["k"], dring["v"], dring["pos"][c % 2],
+                      dring["pos"][(c + 1) % 2], window=dc.W, out=do)
+        dring["c"] = c + 1
+
+    def gqa_prefill(i):
+        vx.gqa_prefill(gq, gk, gv, window=gc.W, table=gtab, out=go)
+
     def prefill():
         vx.prefill(q, k, v, window=pc.W, table=table, out=o)
 
@@ -197,7 +246,8 @@ def main():
         fn = {"prefill": lambda j: prefill(), "stream": stream_fused,
               "first_chunk": lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"],
                                                          window=fc["W"], table=ftab, ring_k=frk,
-                                                         ring_v=frv, pos=fpos, out=fo)}[args.only]
+                                                         ring_v=frv, pos=fpos, out=fo),
+              "gqa_prefill": gqa_prefill, "gqa_decode": gqa_decode}[args.only]
         for j in range(args.warmup):
             fn(j)
         torch.cuda.synchronize()
@@ -257,6 +307,9 @@ def main():
     step_us = per_launch_us(stream_fused, reps)
     attend_us = per_launch_us(lambda j: stream(j), reps)
     two_call_us = per_launch_us(lambda j: append(stream(j)), reps)
+
+    dec_us = per_launch_us(gqa_decode, reps)
+    gpre_us = per_launch_us(gqa_prefill, max(K // 5, 5))
 
     tflops = flops / (pre_us * 1e-6) / 1e12
     stream_gbs = sbytes / (step_us * 1e-6) / 1e9
@@ -318,6 +371,29 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fc_flops / (fc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("first_chunk")},
+    }
+
+    dec_gbs = dbytes / (dec_us * 1e-6) / 1e9
+    g_tflops = g_flops / (gpre_us * 1e-6) / 1e12
+    out["decoder"] = {
+        "decode": {
+            "workload": f"grouped-query decode step S{dc.B} n{dc.T} Hq{dc.Hq} Hkv{dc.Hkv} "
+                        f"D{dc.D} W{dc.W} bf16, full rings, RoPE fused, ring append fused",
+            "us_per_step": round(dec_us, 3),
+            "roofline": {"kernel": "gqa_decode_kernel", "bound": "hbm",
+                         "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("gqa_decode")},
+        },
+        "prefill": {
+            "workload": f"grouped-query prefill B{gc.B} T{gc.T} Hq{gc.Hq} Hkv{gc.Hkv} D{gc.D} "
+                        f"W{gc.W} bf16, RoPE fused",
+            "us_per_call": round(gpre_us, 3),
+            "roofline": {"kernel": "gqa_prefill_kernel", "bound": "mfma",
+                         "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic("gqa_prefill")},
+        },
     }
 
     if not args.no_cpu_baseline:

@@ -475,10 +475,12 @@ __global__ void gqa_rope_table_kernel(float* __restrict__ table, int64_t p_begin
 }  // namespace
 
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, DT out, hipStream_t st) {
+  // Groups of 4 (the 32/8 decoder): 8 waves = 4 heads x 64 queries share each
+  // staged tile (measured 14% faster than 4 waves x 32 queries at T 16384).
   switch (a.Hq / a.Hkv) {
     case 1: return launch_g<4, 1>(a, out, st);
     case 2: return launch_g<4, 2>(a, out, st);
-    case 4: return launch_g<4, 4>(a, out, st);
+    case 4: return launch_g<8, 4>(a, out, st);
     case 8: return launch_g<8, 8>(a, out, st);
   }
   return hipErrorInvalidValue;

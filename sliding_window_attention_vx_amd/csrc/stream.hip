@@ -312,9 +312,12 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreq
 // ---------------------------------------------------------------------------
 // bf16 streaming step on matrix cores (v_mfma_f32_16x16x32_bf16).
 //
-// One wave per (stream, head, chunk of up to 16 new queries): the 16 query
-// columns of the MFMA hold the chunk (4 in the Voxtral schedule; the rest are
-// zero).  Keys are processed in blocks of 32:
+// One workgroup of kSWaves waves per (stream, head, chunk of up to 16 new
+// queries): the 16 query columns of the MFMA hold the chunk (4 in the Voxtral
+// schedule; the rest are zero).  The keys' 32-key blocks are cut into one
+// contiguous run per wave, so twice as many ring reads are in flight as with
+// one wave per ring; the waves' partial (max, sum, O) merge through LDS at the
+// end.  Per block and wave:
 //   S^T = K' Q'^T  two 16-key MFMA pairs; the A operand (16 keys x 8 dims per
 //                  lane) is loaded straight from the ring in HBM; new keys are
 //                  rotated in registers (dims d and d+32 sit in the same lane).
@@ -326,9 +329,10 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreq
 //                  comes back through ds_read_b64_tr_b16, which hands a lane
 //                  four consecutive keys of one dim: exactly the key order
 //                  of the score registers.
-// The next block's K and V loads are issued before the current block's math,
-// so each wave keeps 16 KB of ring reads in flight.
+// The next block's K and V loads (8 KB) are issued before the current block's
+// math.  Ring rows are read with non-temporal loads.
 constexpr int kSQ = 16;                    // query columns per wave
+constexpr int kSWaves = 2;                 // waves per workgroup, each taking half the keys
 constexpr int kSRowV = 160;                // LDS bytes per staged V row (conflict-free)
 constexpr int kSBufV = 32 * kSRowV;        // one 32-key V block
 
@@ -351,18 +355,26 @@ __device__ __forceinline__ float sum32x(float x) {
 
 typedef __attribute__((address_space(3))) bf16x4 s_lds_bf16x4;
 
+// Ring rows are streamed once per step: non-temporal loads keep them from
+// displacing other lines.
+__device__ __forceinline__ u32x4 ring_row_load(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <typename TO>
-__global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, RopeFreqs fr) {
+__global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(StreamArgs a, RopeFreqs fr) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* cs = (float*)smem;                                  // [i1][2][32] cos/sin
-  char* vbuf = smem + align16((size_t)a.n * kD * sizeof(float));  // 2 x 32 V rows
+  char* work = smem + align16((size_t)a.n * kD * sizeof(float));
   const int H = a.H, W = a.W, n = a.n;
   const int s = blockIdx.x / H, h = blockIdx.x % H;
   const int i0 = blockIdx.y * kSQ;
   const int i1 = min(n, i0 + kSQ);
   const int nq = i1 - i0;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane & 15, g = lane >> 4;
+  char* vbuf = work + wave * 2 * kSBufV;  // this wave's two 32-key V blocks
 
   const int64_t P = a.pos[s];
   const int64_t lo = max((int64_t)0, P + i0 - W + 1);
@@ -375,13 +387,13 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
   const bf16* __restrict__ kn = (const bf16*)a.k + fbase;
   const bf16* __restrict__ vn = (const bf16*)a.v + fbase;
   const size_t rbase = ((size_t)s * H + h) * (size_t)W * kD;
-  const bf16* __restrict__ rk = (const bf16*)a.ring_k + rbase;
-  const bf16* __restrict__ rv = (const bf16*)a.ring_v + rbase;
+  const bf16* rk = (const bf16*)a.ring_k + rbase;  // not restrict: the fused append writes it
+  const bf16* rv = (const bf16*)a.ring_v + rbase;
   const bool rope = a.rope;
 
   // cos/sin of the new positions P .. P+i1-1 (float64 angle, as everywhere)
   if (rope) {
-    for (int u = lane; u < i1 * kHalf; u += 64) {
+    for (int u = tid; u < i1 * kHalf; u += kSWaves * 64) {
       const int j = u / kHalf, f = u % kHalf;
       float cc, ss;
       rope_cs(P + j, fr.f[f], &cc, &ss);
@@ -433,8 +445,8 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
         int slot = lo_slot + kk;
         if (slot >= W) slot -= W;
         const bf16* kr = rk + (size_t)slot * kD + 8 * g;
-        B.k[sb][0] = *reinterpret_cast<const u32x4*>(kr);
-        B.k[sb][1] = *reinterpret_cast<const u32x4*>(kr + kHalf);
+        B.k[sb][0] = ring_row_load(kr);
+        B.k[sb][1] = ring_row_load(kr + kHalf);
       } else if (kk < nk) {
         new_row(kn, kk - nring, B.k[sb][0], B.k[sb][1]);
       } else {
@@ -449,12 +461,30 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
       if (kk < nring) {
         int slot = lo_slot + kk;
         if (slot >= W) slot -= W;
-        B.v[j] = *reinterpret_cast<const u32x4*>(rv + (size_t)slot * kD + 8 * c);
+        B.v[j] = ring_row_load(rv + (size_t)slot * kD + 8 * c);
       } else if (kk < nk) {
         B.v[j] = *reinterpret_cast<const u32x4*>(vn + (size_t)(kk - nring) * frs + 8 * c);
       } else {
         B.v[j] = u32x4{0, 0, 0, 0};
       }
+    }
+  };
+
+  // blocks made only of ring keys (kb + 32 <= nring): unconditional loads
+  auto load_ring = [&](int kb, Blk& B) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      int slot = lo_slot + kb + 16 * sb + q;
+      if (slot >= W) slot -= W;
+      const bf16* kr = rk + (size_t)slot * kD + 8 * g;
+      B.k[sb][0] = ring_row_load(kr);
+      B.k[sb][1] = ring_row_load(kr + kHalf);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int slot = lo_slot + kb + 8 * j + (lane >> 3);
+      if (slot >= W) slot -= W;
+      B.v[j] = ring_row_load(rv + (size_t)slot * kD + 8 * (lane & 7));
     }
   };
 
@@ -467,12 +497,14 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
   for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // the keys' 32-key blocks are split into kSWaves contiguous runs, one per wave
   const int nblk = (nk + 31) / 32;
-  Blk cur, nxt;
-  load_blk(0, cur);
-  for (int bi = 0; bi < nblk; ++bi) {
+  const int b0 = wave * nblk / kSWaves, b1 = (wave + 1) * nblk / kSWaves;
+  // One block.  Only the first block (ring keys that leave the window of a
+  // later query of the chunk: key index < 15) and the blocks past the ring
+  // keys (new frames, padding) can hold masked keys; the others skip the mask.
+  auto step = [&](const Blk& cur, int bi) {
     const int kb = 32 * bi;
-    if (bi + 1 < nblk) load_blk(kb + 32, nxt);
     char* vb = vbuf + (bi & 1) * kSBufV;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -488,18 +520,23 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
                                                     qf[1], acc, 0, 0, 0);
       sc[sb] = acc;
     }
-    // mask: key kb+16sb+4g+r sits at position lo+kk (ring) or P+(kk-nring) (new)
+    if (kb < kSQ - 1 || kb + 32 > nring) {
+      // key kb+16sb+4g+r sits at position lo+kk (ring) or P+(kk-nring) (new)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = kb + 16 * sb + 4 * g + r;
+          const int64_t pk = kk < nring ? lo + kk : P + (kk - nring);
+          const bool ok = (q < nq) && (kk < nk) && (pk <= pq) && (pk > pq - W);
+          sc[sb][r] = ok ? sc[sb][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = kb + 16 * sb + 4 * g + r;
-        const int64_t pk = kk < nring ? lo + kk : P + (kk - nring);
-        const bool ok = (q < nq) && (kk < nk) && (pk <= pq) && (pk > pq - W);
-        sc[sb][r] = ok ? sc[sb][r] : -INFINITY;
-        mx = fmaxf(mx, sc[sb][r]);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[sb][r]);
     mx = max32x(max16x(mx)) * c2;
     const bool need = mx > m_run + 8.0f;
     if (__any(need)) {
@@ -522,7 +559,10 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
 #pragma unroll
     for (int i = 0; i < 4; ++i) l_run = dot2_ones(pw[i], l_run);
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-    __syncthreads();  // V rows of this block are in LDS
+    // The V rows written above are read back below by the same wave; LDS
+    // instructions of one wave execute in order, so only the compiler must
+    // keep the order.
+    __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const char* p0 = vb + v_off + 32 * db;
@@ -531,14 +571,47 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
       const bf16x8 vf = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
     }
+    __asm__ volatile("" ::: "memory");
+  };
+  // this wave's pure-ring blocks [b0, bf) with the next block's loads in
+  // flight while one computes, then the (at most two) blocks that hold new
+  // frames or padding
+  const int bf = min(b1, max(b0, nring >> 5));
+  Blk cur, nxt;
+  if (b0 < bf) load_ring(32 * b0, cur);
+  for (int bi = b0; bi < bf; ++bi) {
+    if (bi + 1 < bf) load_ring(32 * (bi + 1), nxt);
+    step(cur, bi);
     cur = nxt;
   }
+  for (int bi = bf; bi < b1; ++bi) {
+    load_blk(32 * bi, cur);
+    step(cur, bi);
+  }
+
+  // ---- merge the waves' partial (max, sum, O^T) through LDS
+  __syncthreads();  // both waves are done with their V blocks and their ring reads
+  float* Mw = reinterpret_cast<float*>(work);  // [kSWaves][16] running max (log2 domain)
+  float* Lw = Mw + kSWaves * 16;               // [kSWaves][16] row sums
+  float* Ow = Lw + kSWaves * 16;               // [kSWaves][16][64] unnormalised O
+  {
+    const float l_tot = sum32x(sum16x(l_run));
+    if (g == 0) {
+      Mw[wave * 16 + q] = m_run;
+      Lw[wave * 16 + q] = l_tot;
+    }
+    // O^T[d = 16db + 4g + r][q]
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      *reinterpret_cast<f32x4*>(Ow + (wave * 16 + q) * kD + 16 * db + 4 * g) = oacc[db];
+  }
+  __syncthreads();
 
   if (a.append) {
     // fused append (one chunk per (stream, head), so every ring read of this
     // ring is done): rotated new keys and raw values go to slot (P+j) mod W.
     const int j = q;
-    if (j < n) {
+    if (wave == 0 && j < n) {
       int slot = (int)(((P % W) + W) % W) + j;
       if (slot >= W) slot -= W;
       u32x4 x, y;
@@ -552,29 +625,32 @@ __global__ __launch_bounds__(64) void stream_step_mfma_kernel(StreamArgs a, Rope
       *reinterpret_cast<u32x4*>(wv + kHalf + 8 * g) =
           *reinterpret_cast<const u32x4*>(vn + (size_t)j * frs + kHalf + 8 * g);
     }
-    if (h == 0 && lane == 0) a.pos_out[s] = P + n;
+    if (h == 0 && tid == 0) a.pos_out[s] = P + n;
   }
 
-  // O^T[d = 16db + 4g + r][q]; the row sum is spread over the four lanes of q
-  const float l_tot = sum32x(sum16x(l_run));
-  if (q < nq) {
-    const float inv = 1.f / l_tot;
-    TO* op = (TO*)a.o + fbase + (size_t)(i0 + q) * frs;
+  // O rows: query i0+qq, dims d0 .. d0+7 per thread
+  for (int t = tid; t < nq * 8; t += kSWaves * 64) {
+    const int qq = t >> 3, d0 = 8 * (t & 7);
+    float mst = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d0 = 16 * db + 4 * g;
-      if constexpr (sizeof(TO) == 2) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
-        w.y = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
-        *reinterpret_cast<uint2*>(op + d0) = w;
-      } else {
-        f32x4 w;
+    for (int w = 0; w < kSWaves; ++w) mst = fmaxf(mst, Mw[w * 16 + qq]);
+    float den = 0.f, acc[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = oacc[db][e] * inv;
-        *reinterpret_cast<f32x4*>(op + d0) = w;
-      }
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) {
+      const float mw = Mw[w * 16 + qq];
+      const float sw = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - mst);
+      den = fmaf(sw, Lw[w * 16 + qq], den);
+      float ov[8];
+      load8(Ow + (w * 16 + qq) * kD + d0, ov);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(sw, ov[e], acc[e]);
     }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    store8((TO*)a.o + fbase + (size_t)(i0 + qq) * frs + d0, acc);
   }
 }
 
@@ -648,11 +724,13 @@ hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreq
   }
   // bf16: matrix-core kernel, one wave per (stream, head, 16-query chunk)
   dim3 grid16((unsigned)(a.S * a.H), (unsigned)((a.n + kSQ - 1) / kSQ));
-  const size_t smem16 = align16((size_t)a.n * kD * sizeof(float)) + 2 * kSBufV;
+  constexpr size_t kVBufs = (size_t)kSWaves * 2 * kSBufV;
+  constexpr size_t kMerge = (size_t)kSWaves * (2 * 16 + 16 * kD) * sizeof(float);
+  const size_t smem16 = align16((size_t)a.n * kD * sizeof(float)) + (kVBufs > kMerge ? kVBufs : kMerge);
   if (out == DT::BF16)
-    hipLaunchKernelGGL((stream_step_mfma_kernel<bf16>), grid16, dim3(64), smem16, st, a, fr);
+    hipLaunchKernelGGL((stream_step_mfma_kernel<bf16>), grid16, dim3(kSWaves * 64), smem16, st, a, fr);
   else
-    hipLaunchKernelGGL((stream_step_mfma_kernel<float>), grid16, dim3(64), smem16, st, a, fr);
+    hipLaunchKernelGGL((stream_step_mfma_kernel<float>), grid16, dim3(kSWaves * 64), smem16, st, a, fr);
   return hipGetLastError();
 }
 
