@@ -205,12 +205,18 @@ void vx_default_gqa_cfg(vx_attn_cfg *cfg);
  * (needs pos0 == 0), the rotated keys and the values of frames t >= T - W
  * go to slot t mod W of batch entry b's rings (other slots keep their
  * contents) and pos[b] (device int64 [B], required) is set to T: the state
- * from which vx_gqa_attn_decode continues at position T. */
+ * from which vx_gqa_attn_decode continues at position T.
+ * k_rot: NULL, or a caller-owned [B,T,Hkv,128] bf16 buffer (rope_applied
+ *   must be 0, VX_E_RANGE otherwise; it must not overlap any other tensor).
+ *   When given, the call first writes the rotated keys k' there (bf16, the
+ *   exact values the attention uses) and then attends over them, so the keys
+ *   are rotated once instead of once per query tile: two launches, same
+ *   results bit for bit, and faster on long prompts. */
 vx_status vx_gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
                               int32_t T, int32_t Hq, int32_t Hkv, int64_t pos0,
                               int32_t rope_applied, const float *rope_table, int64_t table_p0,
                               int64_t table_len, void *ring_k, void *ring_v, int64_t *pos,
-                              const vx_attn_cfg *cfg, void *stream);
+                              void *k_rot, const vx_attn_cfg *cfg, void *stream);
 
 /* One decode step of S independent streams with n new tokens each, and its
  * ring append, in one launch.  q_new, o: [S,n,Hq,128]; k_new, v_new:

@@ -24,7 +24,8 @@ struct GqaPrefillArgs {
   const bf16* v;  // [B,T,Hkv,128]
   void* o;        // [B,T,Hq,128]
   int B, T, Hq, Hkv, W;
-  bool rope;             // rotate q, k on load from the table
+  bool rope;             // rotate q (and k unless rope_k is false) on load from the table
+  bool rope_k = true;    // false: k holds rotated keys already (written by the rows kernel)
   const float* table;    // [.., 2, 64] cos/sin rows
   int64_t table_row0;    // table row of position pos0
   float scale_log2;      // softmax scale * log2(e)
@@ -54,6 +55,10 @@ constexpr int kGqaMaxCols = 16;  // n * Hq/Hkv query columns per decode workgrou
 hipError_t launch_gqa_rope_table(float* table, int64_t p_begin, int count,
                                  const RopeFreqs128& fr, hipStream_t st);
 hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, DT out, hipStream_t st);
+// k_rot[b,t,h] = k[b,t,h] rotated at position pos0 + t from the table (row
+// table_row0 + t), rounded to bf16: the rotation the prefill's staging applies.
+hipError_t launch_gqa_rope_rows(const bf16* k, bf16* k_rot, int B, int T, int Hkv,
+                                const float* table, int64_t table_row0, hipStream_t st);
 hipError_t launch_gqa_decode(const GqaDecodeArgs& a, DT out, const RopeFreqs128& fr,
                              hipStream_t st);
 

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
   const bf16* __restrict__ v = a.v + (size_t)b * T * krs + (size_t)kvh * kGD;
   TO* __restrict__ o = (TO*)a.o + (size_t)b * T * qrs + (size_t)h * kGD;
   const bool rope = a.rope;
+  const bool rope_k = a.rope && a.rope_k;
 
   const int q0 = qt * BM;
   const int qw = q0 + qb * 32;
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
   const int it0 = kbeg / kBN, it1 = klast / kBN;
 
   GStage<NT> st;
-  gstage_load<NT>(st, k, v, krs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
+  gstage_load<NT>(st, k, v, krs, T, it0 * kBN, rope_k, a.table, a.table_row0, tid);
   if (rope) __syncthreads();  // every wave has read its Q table rows
   GSeed sd0{};
   if (SEED) {
@@ -310,14 +311,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
     sd.kt0 = kt0;
     return sd;
   };
-  gstage_commit<NT, SEED>(st, lds, lds + kTileK, rope, tid, seed_for(it0 * kBN));
+  gstage_commit<NT, SEED>(st, lds, lds + kTileK, rope_k, tid, seed_for(it0 * kBN));
   __syncthreads();
 
   for (int it = it0; it <= it1; ++it) {
     const int buf = (it - it0) & 1;
     const bool more = it < it1;
     if (more)
-      gstage_load<NT>(st, k, v, krs, T, (it + 1) * kBN, rope, a.table, a.table_row0, tid);
+      gstage_load<NT>(st, k, v, krs, T, (it + 1) * kBN, rope_k, a.table, a.table_row0, tid);
 
     const char* Kb = lds + buf * kStage;
     const char* Vb = Kb + kTileK;
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
 
     if (more)
       gstage_commit<NT, SEED>(st, lds + (buf ^ 1) * kStage, lds + (buf ^ 1) * kStage + kTileK,
-                              rope, tid, seed_for((it + 1) * kBN));
+                              rope_k, tid, seed_for((it + 1) * kBN));
     __syncthreads();
   }
 
@@ -460,6 +461,36 @@ hipError_t launch_g(const GqaPrefillArgs& a, DT out, hipStream_t st) {
   return hipGetLastError();
 }
 
+// One thread per (frame, head, chunk pair): dims 8cp.. and their partners
+// 64+8cp.. rotated with the table row of the frame's position.
+__global__ __launch_bounds__(256) void gqa_rope_rows_kernel(const bf16* __restrict__ k,
+                                                            bf16* __restrict__ k_rot, int T,
+                                                            int Hkv, int64_t units,
+                                                            const float* __restrict__ table,
+                                                            int64_t row0) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= units) return;
+  const int cp = (int)(u & 7);
+  const int64_t row = u >> 3;                   // (b*T + t)*Hkv + h
+  const int t = (int)((row / Hkv) % T);
+  const size_t off = (size_t)row * kGD + 8 * cp;
+  float x[8], y[8], c[8], sn[8];
+  load8(k + off, x);
+  load8(k + off + kGHalf, y);
+  const float* cs = table + (row0 + t) * kGD + 8 * cp;
+  load8(cs, c);
+  load8(cs + kGHalf, sn);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float xo, yo;
+    rope_pair(x[e], y[e], c[e], sn[e], &xo, &yo);
+    x[e] = xo;
+    y[e] = yo;
+  }
+  store8(k_rot + off, x);
+  store8(k_rot + off + kGHalf, y);
+}
+
 __global__ void gqa_rope_table_kernel(float* __restrict__ table, int64_t p_begin, int count,
                                       RopeFreqs128 fr) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -484,6 +515,15 @@ hipError_t launch_gqa_prefill(const GqaPrefillArgs& a, DT out, hipStream_t st) {
     case 8: return launch_g<8, 8>(a, out, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_rope_rows(const bf16* k, bf16* k_rot, int B, int T, int Hkv,
+                                const float* table, int64_t table_row0, hipStream_t st) {
+  const int64_t units = (int64_t)B * T * Hkv * 8;
+  const int64_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(gqa_rope_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, k, k_rot, T,
+                     Hkv, units, table, table_row0);
+  return hipGetLastError();
 }
 
 hipError_t launch_gqa_rope_table(float* table, int64_t p_begin, int count,

@@ -470,7 +470,7 @@ vx_status vx_gqa_attn_prefill(const void* q, const void* k, const void* v, void*
                               int32_t T, int32_t Hq, int32_t Hkv, int64_t pos0,
                               int32_t rope_applied, const float* rope_table, int64_t table_p0,
                               int64_t table_len, void* ring_k, void* ring_v, int64_t* pos,
-                              const vx_attn_cfg* cfg, void* stream) {
+                              void* k_rot, const vx_attn_cfg* cfg, void* stream) {
   const char* what = "gqa_prefill";
   vx_status st = check_gqa_cfg(what, cfg);
   if (st) return st;
@@ -519,6 +519,18 @@ vx_status vx_gqa_attn_prefill(const void* q, const void* k, const void* v, void*
     a.ring_v = (vx::bf16*)ring_v;
     a.pos_out = pos;
   }
+  if (k_rot) {
+    if (!a.rope) return fail(VX_E_RANGE, "%s: k_rot needs rope_applied == 0", what);
+    if (!aligned16(k_rot)) return fail(VX_E_ALIGN, "%s: k_rot is not 16-byte aligned", what);
+    if (overlap(k_rot, kb, q, qb) || overlap(k_rot, kb, k, kb) || overlap(k_rot, kb, v, kb) ||
+        overlap(k_rot, kb, o, ob))
+      return fail(VX_E_RANGE, "%s: k_rot overlaps q, k, v or o", what);
+    if (seed) {
+      const size_t rb = (size_t)B * Hkv * cfg->window * vx::kGD * 2;
+      if (overlap(k_rot, kb, ring_k, rb) || overlap(k_rot, kb, ring_v, rb))
+        return fail(VX_E_RANGE, "%s: k_rot overlaps a ring", what);
+    }
+  }
   if (a.rope) {
     if (!rope_table) return fail(VX_E_NULL, "%s: rope_table is NULL and rope_applied == 0", what);
     if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "%s: rope_table is not 16-byte aligned", what);
@@ -531,6 +543,14 @@ vx_status vx_gqa_attn_prefill(const void* q, const void* k, const void* v, void*
     a.table_row0 = pos0 - table_p0;
   }
   (void)hipGetLastError();
+  if (k_rot) {
+    // rotate the keys once into k_rot, then attend over them with only q rotated in the kernel
+    vx_status s1 = launched(vx::launch_gqa_rope_rows(a.k, (vx::bf16*)k_rot, B, T, Hkv, a.table,
+                                                     a.table_row0, (hipStream_t)stream));
+    if (s1) return s1;
+    a.k = (const vx::bf16*)k_rot;
+    a.rope_k = false;
+  }
   return launched(vx::launch_gqa_prefill(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
 }
 

@@ -344,11 +344,11 @@ def test_gqa_prefill_argument_errors(L):
     c64 = gqa_cfg(window=64)
 
     def call(B=1, T=8, Hq=4, Hkv=1, pos0=0, rope_applied=1, c=c64, tlen=0, **ov):
-        a = dict(q=b.new(), k=b.new(), v=b.new(), o=b.new(), table=z, rk=z, rv=z, pos=z)
+        a = dict(q=b.new(), k=b.new(), v=b.new(), o=b.new(), table=z, rk=z, rv=z, pos=z, kr=z)
         a.update(ov)
         return L.vx_gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], B, T, Hq, Hkv, pos0,
                                      rope_applied, a["table"], 0, tlen, a["rk"], a["rv"], a["pos"],
-                                     ctypes.byref(c), None)
+                                     a["kr"], ctypes.byref(c), None)
     assert call(c=gqa_cfg(head_dim=64)) == E_SHAPE
     assert call(c=gqa_cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
     assert call(c=gqa_cfg(out_dtype=5)) == E_DTYPE
@@ -369,6 +369,13 @@ def test_gqa_prefill_argument_errors(L):
     assert call(rk=b.new()) == E_NULL                # seeding needs both rings and pos
     assert call(rk=b.new(), rv=b.new(), pos=b.new(), pos0=2) == E_RANGE
     assert call(rk=b.new(), rv=b.new(), pos=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    assert call(kr=b.new()) == E_RANGE                               # k_rot with rope_applied
+    t8 = b.new()
+    assert call(rope_applied=0, table=t8, tlen=8, kr=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    r = b.new()
+    assert call(rope_applied=0, table=t8, tlen=8, kr=r, k=r) == E_RANGE   # k_rot overlaps k
+    r = b.new()
+    assert call(rope_applied=0, table=t8, tlen=8, kr=r, o=r) == E_RANGE
     assert call(B=0) == OK and call(T=0) == OK
     assert L.vx_last_error().decode() == ""
     assert b.untouched()

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 D = 128
 
 
-def _prefill(x, W, out_dtype="f32", rings=False, fill=0.0, rope_applied=False):
+def _prefill(x, W, out_dtype="f32", rings=False, fill=0.0, rope_applied=False, k_rot=False):
     import torch
     q, k, v = (dev(x[n], "bf16") for n in ("q", "k", "v"))
     B, T, Hkv = k.shape[0], k.shape[1], k.shape[2]
@@ -34,7 +34,7 @@ def _prefill(x, W, out_dtype="f32", rings=False, fill=0.0, rope_applied=False):
         rv = rk.clone()
         pos = torch.full((B,), -7, dtype=torch.int64, device="cuda")
     o = vx.gqa_prefill(q, k, v, window=W, ring_k=rk, ring_v=rv, pos=pos, out_dtype=out_dtype,
-                       rope_applied=rope_applied)
+                       rope_applied=rope_applied, k_rot=torch.empty_like(k) if k_rot else None)
     return o, rk, rv, pos
 
 
@@ -99,11 +99,13 @@ def test_gqa_prefill_pre_rotated_input_equals_fused_rope():
     check_bf16(host(o_fused), host(o_pre), "fused vs pre-rotated")
 
 
-def test_gqa_prefill_full_size_sampled_rows():
+@pytest.mark.parametrize("k_rot", [True, False])
+def test_gqa_prefill_full_size_sampled_rows(k_rot):
     c = synth.GQA_CONFIGS["dec_prefill"]
-    say(f"gqa prefill full size B{c.B} T{c.T} Hq{c.Hq} Hkv{c.Hkv} W{c.W}; oracle on sampled rows")
+    say(f"gqa prefill full size B{c.B} T{c.T} Hq{c.Hq} Hkv{c.Hkv} W{c.W} k_rot {k_rot}; "
+        "oracle on sampled rows")
     x = synth.make_gqa_config("dec_prefill")
-    o, *_ = _prefill(x, c.W, out_dtype="bf16")
+    o, *_ = _prefill(x, c.W, out_dtype="bf16", k_rot=k_rot)
     got = host(o)
     assert np.all(np.isfinite(got))
     for t0 in (0, 1000, c.W - 3, c.W + 517, c.T - 4):
@@ -274,3 +276,31 @@ def test_gqa_decode_batch_invariance():
                             pin[s:s + 1].clone(), pout[s:s + 1].clone(), window=W)
         torch.cuda.synchronize()
         assert torch.equal(one[0], full[s])
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,W", [(2, 150, 8, 2, 64), (1, 700, 32, 8, 256)])
+def test_gqa_prefill_k_rot_path_equals_fused(B, T, Hq, Hkv, W):
+    # keys rotated once into k_rot, then attended: the same outputs and seeded
+    # rings bit for bit as the single fused kernel, and k_rot holds the
+    # bf16-rounded rotated keys
+    import torch
+    say(f"gqa prefill k_rot path B{B} T{T} Hq{Hq} Hkv{Hkv} W{W}")
+    x = synth.make_gqa_prefill(B, T, Hq, Hkv, seed=[41, T])
+    q, k, v = (dev(x[n], "bf16") for n in ("q", "k", "v"))
+    outs = []
+    for use_krot in (False, True):
+        rk = torch.full((B, Hkv, W, D), 3.0, device="cuda").to(torch.bfloat16)
+        rv = rk.clone()
+        pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+        kr = torch.empty_like(k) if use_krot else None
+        o = vx.gqa_prefill(q, k, v, window=W, ring_k=rk, ring_v=rv, pos=pos, k_rot=kr)
+        outs.append((o, rk, rv, pos, kr))
+    torch.cuda.synchronize()
+    (o0, rk0, rv0, p0, _), (o1, rk1, rv1, p1, kr) = outs
+    assert torch.equal(o0, o1) and torch.equal(rk0, rk1) and torch.equal(rv0, rv1)
+    assert torch.equal(p0, p1)
+    want = oracle.bf16_round(oracle.rope(x["k"]))
+    got = host(kr)
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30)
+    assert (got != want).mean() < 1e-3
+    check_bf16(host(o1), oracle.gqa_prefill(x["q"], x["k"], x["v"], W, bf16=True), "k_rot path")
