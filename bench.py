@@ -16,6 +16,12 @@ Printed value: prefill TFLOP/s over the unmasked band FLOPs
 back-to-back launches on the launch stream.  The streaming step is reported
 in microseconds and GB/s of algorithmic HBM bytes.  The CPU baseline is the
 float64 oracle timed on the host on the same prefill workload.
+
+Beside the step, the same line reports the batched first-chunk prefill and
+the text decoder's grouped-query attention (32 query / 8 key-value heads,
+head_dim 128, window 8192): one decode step of 64 streams over full 8192-slot
+rings (ring append fused) and a 16384-token prompt prefill, each with its
+roofline.
 """
 from __future__ import annotations
 
@@ -42,13 +48,17 @@ MEASURED_TRAFFIC = {
                 "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
                 21_649_408 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
-               "e05bc039dade29edacef14b7022e2959c543d4baf0479d16eb70c2a23daa31e0",
-               396_048_794 + 3_146_240),
+               "392de5a1b23d46da0fd550cc1735e47ed831cf1931fa5f58cb8c45371efed8d6",
+               401_122_923 + 3_146_475),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
                     "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
                     156_001_485 + 107_364_352),
-    "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"), None, None),
-    "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"), None, None),
+    "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
+                   "58d336483cea36ccf6aaa7c66a2ea90242154325345e2e3c1387236221245a72",
+                   2_153_809_067 + 786_965),
+    "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
+                    "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
+                    450_898_048 + 134_419_720),
 }
 
 
