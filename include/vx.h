@@ -238,6 +238,48 @@ vx_status vx_gqa_attn_decode(const void *q_new, const void *k_new, const void *v
                              void *o, int32_t S, int32_t n, int32_t Hq, int32_t Hkv,
                              int32_t rope_applied, const vx_attn_cfg *cfg, void *stream);
 
+/* ---- Projections around the encoder's attention -----------------------------
+ * Each Voxtral Realtime 2602 encoder layer projects its normalised hidden
+ * state (width d_model = 1280) to q, k, v of 32 heads x 64, k_proj without a
+ * bias, applies RoPE to q and k, attends, and projects back to d_model with
+ * the output projection (transcribe.cpp "Voxtral" family notes, Architecture,
+ * Voxtral Realtime 2602).  The Core AI port fuses the q/k/v projections into
+ * one matrix product ([Core AI] "Voxtral Mini 4B Realtime - Core AI",
+ * artifact manifest: fused QKV).  Weights are bf16 [out, in] row-major (the
+ * layout of a linear layer's weight), activations bf16 row-major, fp32
+ * accumulation on matrix cores. */
+
+/* y = x w^T (+ bias): x [M, K], w [N, K], bias [N] or NULL, all bf16;
+ * y [M, N] in out_dtype (VX_BF16 or VX_F32).  K must be a multiple of 128 and
+ * N of 32 (VX_E_SHAPE otherwise); M == 0 is a no-op. */
+vx_status vx_linear(const void *x, const void *w, const void *bias, void *y, int32_t M,
+                    int32_t N, int32_t K, int32_t out_dtype, void *stream);
+
+/* Fused q/k/v projection with RoPE for S streams of n new frames:
+ * x [S, n, d_model]; w_qkv [3*H*64, d_model] holds the q rows, then k, then
+ * v; b_q, b_v [H*64] or NULL (k has no bias).  Writes q' = rope(x Wq^T + b_q),
+ * k' = rope(x Wk^T) and v = x Wv^T + b_v as [S, n, H, 64] bf16 (rounded once
+ * after the rotation), frame i of stream s rotated at position pos[s] + i
+ * (pos: device int64 [S]).  Only cfg->rope_theta and cfg->io_dtype (bf16)
+ * are used.  d_model must be a multiple of 128. */
+vx_status vx_enc_qkv_rope(const void *x, const void *w_qkv, const void *b_q, const void *b_v,
+                          const int64_t *pos, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                          void *q, void *k, void *v, const vx_attn_cfg *cfg, void *stream);
+
+/* One streaming step of the encoder's attention block, three launches on
+ * `stream`: vx_enc_qkv_rope at positions pos_in, the fused streaming step and
+ * ring append of vx_swa_attn_stream_step_append over the rotated q', k' (with
+ * pos_out[s] = pos_in[s] + n), and y = o W_o^T + b_o (w_o [d_model, H*64],
+ * b_o [d_model] or NULL).  q, k, v, o: caller-owned [S, n, H, 64] bf16 work
+ * buffers; y [S, n, d_model] in cfg->out_dtype.  Requires 1 <= n <=
+ * min(W, 16), bf16, H*64 and d_model multiples of 128; no buffer the call
+ * writes may overlap another argument. */
+vx_status vx_enc_attn_step(const void *x, const void *w_qkv, const void *b_q, const void *b_v,
+                           const void *w_o, const void *b_o, void *ring_k, void *ring_v,
+                           const int64_t *pos_in, int64_t *pos_out, void *q, void *k, void *v,
+                           void *o, void *y, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                           const vx_attn_cfg *cfg, void *stream);
+
 /* Static description of a status code. */
 const char *vx_status_string(vx_status s);
 

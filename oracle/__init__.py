@@ -261,3 +261,68 @@ def gqa_stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, W, theta=1e6, scal
     if rc != 0:
         raise ValueError("oracle_gqa_stream_step rejected its arguments")
     return o
+
+
+# ---------------------------------------------------------------------------
+# Encoder attention block around the streaming step (projections)
+# ---------------------------------------------------------------------------
+# Voxtral Realtime 2602 audio encoder (transcribe.cpp "Voxtral" family notes,
+# Architecture): each layer projects its normalised hidden state (width 1280)
+# to q, k, v (32 heads x 64), k_proj without a bias, applies RoPE to q and k,
+# attends, and projects back to 1280 with the output projection.  The
+# projections are plain matrix products (numpy matmul in float64 is the step);
+# everything else is the pinned functions above.
+
+def linear(x, w, b=None):
+    """y = x w^T (+ b) in float64; x [M,K], w [N,K], b [N] -> [M,N]."""
+    y = _f64(x) @ _f64(w).T
+    if b is not None:
+        y = y + _f64(b)[None, :]
+    return y
+
+
+def enc_qkv_rope(x, w_qkv, b_q, b_v, pos_rows, H, theta=1e6, bf16=False):
+    """Fused q/k/v projection and RoPE.
+
+    x [M, d_model]; w_qkv [3*H*64, d_model] with the q rows first, then k,
+    then v; b_q, b_v [H*64] (k has no bias); pos_rows [M] absolute positions.
+    Returns q', k' (rotated) and v as [M, H, 64] float64.  bf16=True rounds
+    the three stored tensors to bfloat16 (the rotated q and k after rotation).
+    """
+    HD = H * 64
+    w = _f64(w_qkv)
+    q = linear(x, w[:HD], b_q)
+    k = linear(x, w[HD:2 * HD])
+    v = linear(x, w[2 * HD:], b_v)
+    M = q.shape[0]
+    p = np.asarray(pos_rows, dtype=np.int64).reshape(1, M)
+    q = rope(q.reshape(1, M, H, 64), pos=p, theta=theta)[0]
+    k = rope(k.reshape(1, M, H, 64), pos=p, theta=theta)[0]
+    v = v.reshape(M, H, 64)
+    if bf16:
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    return q, k, v
+
+
+def enc_attn_step(x, w_qkv, b_q, b_v, w_o, b_o, ring_k, ring_v, pos, W, H, theta=1e6,
+                  bf16=False):
+    """One streaming step of the encoder's attention block for S streams.
+
+    x [S, n, d_model] (frames pos[s] .. pos[s]+n-1 of stream s); rings
+    [S, H, W, 64] float64 and pos int64 [S] are advanced in place exactly as
+    ring_append does.  Returns y [S, n, d_model] = attention(q', k', v) w_o^T
+    + b_o.  bf16=True rounds every tensor the block stores between its steps
+    (q', k', v and the attention output o) to bfloat16.
+    """
+    x = _f64(x)
+    S, n, dm = x.shape
+    pos_rows = (np.asarray(pos, dtype=np.int64)[:, None] + np.arange(n)[None, :]).reshape(-1)
+    q, k, v = enc_qkv_rope(x.reshape(S * n, dm), w_qkv, b_q, b_v, pos_rows, H, theta, bf16)
+    shp = (S, n, H, 64)
+    o = stream_step(q.reshape(shp), k.reshape(shp), v.reshape(shp), ring_k, ring_v, pos, W,
+                    theta=theta, rope_applied=True)
+    ring_append(ring_k, ring_v, k.reshape(shp), v.reshape(shp), pos, W, theta=theta,
+                rope_applied=True)
+    if bf16:
+        o = bf16_round(o)
+    return linear(o.reshape(S * n, H * 64), w_o, b_o).reshape(S, n, dm)

@@ -15,7 +15,8 @@ import os
 
 __all__ = [
     "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
-    "stream_step_append", "gqa_prefill", "gqa_decode",
+    "stream_step_append", "gqa_prefill", "gqa_decode", "linear", "enc_qkv_rope",
+    "enc_attn_step",
     "WINDOW", "THETA", "HEAD_DIM", "DEC_WINDOW", "DEC_HEAD_DIM",
 ]
 
@@ -73,6 +74,12 @@ _SIGS = {
                                            ctypes.POINTER(_Cfg), _vp]),
     "vx_gqa_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                           _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
+    "vx_linear": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "vx_enc_qkv_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                       _vp, ctypes.POINTER(_Cfg), _vp]),
+    "vx_enc_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        ctypes.POINTER(_Cfg), _vp]),
     "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vx_last_error": (ctypes.c_char_p, []),
     "vx_version": (_i32, []),
@@ -443,4 +450,129 @@ def gqa_decode(q_new, k_new, v_new, ring_k, ring_v, pos_in, pos_out, window=DEC_
         _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos_in),
         _ptr(pos_out), _ptr(out), S, n, Hq, Hkv, int(bool(rope_applied)), ctypes.byref(cfg),
         _stream(q_new)), "vx_gqa_attn_decode")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# projections around the encoder's attention (bf16 matrix cores)
+# ---------------------------------------------------------------------------
+
+def _bf16_dev(t, name):
+    _dev_tensor(t, name)
+    if _dt(t) != "bf16":
+        raise ValueError(f"{name} must be bfloat16")
+    return t
+
+
+def linear(x, w, bias=None, out=None, out_dtype="bf16"):
+    """y = x w^T (+ bias): x [M, K], w [N, K], bias [N] bf16 -> y [M, N] (bf16 or f32).
+
+    K must be a multiple of 128 and N of 32.
+    """
+    import torch
+    _bf16_dev(x, "x")
+    _bf16_dev(w, "w")
+    if bias is not None:
+        _bf16_dev(bias, "bias")
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    if bias is not None and bias.shape != (N,):
+        raise ValueError("bias must be [N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                          device=x.device)
+    _dev_tensor(out, "out")
+    if out.shape != (M, N):
+        raise ValueError("out must be [M, N]")
+    od = VX_BF16 if _dt(out) == "bf16" else VX_F32
+    _check(lib().vx_linear(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), M, N, K, od, _stream(x)),
+           "vx_linear")
+    return out
+
+
+def enc_qkv_rope(x, w_qkv, b_q, b_v, pos, H=32, theta=THETA, q=None, k=None, v=None):
+    """Fused q/k/v projection with RoPE: x [S, n, d_model] -> q', k', v [S, n, H, 64] bf16.
+
+    w_qkv [3*H*64, d_model] holds the q rows, then k, then v; k has no bias;
+    frame i of stream s sits at position pos[s] + i.
+    """
+    import torch
+    for name, t in (("x", x), ("w_qkv", w_qkv)):
+        _bf16_dev(t, name)
+    for name, t in (("b_q", b_q), ("b_v", b_v)):
+        if t is not None:
+            _bf16_dev(t, name)
+    _dev_tensor(pos, "pos")
+    if x.dim() != 3:
+        raise ValueError("x must be [S, n, d_model]")
+    S, n, dm = x.shape
+    if w_qkv.shape != (3 * H * HEAD_DIM, dm):
+        raise ValueError(f"w_qkv must be [3*H*64, d_model] = {(3 * H * HEAD_DIM, dm)}")
+    if pos.dtype != torch.int64 or pos.shape != (S,):
+        raise ValueError("pos must be int64 [S]")
+    outs = []
+    for t in (q, k, v):
+        if t is None:
+            t = torch.empty((S, n, H, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+        _bf16_dev(t, "q/k/v")
+        if t.shape != (S, n, H, HEAD_DIM):
+            raise ValueError("q, k, v must be [S, n, H, 64]")
+        outs.append(t)
+    cfg = Config(theta=theta).c()
+    _check(lib().vx_enc_qkv_rope(_ptr(x), _ptr(w_qkv), _ptr(b_q), _ptr(b_v), _ptr(pos), S, n, H,
+                                 dm, _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                 ctypes.byref(cfg), _stream(x)), "vx_enc_qkv_rope")
+    return tuple(outs)
+
+
+def enc_attn_step(x, w_qkv, b_q, b_v, w_o, b_o, ring_k, ring_v, pos_in, pos_out, window=WINDOW,
+                  theta=THETA, scale=0.0, H=32, work=None, out=None, out_dtype="bf16"):
+    """One streaming step of the encoder's attention block (three launches):
+    q', k', v = x W_qkv^T (+ b_q, b_v) rotated at pos_in[s] + i; attention over
+    the rings and the new frames, with the ring append; y = o W_o^T + b_o.
+
+    x [S, n, d_model] bf16; rings [S, H, W, 64] bf16; pos_in/pos_out int64 [S]
+    (distinct); work: optional dict of bf16 [S, n, H, 64] buffers q, k, v, o.
+    Returns y [S, n, d_model].
+    """
+    import torch
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("w_o", w_o), ("ring_k", ring_k),
+                    ("ring_v", ring_v)):
+        _bf16_dev(t, name)
+    for name, t in (("b_q", b_q), ("b_v", b_v), ("b_o", b_o)):
+        if t is not None:
+            _bf16_dev(t, name)
+    for name, t in (("pos_in", pos_in), ("pos_out", pos_out)):
+        _dev_tensor(t, name)
+    if x.dim() != 3:
+        raise ValueError("x must be [S, n, d_model]")
+    S, n, dm = x.shape
+    if w_qkv.shape != (3 * H * HEAD_DIM, dm) or w_o.shape != (dm, H * HEAD_DIM):
+        raise ValueError("w_qkv must be [3*H*64, d_model] and w_o [d_model, H*64]")
+    if ring_k.shape != (S, H, window, HEAD_DIM) or ring_v.shape != ring_k.shape:
+        raise ValueError(f"rings must be [S, H, W, 64] = {(S, H, window, HEAD_DIM)}")
+    for t in (pos_in, pos_out):
+        if t.dtype != torch.int64 or t.shape != (S,):
+            raise ValueError("pos_in and pos_out must be int64 [S]")
+    work = dict(work or {})
+    for key in ("q", "k", "v", "o"):
+        if key not in work:
+            work[key] = torch.empty((S, n, H, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+        _bf16_dev(work[key], key)
+        if work[key].shape != (S, n, H, HEAD_DIM):
+            raise ValueError("work buffers must be [S, n, H, 64]")
+    if out is None:
+        out = torch.empty((S, n, dm), dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                          device=x.device)
+    _dev_tensor(out, "out")
+    if out.shape != (S, n, dm):
+        raise ValueError("out must be [S, n, d_model]")
+    cfg = Config(window, theta, scale, "bf16", _dt(out)).c()
+    _check(lib().vx_enc_attn_step(
+        _ptr(x), _ptr(w_qkv), _ptr(b_q), _ptr(b_v), _ptr(w_o), _ptr(b_o), _ptr(ring_k),
+        _ptr(ring_v), _ptr(pos_in), _ptr(pos_out), _ptr(work["q"]), _ptr(work["k"]),
+        _ptr(work["v"]), _ptr(work["o"]), _ptr(out), S, n, H, dm, ctypes.byref(cfg),
+        _stream(x)), "vx_enc_attn_step")
     return out

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "gqa_launch.h"
+#include "linear_launch.h"
 #include "vx.h"
 #include "vx_launch.h"
 
@@ -612,6 +613,194 @@ vx_status vx_gqa_attn_decode(const void* q_new, const void* k_new, const void* v
   (void)hipGetLastError();
   return launched(vx::launch_gqa_decode(a, to_dt(cfg->out_dtype), rope_freqs128(cfg->rope_theta),
                                         (hipStream_t)stream));
+}
+
+// ---- projections around the encoder's attention ---------------------------
+
+static vx_status check_linear_shape(const char* what, int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || N < 1 || K < 1) return fail(VX_E_SHAPE, "%s: need M >= 0, N >= 1, K >= 1", what);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(VX_E_SHAPE, "%s: size too large", what);
+  if (K % vx::kLinKStep != 0)
+    return fail(VX_E_SHAPE, "%s: K (%d) must be a multiple of %d", what, K, vx::kLinKStep);
+  if (N % 32 != 0) return fail(VX_E_SHAPE, "%s: N (%d) must be a multiple of 32", what, N);
+  if ((int64_t)M * K > kMaxElems || (int64_t)N * K > kMaxElems || (int64_t)M * N > kMaxElems)
+    return fail(VX_E_SHAPE, "%s: tensor too large", what);
+  if ((int64_t)((M + 63) / 64) > 65535) return fail(VX_E_SHAPE, "%s: M too large", what);
+  return VX_OK;
+}
+
+vx_status vx_linear(const void* x, const void* w, const void* bias, void* y, int32_t M, int32_t N,
+                    int32_t K, int32_t out_dtype, void* stream) {
+  const char* what = "linear";
+  vx_status st = check_linear_shape(what, M, N, K);
+  if (st) return st;
+  if (out_dtype != VX_BF16 && out_dtype != VX_F32)
+    return fail(VX_E_DTYPE, "%s: unknown output dtype %d", what, out_dtype);
+  if (M == 0) return ok();
+  if (!x || !w || !y) return fail(VX_E_NULL, "%s: x, w and y must be non-NULL", what);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(VX_E_ALIGN, "%s: x, w, bias and y must be 16-byte aligned", what);
+  const size_t yb = (size_t)M * N * elem_size(out_dtype);
+  if (overlap(y, yb, x, (size_t)M * K * 2) || overlap(y, yb, w, (size_t)N * K * 2) ||
+      (bias && overlap(y, yb, bias, (size_t)N * 2)))
+    return fail(VX_E_RANGE, "%s: y overlaps an input", what);
+  vx::LinearArgs a{};
+  a.x = (const vx::bf16*)x;
+  a.w = (const vx::bf16*)w;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bias = (const vx::bf16*)bias;
+  a.y = y;
+  (void)hipGetLastError();
+  return launched(vx::launch_linear(a, to_dt(out_dtype), (hipStream_t)stream));
+}
+
+static vx_status check_block(const char* what, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                             const vx_attn_cfg* cfg) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->io_dtype != VX_BF16) return fail(VX_E_DTYPE, "%s: only bf16 is supported", what);
+  if (cfg->flags != 0) return fail(VX_E_RANGE, "%s: no flags apply (got 0x%x)", what, cfg->flags);
+  if (S < 0 || n < 1 || H < 1) return fail(VX_E_SHAPE, "%s: need S >= 0, n >= 1, H >= 1", what);
+  if ((int64_t)S * n > kMaxDim) return fail(VX_E_SHAPE, "%s: S*n too large", what);
+  if ((st = check_linear_shape(what, S * n, 3 * H * vx::kD, d_model))) return st;
+  if ((st = check_linear_shape(what, S * n, d_model, H * vx::kD))) return st;
+  return VX_OK;
+}
+
+vx_status vx_enc_qkv_rope(const void* x, const void* w_qkv, const void* b_q, const void* b_v,
+                          const int64_t* pos, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                          void* q, void* k, void* v, const vx_attn_cfg* cfg, void* stream) {
+  const char* what = "enc_qkv_rope";
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->io_dtype != VX_BF16) return fail(VX_E_DTYPE, "%s: only bf16 is supported", what);
+  if (S < 0 || n < 1 || H < 1) return fail(VX_E_SHAPE, "%s: need S >= 0, n >= 1, H >= 1", what);
+  if ((int64_t)S * n > kMaxDim) return fail(VX_E_SHAPE, "%s: S*n too large", what);
+  if ((st = check_linear_shape(what, S * n, 3 * H * vx::kD, d_model))) return st;
+  if (S == 0) return ok();
+  if (!x || !w_qkv || !pos || !q || !k || !v)
+    return fail(VX_E_NULL, "%s: x, w_qkv, pos, q, k and v must be non-NULL", what);
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      (b_q && !aligned16(b_q)) || (b_v && !aligned16(b_v)))
+    return fail(VX_E_ALIGN, "%s: tensors must be 16-byte aligned", what);
+  if (((uintptr_t)pos & 7u) != 0) return fail(VX_E_ALIGN, "%s: pos must be 8-byte aligned", what);
+  const size_t ob = (size_t)S * n * H * vx::kD * 2;
+  const size_t xb = (size_t)S * n * d_model * 2, wb = (size_t)3 * H * vx::kD * d_model * 2;
+  const void* outs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], ob, x, xb) || overlap(outs[i], ob, w_qkv, wb))
+      return fail(VX_E_RANGE, "%s: an output overlaps an input", what);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], ob, outs[j], ob)) return fail(VX_E_RANGE, "%s: q, k, v overlap", what);
+  }
+  vx::LinearArgs a{};
+  a.x = (const vx::bf16*)x;
+  a.w = (const vx::bf16*)w_qkv;
+  a.M = S * n;
+  a.N = 3 * H * vx::kD;
+  a.K = d_model;
+  a.HD = H * vx::kD;
+  a.n = n;
+  a.pos = pos;
+  a.b_q = (const vx::bf16*)b_q;
+  a.b_v = (const vx::bf16*)b_v;
+  a.q = (vx::bf16*)q;
+  a.k = (vx::bf16*)k;
+  a.v = (vx::bf16*)v;
+  (void)hipGetLastError();
+  return launched(vx::launch_qkv_rope(a, rope_freqs(cfg->rope_theta), (hipStream_t)stream));
+}
+
+vx_status vx_enc_attn_step(const void* x, const void* w_qkv, const void* b_q, const void* b_v,
+                           const void* w_o, const void* b_o, void* ring_k, void* ring_v,
+                           const int64_t* pos_in, int64_t* pos_out, void* q, void* k, void* v,
+                           void* o, void* y, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                           const vx_attn_cfg* cfg, void* stream) {
+  const char* what = "enc_attn_step";
+  vx_status st = check_block(what, S, n, H, d_model, cfg);
+  if (st) return st;
+  if ((st = check_stream_common(what, S, n, H, cfg))) return st;
+  if (n > vx::kStreamFusedMaxNew)
+    return fail(VX_E_RANGE, "%s: at most %d new frames per step (got %d)", what,
+                vx::kStreamFusedMaxNew, n);
+  if (S == 0) return ok();
+  if (!x || !w_qkv || !w_o || !ring_k || !ring_v || !pos_in || !pos_out || !q || !k || !v || !o ||
+      !y)
+    return fail(VX_E_NULL, "%s: a required pointer is NULL", what);
+  const void* al[] = {x, w_qkv, w_o, ring_k, ring_v, q, k, v, o, y};
+  for (const void* p : al)
+    if (!aligned16(p)) return fail(VX_E_ALIGN, "%s: tensors must be 16-byte aligned", what);
+  if ((b_q && !aligned16(b_q)) || (b_v && !aligned16(b_v)) || (b_o && !aligned16(b_o)))
+    return fail(VX_E_ALIGN, "%s: biases must be 16-byte aligned", what);
+  if (((uintptr_t)pos_in & 7u) != 0 || ((uintptr_t)pos_out & 7u) != 0)
+    return fail(VX_E_ALIGN, "%s: pos_in/pos_out must be 8-byte aligned", what);
+  const size_t M = (size_t)S * n;
+  const size_t act = M * H * vx::kD * 2, xb = M * d_model * 2;
+  const size_t yb = M * d_model * elem_size(cfg->out_dtype);
+  const size_t rb = (size_t)S * H * cfg->window * vx::kD * 2, pb = (size_t)S * sizeof(int64_t);
+  // the buffers the block writes must not overlap anything else it touches
+  const void* wr[] = {q, k, v, o, y, ring_k, ring_v};
+  const size_t wrb[] = {act, act, act, act, yb, rb, rb};
+  const void* all[] = {x, w_qkv, w_o, q, k, v, o, y, ring_k, ring_v};
+  const size_t allb[] = {xb, (size_t)3 * H * vx::kD * d_model * 2, (size_t)d_model * H * vx::kD * 2,
+                         act, act, act, act, yb, rb, rb};
+  for (int i = 0; i < 7; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (wr[i] != all[j] && overlap(wr[i], wrb[i], all[j], allb[j]))
+        return fail(VX_E_RANGE, "%s: buffers overlap", what);
+  if (overlap(pos_in, pb, pos_out, pb))
+    return fail(VX_E_RANGE, "%s: pos_in and pos_out must not overlap", what);
+  (void)hipGetLastError();
+  const hipStream_t hs = (hipStream_t)stream;
+  const vx::RopeFreqs fr = rope_freqs(cfg->rope_theta);
+  // 1. q', k' (rotated at pos_in[s] + i) and v from the hidden state
+  vx::LinearArgs a{};
+  a.x = (const vx::bf16*)x;
+  a.w = (const vx::bf16*)w_qkv;
+  a.M = (int)M;
+  a.N = 3 * H * vx::kD;
+  a.K = d_model;
+  a.HD = H * vx::kD;
+  a.n = n;
+  a.pos = pos_in;
+  a.b_q = (const vx::bf16*)b_q;
+  a.b_v = (const vx::bf16*)b_v;
+  a.q = (vx::bf16*)q;
+  a.k = (vx::bf16*)k;
+  a.v = (vx::bf16*)v;
+  if ((st = launched(vx::launch_qkv_rope(a, fr, hs)))) return st;
+  // 2. attention over the ring and the new frames, then the append (q, k already rotated)
+  vx::StreamArgs sa{};
+  sa.q = q;
+  sa.k = k;
+  sa.v = v;
+  sa.ring_k = ring_k;
+  sa.ring_v = ring_v;
+  sa.pos = pos_in;
+  sa.o = o;
+  sa.S = S;
+  sa.n = n;
+  sa.H = H;
+  sa.W = cfg->window;
+  sa.rope = false;
+  sa.scale_log2 = scale_log2(cfg);
+  sa.append = true;
+  sa.ring_k_w = ring_k;
+  sa.ring_v_w = ring_v;
+  sa.pos_out = pos_out;
+  if ((st = launched(vx::launch_stream_step(sa, vx::DT::BF16, vx::DT::BF16, fr, hs)))) return st;
+  // 3. output projection
+  vx::LinearArgs b{};
+  b.x = (const vx::bf16*)o;
+  b.w = (const vx::bf16*)w_o;
+  b.M = (int)M;
+  b.N = d_model;
+  b.K = H * vx::kD;
+  b.bias = (const vx::bf16*)b_o;
+  b.y = y;
+  return launched(vx::launch_linear(b, to_dt(cfg->out_dtype), hs));
 }
 
 const char* vx_status_string(vx_status s) {

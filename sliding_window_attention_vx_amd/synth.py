@@ -304,3 +304,37 @@ def make_gqa_decode_state(name: str = "dec_decode"):
     assert c.kind == "decode"
     return make_stream_state(c.B, c.Hkv, c.W, seed=c.seed, pos_lo=c.pos_lo, pos_hi=c.pos_hi,
                              dtype=c.dtype, D=c.D)
+
+
+# ---------------------------------------------------------------------------
+# encoder attention block (projections around the streaming step)
+# ---------------------------------------------------------------------------
+# One encoder layer's q/k/v and output projections (d_model 1280, 32 heads x
+# 64, k_proj without a bias) around the streaming step of the stream
+# workload: 64 streams x 4 new frames.
+
+ENC_BLOCK = dict(S=64, n=4, H=32, d_model=1280, W=750, seed=8, pos_lo=750, pos_hi=20000)
+
+
+def make_enc_block_weights(d_model: int, H: int, *, seed):
+    """Synthetic projection weights at a trained layer's scale, bf16 values in float32 arrays.
+
+    w_qkv [3*H*64, d_model] (q rows, then k, then v) and w_o [d_model, H*64]
+    are N(0, 1/fan_in); b_q, b_v [H*64] and b_o [d_model] are 0.02*N(0,1).
+    Draw order: w_qkv, b_q, b_v, w_o, b_o.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2024])))
+    HD = H * 64
+    w_qkv = rng.standard_normal((3 * HD, d_model), dtype=np.float32) * np.float32(d_model ** -0.5)
+    b_q = rng.standard_normal(HD, dtype=np.float32) * np.float32(0.02)
+    b_v = rng.standard_normal(HD, dtype=np.float32) * np.float32(0.02)
+    w_o = rng.standard_normal((d_model, HD), dtype=np.float32) * np.float32(HD ** -0.5)
+    b_o = rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.02)
+    return {name: _store(a, "bf16") for name, a in
+            (("w_qkv", w_qkv), ("b_q", b_q), ("b_v", b_v), ("w_o", w_o), ("b_o", b_o))}
+
+
+def make_enc_block_input(S: int, n: int, d_model: int, *, seed, step: int):
+    """Normalised hidden states x [S, n, d_model] (N(0,1), bf16) for streaming step `step`."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77, step])))
+    return _store(rng.standard_normal((S, n, d_model), dtype=np.float32), "bf16")

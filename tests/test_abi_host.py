@@ -41,7 +41,8 @@ def test_header_declares_the_four_calls():
     for f in ("vx_rope_qk", "vx_swa_attn_prefill", "vx_swa_attn_stream_step", "vx_kv_ring_append",
               "vx_swa_attn_stream_step_append", "vx_rope_table", "vx_status_string",
               "vx_last_error", "vx_version", "vx_default_cfg", "vx_swa_attn_prefill_varlen",
-              "vx_default_gqa_cfg", "vx_gqa_attn_prefill", "vx_gqa_attn_decode"):
+              "vx_default_gqa_cfg", "vx_gqa_attn_prefill", "vx_gqa_attn_decode", "vx_linear",
+              "vx_enc_qkv_rope", "vx_enc_attn_step"):
         assert f in names
 
 
@@ -421,4 +422,74 @@ def test_rope_table_head_dims(L):
     assert L.vx_rope_table(q, 0, 3, ctypes.byref(cfg(head_dim=96)), None) == E_SHAPE
     assert L.vx_rope_table(q, -1, 3, ctypes.byref(gqa_cfg()), None) == E_RANGE
     assert L.vx_rope_table(ctypes.c_void_p(0), 0, 0, ctypes.byref(gqa_cfg()), None) == OK
+    assert b.untouched()
+
+
+# ---------------------------------------------------------------------------
+# projections around the encoder's attention
+# ---------------------------------------------------------------------------
+
+def test_linear_argument_errors(L):
+    b = Bufs()
+    z = ctypes.c_void_p(0)
+
+    def call(M=4, N=64, K=128, od=vx.VX_BF16, **ov):
+        a = dict(x=b.new(), w=b.new(), bias=z, y=b.new())
+        a.update(ov)
+        return L.vx_linear(a["x"], a["w"], a["bias"], a["y"], M, N, K, od, None)
+    assert call(K=100) == E_SHAPE       # K not a multiple of 128
+    assert call(N=48) == E_SHAPE        # N not a multiple of 32
+    assert call(N=0) == E_SHAPE
+    assert call(M=-1) == E_SHAPE
+    assert call(od=7) == E_DTYPE
+    assert call(x=z) == E_NULL
+    assert call(w=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    assert call(bias=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    r = b.new()
+    assert call(x=r, y=r) == E_RANGE
+    assert call(M=0) == OK
+    assert b.untouched()
+
+
+def test_enc_qkv_rope_and_attn_step_errors(L):
+    b = Bufs()
+    z = ctypes.c_void_p(0)
+    c = cfg()
+
+    def qkv(S=2, n=4, H=2, dm=128, cc=c, **ov):
+        a = dict(x=b.new(), w=b.new(), bq=z, bv=z, pos=b.new(), q=b.new(), k=b.new(), v=b.new())
+        a.update(ov)
+        return L.vx_enc_qkv_rope(a["x"], a["w"], a["bq"], a["bv"], a["pos"], S, n, H, dm, a["q"],
+                                 a["k"], a["v"], ctypes.byref(cc), None)
+    assert qkv(dm=96) == E_SHAPE
+    assert qkv(H=0) == E_SHAPE
+    assert qkv(n=0) == E_SHAPE
+    assert qkv(cc=cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
+    assert qkv(pos=z) == E_NULL
+    assert qkv(pos=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    r = b.new()
+    assert qkv(q=r, k=r) == E_RANGE
+    r = b.new()
+    assert qkv(x=r, v=r) == E_RANGE
+    assert qkv(S=0) == OK
+
+    def step(S=2, n=4, H=2, dm=128, cc=c, **ov):
+        a = dict(x=b.new(), wqkv=b.new(), bq=z, bv=z, wo=b.new(), bo=z, rk=b.new(), rv=b.new(),
+                 pin=b.new(), pout=b.new(), q=b.new(), k=b.new(), v=b.new(), o=b.new(), y=b.new())
+        a.update(ov)
+        return L.vx_enc_attn_step(a["x"], a["wqkv"], a["bq"], a["bv"], a["wo"], a["bo"], a["rk"],
+                                  a["rv"], a["pin"], a["pout"], a["q"], a["k"], a["v"], a["o"],
+                                  a["y"], S, n, H, dm, ctypes.byref(cc), None)
+    assert step(n=17) == E_RANGE           # above the fused step's 16 frames
+    assert step(H=1) == E_SHAPE            # H*64 = 64 is not a multiple of 128
+    assert step(dm=200) == E_SHAPE
+    p = b.new()
+    assert step(pin=p, pout=p) == E_RANGE
+    r = b.new()
+    assert step(o=r, y=r) == E_RANGE
+    r = b.new()
+    assert step(q=r, rk=r) == E_RANGE
+    assert step(y=z) == E_NULL
+    assert step(cc=cfg(flags=1)) == E_RANGE
+    assert step(S=0) == OK
     assert b.untouched()

@@ -542,3 +542,67 @@ def test_decoder_constants_match_pages():
         assert cfg.D == c["text_decoder_head_dim"]["value"]
         assert cfg.W == c["text_decoder_window"]["value"]
         assert cfg.theta == c["text_decoder_rope_theta"]["value"]
+
+
+# --------------------------------------------------------------------------
+# encoder attention block: projections around the streaming step
+# --------------------------------------------------------------------------
+
+def test_linear_matches_loops():
+    x, w, b = rnd((3, 5), 100), rnd((4, 5), 101), rnd(4, 102)
+    got = oracle.linear(x, w, b)
+    for m in range(3):
+        for n in range(4):
+            want = b[n] + sum(x[m, kk] * w[n, kk] for kk in range(5))
+            assert abs(got[m, n] - want) < 1e-12
+    np.testing.assert_allclose(oracle.linear(x, w), got - b[None, :], rtol=0, atol=1e-12)
+
+
+def test_qkv_rope_split_order_bias_and_positions():
+    # d_model 64, one head: q rows = I (plus b_q), k rows = 2I (no bias), v rows = a
+    # permutation (plus b_v); so q' and k' are rotations of known vectors at the
+    # row positions, and v is the permuted input plus its bias.
+    M, H = 5, 1
+    x = rnd((M, 64), 103)
+    perm = np.random.default_rng(104).permutation(64)
+    w = np.concatenate([np.eye(64), 2 * np.eye(64), np.eye(64)[perm]])
+    bq, bv = rnd(64, 105), rnd(64, 106)
+    pos = np.array([0, 1, 749, 750, 123456])
+    q, k, v = oracle.enc_qkv_rope(x, w, bq, bv, pos, H)
+    np.testing.assert_allclose(q[:, 0], complex_rope((x + bq)[:, None], pos)[:, 0], atol=1e-12)
+    np.testing.assert_allclose(k[:, 0], complex_rope((2 * x)[:, None], pos)[:, 0], atol=1e-12)
+    np.testing.assert_array_equal(v[:, 0], x[:, perm] + bv)
+
+
+def test_enc_attn_step_zero_output_weights_give_bias():
+    S, n, H, W, dm = 2, 3, 2, 8, 16
+    x = rnd((S, n, dm), 107)
+    w_qkv, bq, bv = rnd((3 * H * 64, dm), 108), rnd(H * 64, 109), rnd(H * 64, 110)
+    b_o = rnd(dm, 111)
+    rk, rv = np.zeros((S, H, W, 64)), np.zeros((S, H, W, 64))
+    pos = np.array([0, 5], dtype=np.int64)
+    y = oracle.enc_attn_step(x, w_qkv, bq, bv, np.zeros((dm, H * 64)), b_o, rk, rv, pos, W, H)
+    np.testing.assert_array_equal(y, np.broadcast_to(b_o, y.shape))
+    assert list(pos) == [3, 8]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_enc_attn_step_streamed_equals_prefill_of_projected_sequence(bf16):
+    # Streaming the block n frames at a time over a W-slot ring gives the same
+    # y as projecting the whole sequence, one prefill over it, and the output
+    # projection (the bf16 contract rounds q', k', v and o on both sides).
+    T, H, W, dm, n = 40, 2, 12, 32, 4
+    x = rnd((1, T, dm), 112) * 0.5
+    w_qkv = rnd((3 * H * 64, dm), 113) / np.sqrt(dm)
+    bq, bv = rnd(H * 64, 114) * 0.1, rnd(H * 64, 115) * 0.1
+    w_o, b_o = rnd((dm, H * 64), 116) / np.sqrt(H * 64), rnd(dm, 117) * 0.1
+    rk, rv = np.full((1, H, W, 64), 1e3), np.full((1, H, W, 64), -1e3)
+    pos = np.zeros(1, dtype=np.int64)
+    got = np.concatenate([oracle.enc_attn_step(x[:, t:t + n], w_qkv, bq, bv, w_o, b_o, rk, rv, pos,
+                                               W, H, bf16=bf16) for t in range(0, T, n)], axis=1)
+    q, k, v = oracle.enc_qkv_rope(x[0], w_qkv, bq, bv, np.arange(T), H, bf16=bf16)
+    o = oracle.prefill(q[None], k[None], v[None], W, rope_applied=True)[0]
+    if bf16:
+        o = oracle.bf16_round(o)
+    want = oracle.linear(o.reshape(T, H * 64), w_o, b_o)
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-12)
