@@ -56,6 +56,8 @@ MEASURED_TRAFFIC = {
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "58d336483cea36ccf6aaa7c66a2ea90242154325345e2e3c1387236221245a72",
                    2_153_809_067 + 786_965),
+    "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"), None, None),
+    "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"), None, None),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
                     "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
                     450_898_048 + 134_419_720),
@@ -116,7 +118,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=60,
                     help="oracle repetitions of the prefill workload for the CPU baseline")
     ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "gqa_prefill",
-                                       "gqa_decode", "copy"], default=None,
+                                       "gqa_decode", "qkv", "oproj", "enc_block", "copy"],
+                    default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
                          "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
     ap.add_argument("--copy-mib", type=int, default=1024)
@@ -230,6 +233,39 @@ def main():
     def gqa_prefill_fused(i):
         vx.gqa_prefill(gq, gk, gv, window=gc.W, table=gtab, out=go)
 
+    # ---- encoder attention block: q/k/v projection + RoPE, attention step, output projection
+    ec = synth.ENC_BLOCK
+    ew = {k_: to(v_) for k_, v_ in synth.make_enc_block_weights(ec["d_model"], ec["H"],
+                                                                 seed=ec["seed"]).items()}
+    est = synth.make_stream_state(ec["S"], ec["H"], ec["W"], seed=[ec["seed"], 1],
+                                  pos_lo=ec["pos_lo"], pos_hi=ec["pos_hi"])
+    ering = {"k": to(est["ring_k"]), "v": to(est["ring_v"]), "c": 0,
+             "pos": [torch.from_numpy(est["pos"].copy()).to(dev)]}
+    ering["pos"].append(ering["pos"][0].clone())
+    ex = [to(synth.make_enc_block_input(ec["S"], ec["n"], ec["d_model"], seed=ec["seed"], step=i))
+          for i in range(8)]
+    eshape = (ec["S"], ec["n"], ec["H"], 64)
+    ework = {k_: torch.empty(eshape, dtype=torch.bfloat16, device=dev) for k_ in "qkvo"}
+    ey = torch.empty_like(ex[0])
+    eM, eHD, edm = ec["S"] * ec["n"], ec["H"] * 64, ec["d_model"]
+    qkv_bytes = 3 * eHD * edm * 2 + eM * edm * 2 + 3 * eM * eHD * 2 + 2 * eHD * 2 + ec["S"] * 8
+    oproj_bytes = edm * eHD * 2 + eM * eHD * 2 + eM * edm * 2 + edm * 2
+    blk_bytes = qkv_bytes + stream_bytes(ec["S"], ec["n"], ec["H"], ec["W"]) + oproj_bytes
+
+    def enc_block(i):
+        c = ering["c"]
+        vx.enc_attn_step(ex[i % 8], ew["w_qkv"], ew["b_q"], ew["b_v"], ew["w_o"], ew["b_o"],
+                         ering["k"], ering["v"], ering["pos"][c % 2], ering["pos"][(c + 1) % 2],
+                         window=ec["W"], H=ec["H"], work=ework, out=ey)
+        ering["c"] = c + 1
+
+    def qkv(i):
+        vx.enc_qkv_rope(ex[i % 8], ew["w_qkv"], ew["b_q"], ew["b_v"], ering["pos"][0], H=ec["H"],
+                        q=ework["q"], k=ework["k"], v=ework["v"])
+
+    def oproj(i):
+        vx.linear(ework["o"].view(eM, eHD), ew["w_o"], ew["b_o"], out=ey.view(eM, edm))
+
     def prefill():
         vx.prefill(q, k, v, window=pc.W, table=table, out=o)
 
@@ -261,7 +297,8 @@ def main():
               "first_chunk": lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"],
                                                          window=fc["W"], table=ftab, ring_k=frk,
                                                          ring_v=frv, pos=fpos, out=fo),
-              "gqa_prefill": gqa_prefill, "gqa_decode": gqa_decode}[args.only]
+              "gqa_prefill": gqa_prefill, "gqa_decode": gqa_decode, "qkv": qkv, "oproj": oproj,
+              "enc_block": enc_block}[args.only]
         for j in range(args.warmup):
             fn(j)
         torch.cuda.synchronize()
@@ -324,6 +361,9 @@ def main():
     attend_us = per_launch_us(lambda j: stream(j), reps)
     two_call_us = per_launch_us(lambda j: append(stream(j)), reps)
 
+    blk_us = per_launch_us(enc_block, reps)
+    qkv_us = per_launch_us(qkv, reps)
+    oproj_us = per_launch_us(oproj, reps)
     dec_us = per_launch_us(gqa_decode, reps)
     gpre_us = per_launch_us(gqa_prefill, max(K // 5, 5))
     gpre_fused_us = per_launch_us(gqa_prefill_fused, max(K // 5, 5))
@@ -413,6 +453,27 @@ def main():
                          "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("gqa_prefill")},
         },
+    }
+
+    out["enc_block"] = {
+        "workload": f"encoder attention block step S{ec['S']} n{ec['n']} d_model {edm} "
+                    f"H{ec['H']} D64 W{ec['W']} bf16: q/k/v projection with RoPE, attention "
+                    f"step with ring append, output projection (three launches)",
+        "us_per_step": round(blk_us, 3),
+        "GBps_algorithmic": round(blk_bytes / (blk_us * 1e-6) / 1e9, 1),
+        "qkv_rope_us": round(qkv_us, 3),
+        "out_proj_us": round(oproj_us, 3),
+        "roofline_qkv": {"kernel": "linear_kernel (q/k/v + RoPE epilogue)", "bound": "hbm",
+                         "achieved": round(qkv_bytes / (qkv_us * 1e-6) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(qkv_bytes / (qkv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("qkv")},
+        "roofline_out_proj": {"kernel": "linear_kernel (bias epilogue)", "bound": "hbm",
+                              "achieved": round(oproj_bytes / (oproj_us * 1e-6) / 1e9, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(oproj_bytes / (oproj_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                            4),
+                              "traffic": measured_traffic("oproj")},
     }
 
     if not args.no_cpu_baseline:

@@ -261,7 +261,7 @@ vx_status vx_linear(const void *x, const void *w, const void *bias, void *y, int
  * k' = rope(x Wk^T) and v = x Wv^T + b_v as [S, n, H, 64] bf16 (rounded once
  * after the rotation), frame i of stream s rotated at position pos[s] + i
  * (pos: device int64 [S]).  Only cfg->rope_theta and cfg->io_dtype (bf16)
- * are used.  d_model must be a multiple of 128. */
+ * are used.  d_model and H*64 must be multiples of 128. */
 vx_status vx_enc_qkv_rope(const void *x, const void *w_qkv, const void *b_q, const void *b_v,
                           const int64_t *pos, int32_t S, int32_t n, int32_t H, int32_t d_model,
                           void *q, void *k, void *v, const vx_attn_cfg *cfg, void *stream);

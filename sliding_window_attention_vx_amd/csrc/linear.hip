@@ -10,10 +10,12 @@
 // x and w rows go global -> registers -> LDS (rows padded to 272 bytes so the
 // 16-byte operand reads of 16 consecutive rows hit distinct banks), with the
 // next two stages' loads in flight in two register sets while the current
-// stage computes.  The epilogue parks the fp32 tile in LDS and writes whole
-// 16-byte chunks: either y + bias (bf16 or fp32), or, for the fused q/k/v
-// projection, q + b_q and k rotated at each row's position (RoPE pairs d and
-// d+32 of a head lie in the same 64-column tile), v + b_v, all rounded to bf16.
+// stage computes (buffer loads with loop-invariant per-lane offsets, all
+// unconditional, so the compiler keeps both stages in flight).  The epilogue
+// parks the fp32 tile in LDS and writes whole 16-byte chunks: either
+// y + bias (bf16 or fp32), or, for the fused q/k/v projection, q + b_q and k
+// rotated at each row's position (RoPE pairs d and d+32 of a head lie in the
+// same 64-column tile), v + b_v, all rounded to bf16.
 #include "linear_launch.h"
 
 namespace vx {
@@ -55,20 +57,36 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
     u32x4 w[TL::PW];
   };
   // chunk u of a stage: row u / CH, 16-byte chunk u % CH (16 consecutive lanes
-  // read one contiguous 256-byte row segment); rows past M repeat row M-1
+  // read one contiguous 256-byte row segment); rows past M repeat row M-1.
+  // Buffer loads: each thread's byte offsets within the tile's rows stay in
+  // VGPRs for the whole K loop and a stage adds its k offset as a scalar, so
+  // no address registers are rebuilt per stage (rebuilt 64-bit addresses land
+  // in registers of loads still in flight and force waits for them).  Each
+  // resource covers the tile's rows exactly.
+  uint32_t xo[TL::PX], wo[TL::PW];
+#pragma unroll
+  for (int j = 0; j < TL::PX; ++j) {
+    const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
+    xo[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < TL::PW; ++j) {
+    const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
+    wo[j] = (uint32_t)(r * K + 8 * c) * 2u;
+  }
+  const int xrows = min(MT, M - m0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(x + (size_t)m0 * K), (short)0, xrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(w + (size_t)n0 * K), (short)0, NC * K * 2, 0x00020000);
   auto load = [&](int s, Stage& R) {
-    const int k0 = s * kKS;
+    const int ko = s * kKS * 2;  // uniform byte offset of the stage
 #pragma unroll
-    for (int j = 0; j < TL::PX; ++j) {
-      const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-      const int row = min(m0 + r, M - 1);
-      R.x[j] = *reinterpret_cast<const u32x4*>(x + (size_t)row * K + k0 + 8 * c);
-    }
+    for (int j = 0; j < TL::PX; ++j)
+      R.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo[j], ko, 0));
 #pragma unroll
-    for (int j = 0; j < TL::PW; ++j) {
-      const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-      R.w[j] = *reinterpret_cast<const u32x4*>(w + (size_t)(n0 + r) * K + k0 + 8 * c);
-    }
+    for (int j = 0; j < TL::PW; ++j)
+      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo[j], ko, 0));
   };
   auto commit = [&](const Stage& R, int b) {
     char* base = lds + b * TL::STAGE;
@@ -97,23 +115,26 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
     }
   };
 
-  const int nk = K / kKS;
+  // Every load is unconditional (past the last stage it repeats the last
+  // stage, which the caches hold): with conditional loads the compiler cannot
+  // count the loads in flight across the branch and waits for all of them
+  // before each commit, which leaves one stage in flight instead of two.
+  const int nk = K / kKS, last = nk - 1;
   Stage R0, R1;
   load(0, R0);
-  if (nk > 1) load(1, R1);
+  load(min(1, last), R1);
   commit(R0, 0);
   __syncthreads();
   for (int s = 0; s < nk; s += 2) {
-    if (s + 2 < nk) load(s + 2, R0);
+    load(min(s + 2, last), R0);
     compute(0);
-    if (s + 1 < nk) commit(R1, 1);
+    commit(R1, 1);
     __syncthreads();
-    if (s + 1 < nk) {
-      if (s + 3 < nk) load(s + 3, R1);
-      compute(1);
-      if (s + 2 < nk) commit(R0, 0);
-      __syncthreads();
-    }
+    if (s + 1 >= nk) break;
+    load(min(s + 3, last), R1);
+    compute(1);
+    commit(R0, 0);
+    __syncthreads();
   }
 
   // ---- epilogue: the fp32 tile through LDS (the last loop step ended with a barrier)

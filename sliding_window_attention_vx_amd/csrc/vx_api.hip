@@ -626,6 +626,9 @@ static vx_status check_linear_shape(const char* what, int32_t M, int32_t N, int3
   if ((int64_t)M * K > kMaxElems || (int64_t)N * K > kMaxElems || (int64_t)M * N > kMaxElems)
     return fail(VX_E_SHAPE, "%s: tensor too large", what);
   if ((int64_t)((M + 63) / 64) > 65535) return fail(VX_E_SHAPE, "%s: M too large", what);
+  // the kernel addresses x and w with 32-bit byte offsets
+  if ((int64_t)M * K * 2 >= ((int64_t)1 << 30) || (int64_t)N * K * 2 >= ((int64_t)1 << 30))
+    return fail(VX_E_SHAPE, "%s: x and w must each be smaller than 2^30 bytes", what);
   return VX_OK;
 }
 
@@ -679,6 +682,7 @@ vx_status vx_enc_qkv_rope(const void* x, const void* w_qkv, const void* b_q, con
   if (S < 0 || n < 1 || H < 1) return fail(VX_E_SHAPE, "%s: need S >= 0, n >= 1, H >= 1", what);
   if ((int64_t)S * n > kMaxDim) return fail(VX_E_SHAPE, "%s: S*n too large", what);
   if ((st = check_linear_shape(what, S * n, 3 * H * vx::kD, d_model))) return st;
+  if ((H * vx::kD) % 128 != 0) return fail(VX_E_SHAPE, "%s: H*64 must be a multiple of 128", what);
   if (S == 0) return ok();
   if (!x || !w_qkv || !pos || !q || !k || !v)
     return fail(VX_E_NULL, "%s: x, w_qkv, pos, q, k and v must be non-NULL", what);

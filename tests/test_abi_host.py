@@ -462,6 +462,7 @@ def test_enc_qkv_rope_and_attn_step_errors(L):
         return L.vx_enc_qkv_rope(a["x"], a["w"], a["bq"], a["bv"], a["pos"], S, n, H, dm, a["q"],
                                  a["k"], a["v"], ctypes.byref(cc), None)
     assert qkv(dm=96) == E_SHAPE
+    assert qkv(H=1) == E_SHAPE             # H*64 = 64 is not a multiple of 128
     assert qkv(H=0) == E_SHAPE
     assert qkv(n=0) == E_SHAPE
     assert qkv(cc=cfg(io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
