@@ -56,8 +56,12 @@ MEASURED_TRAFFIC = {
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "58d336483cea36ccf6aaa7c66a2ea90242154325345e2e3c1387236221245a72",
                    2_153_809_067 + 786_965),
-    "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"), None, None),
-    "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"), None, None),
+    "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"),
+            "22f12534bc1b27ef3816031917746027bb203db0be6fbec5383633e9faee0c4c",
+            21_198_336 + 3_145_728),
+    "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"),
+              "22f12534bc1b27ef3816031917746027bb203db0be6fbec5383633e9faee0c4c",
+              13_699_819 + 655_360),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
                     "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
                     450_898_048 + 134_419_720),
