@@ -326,3 +326,95 @@ def enc_attn_step(x, w_qkv, b_q, b_v, w_o, b_o, ring_k, ring_v, pos, W, H, theta
     if bf16:
         o = bf16_round(o)
     return linear(o.reshape(S * n, H * 64), w_o, b_o).reshape(S, n, dm)
+
+
+# ---------------------------------------------------------------------------
+# Whole streaming encoder step: conv stem and transformer layers
+# ---------------------------------------------------------------------------
+# Voxtral Realtime 2602 audio encoder (transcribe.cpp "Voxtral" family notes,
+# Architecture): a causal (left-pad-only) conv stem, conv1 128 -> 1280 kernel
+# 3 stride 1 and conv2 1280 -> 1280 kernel 3 stride 2, each followed by GELU;
+# then 32 pre-norm layers: RMSNorm, the attention block, residual add,
+# RMSNorm, a SwiGLU MLP (bias only on the down projection), residual add.
+# Streaming feeds 8 mel frames per step (4 encoder frames, one audio token).
+
+def rmsnorm(x, g, eps=1e-5):
+    """x / sqrt(mean(x^2) + eps) * g over the last axis, float64."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(g)
+
+
+def gelu(x):
+    """GELU with the exact error function: x * (1 + erf(x / sqrt(2))) / 2."""
+    from scipy.special import erf
+    x = _f64(x)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def silu(x):
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def causal_conv1d(xpad, w, b, stride):
+    """Causal 1-D convolution over frames.
+
+    xpad [S, P + T, C_in]: each stream's input frames preceded by its P = k-1
+    cached frames; w [C_out, k, C_in]; b [C_out].  Output frame t (0 <= t <
+    (T - 1) // stride + 1 ... for T a multiple of stride, T // stride) reads
+    padded frames stride*t .. stride*t + k - 1, i.e. input frames up to
+    stride*t (left padding only).  Returns [S, T // stride, C_out].
+    """
+    xpad, w = _f64(xpad), _f64(w)
+    S, TP, Ci = xpad.shape
+    Co, k, _ = w.shape
+    T = TP - (k - 1)
+    n_out = T // stride
+    out = np.empty((S, n_out, Co))
+    for t in range(n_out):
+        win = xpad[:, stride * t:stride * t + k, :].reshape(S, k * Ci)
+        out[:, t] = win @ w.reshape(Co, k * Ci).T
+    return out + _f64(b)[None, None, :]
+
+
+def enc_stem_step(mel_new, mel_cache, c1_cache, w1, b1, w2, b2, bf16=False):
+    """One streaming step of the conv stem for S streams.
+
+    mel_new [S, 8, 128]; mel_cache [S, 2, 128] and c1_cache [S, 2, 1280] are
+    each conv's last two input frames (updated in place).  Returns the 4 new
+    encoder frames [S, 4, 1280].  bf16=True rounds the stored conv outputs.
+    """
+    xp = np.concatenate([_f64(mel_cache), _f64(mel_new)], axis=1)
+    c1 = gelu(causal_conv1d(xp, w1, b1, 1))
+    if bf16:
+        c1 = bf16_round(c1)
+    c1p = np.concatenate([_f64(c1_cache), c1], axis=1)
+    out = gelu(causal_conv1d(c1p, w2, b2, 2))
+    if bf16:
+        out = bf16_round(out)
+    mel_cache[:] = xp[:, -2:]
+    c1_cache[:] = c1p[:, -2:]
+    return out
+
+
+def enc_layer_step(x, wts, ring_k, ring_v, pos, W, H, theta=1e6, eps=1e-5, bf16=False):
+    """One pre-norm encoder layer on the streaming residual x [S, n, d_model]
+    (float64, returned updated).  wts: g_attn, w_qkv, b_q, b_v, w_o, b_o,
+    g_ffn, w_gate, w_up, w_down, b_down.  Rings and pos advance in place.
+    bf16=True rounds every tensor stored between launches (the normalised
+    states, q', k', v, o and the SwiGLU hidden state)."""
+    x = _f64(x)
+    S, n, dm = x.shape
+    h = rmsnorm(x, wts["g_attn"], eps)
+    if bf16:
+        h = bf16_round(h)
+    x = x + enc_attn_step(h, wts["w_qkv"], wts["b_q"], wts["b_v"], wts["w_o"], wts["b_o"], ring_k,
+                          ring_v, pos, W, H, theta=theta, bf16=bf16)
+    h = rmsnorm(x, wts["g_ffn"], eps)
+    if bf16:
+        h = bf16_round(h)
+    h2 = h.reshape(S * n, dm)
+    u = silu(linear(h2, wts["w_gate"])) * linear(h2, wts["w_up"])
+    if bf16:
+        u = bf16_round(u)
+    return x + linear(u, wts["w_down"], wts["b_down"]).reshape(S, n, dm)

@@ -606,3 +606,95 @@ def test_enc_attn_step_streamed_equals_prefill_of_projected_sequence(bf16):
         o = oracle.bf16_round(o)
     want = oracle.linear(o.reshape(T, H * 64), w_o, b_o)
     np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# whole encoder step: norms, activations, conv stem, layer
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_closed_forms():
+    g = rnd(6, 120)
+    c = 2.5
+    y = oracle.rmsnorm(np.full((1, 6), c), g, eps=0.0)
+    np.testing.assert_allclose(y[0], g * np.sign(c), atol=1e-15)
+    y = oracle.rmsnorm(np.full((1, 6), 0.1), np.ones(6), eps=0.01)
+    np.testing.assert_allclose(y, 0.1 / math.sqrt(0.01 + 0.01), atol=1e-15)
+    x = rnd((3, 1280), 121)
+    r = oracle.rmsnorm(x, np.ones(1280), eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(r * r, axis=-1)), 1.0, atol=1e-12)
+
+
+def test_gelu_and_silu_against_standard_library():
+    xs = np.linspace(-6, 6, 97)
+    want = [0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in xs]
+    np.testing.assert_allclose(oracle.gelu(xs), want, rtol=0, atol=1e-15)
+    assert oracle.gelu(np.array([1.0]))[0] == pytest.approx(0.8413447460685429, abs=1e-15)
+    # silu(ln 3) = ln 3 * sigmoid(ln 3) = 0.75 ln 3
+    assert oracle.silu(np.array([math.log(3)]))[0] == pytest.approx(0.75 * math.log(3), abs=1e-15)
+    np.testing.assert_allclose(oracle.silu(xs), [v / (1 + math.exp(-v)) for v in xs], atol=1e-15)
+
+
+@pytest.mark.parametrize("stride", [1, 2])
+def test_causal_conv1d_brute_force_and_causality(stride):
+    S, T, Ci, Co, k = 2, 8, 3, 4, 3
+    xp = rnd((S, T + k - 1, Ci), 122)
+    w, b = rnd((Co, k, Ci), 123), rnd(Co, 124)
+    y = oracle.causal_conv1d(xp, w, b, stride)
+    assert y.shape == (S, T // stride, Co)
+    for s in range(S):
+        for t in range(T // stride):
+            for o in range(Co):
+                want = b[o] + sum(w[o, j, c] * xp[s, stride * t + j, c]
+                                  for j in range(k) for c in range(Ci))
+                assert abs(y[s, t, o] - want) < 1e-12
+    # output t reads padded frames up to stride*t + k - 1 only
+    xq = xp.copy()
+    xq[:, stride * 2 + k:] += 100.0
+    np.testing.assert_array_equal(oracle.causal_conv1d(xq, w, b, stride)[:, :3], y[:, :3])
+
+
+def test_stem_streamed_equals_offline_with_zero_history():
+    # 5 steps of 8 mel frames through the cached stem equal one causal pass over
+    # all 40 frames with two zero frames of left padding for each conv
+    S, n_mel, C = 2, 6, 10
+    w1, b1 = rnd((C, 3, n_mel), 125) * 0.3, rnd(C, 126) * 0.1
+    w2, b2 = rnd((C, 3, C), 127) * 0.3, rnd(C, 128) * 0.1
+    mel = rnd((S, 40, n_mel), 129)
+    mc, cc = np.zeros((S, 2, n_mel)), np.zeros((S, 2, C))
+    got = np.concatenate([oracle.enc_stem_step(mel[:, 8 * i:8 * i + 8], mc, cc, w1, b1, w2, b2)
+                          for i in range(5)], axis=1)
+    c1 = oracle.gelu(oracle.causal_conv1d(np.concatenate([np.zeros((S, 2, n_mel)), mel], 1), w1, b1, 1))
+    want = oracle.gelu(oracle.causal_conv1d(np.concatenate([np.zeros((S, 2, C)), c1], 1), w2, b2, 2))
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(mc, mel[:, -2:])
+
+
+def _layer_weights(dm, H, ffn, seed):
+    r = lambda shape, s, sc: rnd(shape, seed + s) * sc
+    return dict(g_attn=1 + r(dm, 0, 0.1), w_qkv=r((3 * H * 64, dm), 1, dm ** -0.5),
+                b_q=r(H * 64, 2, 0.1), b_v=r(H * 64, 3, 0.1), w_o=r((dm, H * 64), 4, (H * 64) ** -0.5),
+                b_o=r(dm, 5, 0.1), g_ffn=1 + r(dm, 6, 0.1), w_gate=r((ffn, dm), 7, dm ** -0.5),
+                w_up=r((ffn, dm), 8, dm ** -0.5), w_down=r((dm, ffn), 9, ffn ** -0.5),
+                b_down=r(dm, 10, 0.1))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_layer_streamed_equals_offline_layer(bf16):
+    # the layer streamed 4 frames at a time over W-slot rings equals the same
+    # layer over the whole sequence with one prefill for its attention
+    T, H, W, dm, ffn, n = 24, 2, 10, 32, 48, 4
+    wts = _layer_weights(dm, H, ffn, 130)
+    x = rnd((1, T, dm), 131)
+    rk, rv = np.full((1, H, W, 64), 1e3), np.full((1, H, W, 64), -1e3)
+    pos = np.zeros(1, dtype=np.int64)
+    got = np.concatenate([oracle.enc_layer_step(x[:, t:t + n], wts, rk, rv, pos, W, H, bf16=bf16)
+                          for t in range(0, T, n)], axis=1)
+    rd = oracle.bf16_round if bf16 else (lambda a: a)
+    h = rd(oracle.rmsnorm(x[0], wts["g_attn"]))
+    q, k, v = oracle.enc_qkv_rope(h, wts["w_qkv"], wts["b_q"], wts["b_v"], np.arange(T), H, bf16=bf16)
+    o = rd(oracle.prefill(q[None], k[None], v[None], W, rope_applied=True)[0])
+    x1 = x[0] + oracle.linear(o.reshape(T, H * 64), wts["w_o"], wts["b_o"])
+    h = rd(oracle.rmsnorm(x1, wts["g_ffn"]))
+    u = rd(oracle.silu(oracle.linear(h, wts["w_gate"])) * oracle.linear(h, wts["w_up"]))
+    want = x1 + oracle.linear(u, wts["w_down"], wts["b_down"])
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-11)
