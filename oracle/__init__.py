@@ -382,7 +382,9 @@ def enc_stem_step(mel_new, mel_cache, c1_cache, w1, b1, w2, b2, bf16=False):
 
     mel_new [S, 8, 128]; mel_cache [S, 2, 128] and c1_cache [S, 2, 1280] are
     each conv's last two input frames (updated in place).  Returns the 4 new
-    encoder frames [S, 4, 1280].  bf16=True rounds the stored conv outputs.
+    encoder frames [S, 4, 1280].  bf16=True rounds the stored first-conv
+    output; the second conv's output starts the residual stream, which is
+    held in float32 and so compared unrounded.
     """
     xp = np.concatenate([_f64(mel_cache), _f64(mel_new)], axis=1)
     c1 = gelu(causal_conv1d(xp, w1, b1, 1))
@@ -390,8 +392,6 @@ def enc_stem_step(mel_new, mel_cache, c1_cache, w1, b1, w2, b2, bf16=False):
         c1 = bf16_round(c1)
     c1p = np.concatenate([_f64(c1_cache), c1], axis=1)
     out = gelu(causal_conv1d(c1p, w2, b2, 2))
-    if bf16:
-        out = bf16_round(out)
     mel_cache[:] = xp[:, -2:]
     c1_cache[:] = c1p[:, -2:]
     return out

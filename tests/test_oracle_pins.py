@@ -653,7 +653,8 @@ def test_causal_conv1d_brute_force_and_causality(stride):
     np.testing.assert_array_equal(oracle.causal_conv1d(xq, w, b, stride)[:, :3], y[:, :3])
 
 
-def test_stem_streamed_equals_offline_with_zero_history():
+@pytest.mark.parametrize("bf16", [False, True])
+def test_stem_streamed_equals_offline_with_zero_history(bf16):
     # 5 steps of 8 mel frames through the cached stem equal one causal pass over
     # all 40 frames with two zero frames of left padding for each conv
     S, n_mel, C = 2, 6, 10
@@ -661,9 +662,11 @@ def test_stem_streamed_equals_offline_with_zero_history():
     w2, b2 = rnd((C, 3, C), 127) * 0.3, rnd(C, 128) * 0.1
     mel = rnd((S, 40, n_mel), 129)
     mc, cc = np.zeros((S, 2, n_mel)), np.zeros((S, 2, C))
-    got = np.concatenate([oracle.enc_stem_step(mel[:, 8 * i:8 * i + 8], mc, cc, w1, b1, w2, b2)
-                          for i in range(5)], axis=1)
+    got = np.concatenate([oracle.enc_stem_step(mel[:, 8 * i:8 * i + 8], mc, cc, w1, b1, w2, b2,
+                                               bf16=bf16) for i in range(5)], axis=1)
     c1 = oracle.gelu(oracle.causal_conv1d(np.concatenate([np.zeros((S, 2, n_mel)), mel], 1), w1, b1, 1))
+    if bf16:
+        c1 = oracle.bf16_round(c1)
     want = oracle.gelu(oracle.causal_conv1d(np.concatenate([np.zeros((S, 2, C)), c1], 1), w2, b2, 2))
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
     np.testing.assert_array_equal(mc, mel[:, -2:])
