@@ -17,11 +17,12 @@ back-to-back launches on the launch stream.  The streaming step is reported
 in microseconds and GB/s of algorithmic HBM bytes.  The CPU baseline is the
 float64 oracle timed on the host on the same prefill workload.
 
-Beside the step, the same line reports the batched first-chunk prefill and
-the text decoder's grouped-query attention (32 query / 8 key-value heads,
+Beside the step, the same line reports the batched first-chunk prefill, the
+text decoder's grouped-query attention (32 query / 8 key-value heads,
 head_dim 128, window 8192): one decode step of 64 streams over full 8192-slot
 rings (ring append fused) and a 16384-token prompt prefill, each with its
-roofline.
+roofline; the encoder's attention block (projections + attention); and the
+whole streaming encoder step (conv stem + 32 layers, 64 streams x 4 frames).
 """
 from __future__ import annotations
 
@@ -122,11 +123,14 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=60,
                     help="oracle repetitions of the prefill workload for the CPU baseline")
     ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "gqa_prefill",
-                                       "gqa_decode", "qkv", "oproj", "enc_block", "copy"],
+                                       "gqa_decode", "qkv", "oproj", "enc_block", "enc_step",
+                                       "copy"],
                     default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
                          "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--enc-layers", type=int, default=None,
+                    help="layers of the whole encoder step (default: the model's 32)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -270,6 +274,42 @@ def main():
     def oproj(i):
         vx.linear(ework["o"].view(eM, eHD), ew["w_o"], ew["b_o"], out=ey.view(eM, edm))
 
+    # ---- whole streaming encoder step: conv stem + 32 pre-norm layers, 64 streams x 4 frames;
+    # every layer's rings start as the encoder-block leg's full-ring draw
+    cs = synth.ENC_STEP
+    sL = args.enc_layers or cs["L"]
+    sS, sn, sH, sdm, sffn, snm = cs["S"], cs["n"], cs["H"], cs["d_model"], cs["ffn"], cs["n_mels"]
+    s_stem = {k_: to(v_) for k_, v_ in synth.make_enc_stem_weights(sdm, snm,
+                                                                    seed=cs["seed"]).items()}
+    s_layers = [{k_: to(v_) for k_, v_ in synth.make_enc_layer_weights(
+        sdm, sH, sffn, seed=cs["seed"], layer=l).items()} for l in range(sL)]
+    s_rk = ering["k"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
+    s_rv = ering["v"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
+    s_pos = [ering["pos"][0].clone(), ering["pos"][0].clone()]
+    s_mel = [to(synth.make_mel(sS, 2 * sn, snm, seed=cs["seed"], step=i)) for i in range(8)]
+    s_melbuf = torch.zeros((sS, 2 * sn + 2, snm), dtype=torch.bfloat16, device=dev)
+    s_c1buf = torch.zeros((sS, 2 * sn + 2, sdm), dtype=torch.bfloat16, device=dev)
+    s_x = torch.empty((sS, sn, sdm), dtype=torch.float32, device=dev)
+    s_work = vx.enc_work(sS, sn, sH, sdm, sffn, device=dev)
+    s_state = {"c": 0}
+    sM, sHD, sF = sS * sn, sH * 64, 2 * sn + 2
+    s_stem_bytes = (sdm * 3 * snm * 2 + sS * sF * snm * 2 + sS * 2 * sn * sdm * 2  # conv1
+                    + sdm * 3 * sdm * 2 + sS * sF * sdm * 2 + sM * sdm * 4          # conv2
+                    + 2 * sS * 2 * (snm + sdm) * 2 + 2 * 2 * sdm)                   # shift, biases
+    s_layer_bytes = (2 * (sM * sdm * 4 + sM * sdm * 2 + sdm * 2)                    # two RMSNorms
+                     + qkv_bytes + stream_bytes(sS, sn, sH, cs["W"])                # attention
+                     + sdm * sHD * 2 + sM * sHD * 2 + 2 * sM * sdm * 4 + sdm * 2   # out proj
+                     + 2 * sffn * sdm * 2 + sM * sdm * 2 + sM * sffn * 2           # gate/up
+                     + sdm * sffn * 2 + sM * sffn * 2 + 2 * sM * sdm * 4 + sdm * 2)  # down
+    s_bytes = s_stem_bytes + sL * s_layer_bytes
+
+    def enc_step(i):
+        c = s_state["c"]
+        s_melbuf[:, 2:].copy_(s_mel[i % 8])
+        vx.enc_step(s_melbuf, s_c1buf, s_stem, s_layers, s_rk, s_rv, s_pos[c % 2],
+                    s_pos[(c + 1) % 2], x=s_x, window=cs["W"], H=sH, work=s_work)
+        s_state["c"] = c + 1
+
     def prefill():
         vx.prefill(q, k, v, window=pc.W, table=table, out=o)
 
@@ -302,7 +342,7 @@ def main():
                                                          window=fc["W"], table=ftab, ring_k=frk,
                                                          ring_v=frv, pos=fpos, out=fo),
               "gqa_prefill": gqa_prefill, "gqa_decode": gqa_decode, "qkv": qkv, "oproj": oproj,
-              "enc_block": enc_block}[args.only]
+              "enc_block": enc_block, "enc_step": enc_step}[args.only]
         for j in range(args.warmup):
             fn(j)
         torch.cuda.synchronize()
@@ -368,6 +408,7 @@ def main():
     blk_us = per_launch_us(enc_block, reps)
     qkv_us = per_launch_us(qkv, reps)
     oproj_us = per_launch_us(oproj, reps)
+    encs_us = per_launch_us(enc_step, max(K // 5, 5))
     dec_us = per_launch_us(gqa_decode, reps)
     gpre_us = per_launch_us(gqa_prefill, max(K // 5, 5))
     gpre_fused_us = per_launch_us(gqa_prefill_fused, max(K // 5, 5))
@@ -478,6 +519,21 @@ def main():
                               "frac": round(oproj_bytes / (oproj_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                                             4),
                               "traffic": measured_traffic("oproj")},
+    }
+
+    encs_gbs = s_bytes / (encs_us * 1e-6) / 1e9
+    out["enc_step"] = {
+        "workload": f"whole streaming encoder step S{sS} x {2 * sn} mel frames -> {sn} frames: "
+                    f"causal conv stem ({snm}->{sdm} k3 s1, {sdm}->{sdm} k3 s2, GELU) + {sL} "
+                    f"pre-norm layers (d_model {sdm}, H{sH} D64 W{cs['W']}, SwiGLU FFN {sffn}), "
+                    f"bf16 weights/activations, float32 residual, {3 + 7 * sL} launches",
+        "us_per_step": round(encs_us, 3),
+        "encoder_frames_per_s": round(sM / (encs_us * 1e-6), 1),
+        "audio_s_per_s": round(sS * 0.08 / (encs_us * 1e-6), 1),
+        "bytes_algorithmic": int(s_bytes),
+        "roofline": {"kernel": "whole step (all launches)", "bound": "hbm",
+                     "achieved": round(encs_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(encs_gbs / PEAK_HBM_GBS, 4), "traffic": None},
     }
 
     if not args.no_cpu_baseline:

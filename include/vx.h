@@ -280,6 +280,104 @@ vx_status vx_enc_attn_step(const void *x, const void *w_qkv, const void *b_q, co
                            void *o, void *y, int32_t S, int32_t n, int32_t H, int32_t d_model,
                            const vx_attn_cfg *cfg, void *stream);
 
+/* ---- The streaming encoder step ---------------------------------------------
+ * One step of the Voxtral Realtime 2602 audio encoder turns 2n new log-mel
+ * frames (n_mels = 128 bins) of each of S streams into n encoder frames of
+ * width d_model (transcribe.cpp "Voxtral" family notes, Architecture and
+ * Streaming schedule: 8 mel frames -> 4 encoder frames per 80 ms token):
+ *   - a stem of two causal convolutions with kernel 3, each followed by GELU
+ *     (exact erf form): n_mels -> d_model at stride 1, then d_model ->
+ *     d_model at stride 2.  Causal means left padding of k-1 = 2 frames,
+ *     which in a stream are the previous step's last two input frames of
+ *     each convolution (zeros at the start of a stream);
+ *   - L pre-norm layers, each  x += attn(rmsnorm(x) * g_attn)  and then
+ *     x += W_down (silu(h W_gate^T) * (h W_up^T)) + b_down  with
+ *     h = rmsnorm(x) * g_ffn; the attention is vx_enc_attn_step's block
+ *     (q/k/v + RoPE, the windowed attention over each layer's ring with the
+ *     append, the output projection).
+ * RMSNorm: x / sqrt(mean(x^2) + eps), eps = 1e-5 in this model.  The
+ * residual stream x is float32 ([S, n, d_model]); every other tensor stored
+ * between launches (normalised states, q', k', v, attention output, SwiGLU
+ * hidden state, conv1 output) is bf16, accumulation fp32 on matrix cores.
+ * Weights are bf16; convolution weights are [out, tap, in] (tap 2 multiplies
+ * the newest frame).  ffn (5120 in this model), d_model (1280), n_mels and
+ * H*64 must be multiples of 128. */
+
+typedef struct {
+  const void *w1; /* [d_model, 3, n_mels] */
+  const void *b1; /* [d_model] or NULL */
+  const void *w2; /* [d_model, 3, d_model] */
+  const void *b2; /* [d_model] or NULL */
+} vx_enc_stem_weights;
+
+typedef struct {
+  const void *g_attn; /* [d_model] RMSNorm gain in front of the attention */
+  const void *w_qkv;  /* [3*H*64, d_model]: the q rows, then k, then v */
+  const void *b_q;    /* [H*64] or NULL (k has no bias) */
+  const void *b_v;    /* [H*64] or NULL */
+  const void *w_o;    /* [d_model, H*64] */
+  const void *b_o;    /* [d_model] or NULL */
+  const void *g_ffn;  /* [d_model] RMSNorm gain in front of the feed-forward */
+  const void *w_gate; /* [ffn, d_model] */
+  const void *w_up;   /* [ffn, d_model] */
+  const void *w_down; /* [d_model, ffn] */
+  const void *b_down; /* [d_model] or NULL */
+} vx_enc_layer_weights;
+
+/* Caller-owned bf16 work buffers of a layer step (reused by every layer). */
+typedef struct {
+  void *h; /* [S*n, d_model] normalised state */
+  void *q; /* [S*n, H*64] rotated queries */
+  void *k; /* [S*n, H*64] rotated keys */
+  void *v; /* [S*n, H*64] values */
+  void *o; /* [S*n, H*64] attention output */
+  void *u; /* [S*n, ffn] SwiGLU hidden state */
+} vx_enc_work;
+
+/* y = x / sqrt(mean(x^2) + eps) * g per row: x float32 [M, dim], g bf16
+ * [dim], y bf16 [M, dim] (fp32 arithmetic, y rounded once).  dim must be a
+ * multiple of 8, eps finite and >= 0; y must not overlap x or g. */
+vx_status vx_rmsnorm(const float *x, const void *g, void *y, int32_t M, int32_t dim, float eps,
+                     void *stream);
+
+/* The stem for one step, three launches on `stream`.
+ * mel_buf [S, 2n+2, n_mels] bf16: slots 0-1 hold the stream's two previous
+ * mel frames (zeros at its start), slots 2 .. 2n+1 this step's 2n frames,
+ * written by the caller.  c1_buf [S, 2n+2, d_model] bf16: slots 0-1 hold
+ * the first convolution's two previous output frames (zeros at the start);
+ * the call writes this step's outputs to slots 2 .. 2n+1.  x_out [S, n,
+ * d_model] float32 receives the n new frames.  On return slots 0-1 of both
+ * buffers hold slots 2n and 2n+1 (the state for the next step).  Buffers
+ * the call writes must not overlap any other argument; each buffer and w2
+ * must be smaller than 2^30 bytes. */
+vx_status vx_enc_stem_step(void *mel_buf, void *c1_buf, const vx_enc_stem_weights *w,
+                           float *x_out, int32_t S, int32_t n, int32_t n_mels, int32_t d_model,
+                           void *stream);
+
+/* One pre-norm layer for one step, seven launches on `stream`, updating the
+ * residual x [S, n, d_model] float32 in place.  ring_k, ring_v [S, H, W, 64]
+ * bf16 rotated keys and values of this layer; frame i of stream s is at
+ * position pos_in[s] + i; the call appends the new keys and values and sets
+ * pos_out[s] = pos_in[s] + n (distinct arrays).  Requires 1 <= n <=
+ * min(W, 16), cfg->io_dtype bf16, cfg->head_dim 64, no flags; cfg->window,
+ * rope_theta and softmax_scale apply.  No written buffer (x, rings, work,
+ * pos_out) may overlap another argument. */
+vx_status vx_enc_layer_step(float *x, const vx_enc_layer_weights *w, void *ring_k, void *ring_v,
+                            const int64_t *pos_in, int64_t *pos_out, const vx_enc_work *work,
+                            int32_t S, int32_t n, int32_t H, int32_t d_model, int32_t ffn,
+                            float eps, const vx_attn_cfg *cfg, void *stream);
+
+/* A whole encoder step: vx_enc_stem_step into x, then layers[0 .. L-1] in
+ * order as vx_enc_layer_step, layer l on rings ring_k + l*S*H*W*64 (ring_k,
+ * ring_v [L, S, H, W, 64] bf16); all layers read positions pos_in and write
+ * pos_out.  3 + 7L launches on `stream`; 1 <= L <= 4096.  Same buffer
+ * rules as the two calls above. */
+vx_status vx_enc_step(void *mel_buf, void *c1_buf, const vx_enc_stem_weights *stem,
+                      const vx_enc_layer_weights *layers, int32_t L, void *ring_k, void *ring_v,
+                      const int64_t *pos_in, int64_t *pos_out, float *x, const vx_enc_work *work,
+                      int32_t S, int32_t n, int32_t n_mels, int32_t H, int32_t d_model,
+                      int32_t ffn, float eps, const vx_attn_cfg *cfg, void *stream);
+
 /* Static description of a status code. */
 const char *vx_status_string(vx_status s);
 

@@ -16,7 +16,8 @@ import os
 __all__ = [
     "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
     "stream_step_append", "gqa_prefill", "gqa_decode", "linear", "enc_qkv_rope",
-    "enc_attn_step",
+    "enc_attn_step", "rmsnorm", "enc_work", "enc_stem_step", "enc_layer_step", "enc_step",
+    "LAYER_KEYS", "STEM_KEYS",
     "WINDOW", "THETA", "HEAD_DIM", "DEC_WINDOW", "DEC_HEAD_DIM",
 ]
 
@@ -52,6 +53,25 @@ class _Cfg(ctypes.Structure):
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
+
+# encoder-step weight and work structs (field order of include/vx.h)
+STEM_KEYS = ("w1", "b1", "w2", "b2")
+LAYER_KEYS = ("g_attn", "w_qkv", "b_q", "b_v", "w_o", "b_o", "g_ffn", "w_gate", "w_up", "w_down",
+              "b_down")
+WORK_KEYS = ("h", "q", "k", "v", "o", "u")
+
+
+class _StemW(ctypes.Structure):
+    _fields_ = [(k, _vp) for k in STEM_KEYS]
+
+
+class _LayerW(ctypes.Structure):
+    _fields_ = [(k, _vp) for k in LAYER_KEYS]
+
+
+class _Work(ctypes.Structure):
+    _fields_ = [(k, _vp) for k in WORK_KEYS]
+
 _SIGS = {
     "vx_default_cfg": (None, [ctypes.POINTER(_Cfg)]),
     "vx_rope_table": (ctypes.c_int, [_vp, _i64, _i32, ctypes.POINTER(_Cfg), _vp]),
@@ -80,6 +100,15 @@ _SIGS = {
     "vx_enc_attn_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         ctypes.POINTER(_Cfg), _vp]),
+    "vx_rmsnorm": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp]),
+    "vx_enc_stem_step": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(_StemW), _vp, _i32, _i32, _i32,
+                                        _i32, _vp]),
+    "vx_enc_layer_step": (ctypes.c_int, [_vp, ctypes.POINTER(_LayerW), _vp, _vp, _vp, _vp,
+                                         ctypes.POINTER(_Work), _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.c_float, ctypes.POINTER(_Cfg), _vp]),
+    "vx_enc_step": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(_StemW), ctypes.POINTER(_LayerW), _i32,
+                                   _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_Work), _i32, _i32, _i32,
+                                   _i32, _i32, _i32, ctypes.c_float, ctypes.POINTER(_Cfg), _vp]),
     "vx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vx_last_error": (ctypes.c_char_p, []),
     "vx_version": (_i32, []),
@@ -576,3 +605,162 @@ def enc_attn_step(x, w_qkv, b_q, b_v, w_o, b_o, ring_k, ring_v, pos_in, pos_out,
         _ptr(work["v"]), _ptr(work["o"]), _ptr(out), S, n, H, dm, ctypes.byref(cfg),
         _stream(x)), "vx_enc_attn_step")
     return out
+
+
+# ---------------------------------------------------------------------------
+# the streaming encoder step: stem, pre-norm layers (residual stream float32)
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x, g, eps=1e-5, out=None):
+    """y = x / sqrt(mean(x^2) + eps) * g per row: x float32 [..., dim], g bf16 [dim] -> bf16."""
+    import torch
+    _dev_tensor(x, "x")
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    _bf16_dev(g, "g")
+    dim = x.shape[-1]
+    if g.shape != (dim,):
+        raise ValueError("g must be [dim]")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _bf16_dev(out, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    M = x.numel() // dim if dim else 0
+    _check(lib().vx_rmsnorm(_ptr(x), _ptr(g), _ptr(out), M, dim, float(eps), _stream(x)),
+           "vx_rmsnorm")
+    return out
+
+
+def enc_work(S, n, H, d_model, ffn, device="cuda"):
+    """Work buffers of a layer step (dict of bf16 tensors h, q, k, v, o, u)."""
+    import torch
+    M = S * n
+    shapes = dict(h=(M, d_model), q=(M, H * HEAD_DIM), k=(M, H * HEAD_DIM), v=(M, H * HEAD_DIM),
+                  o=(M, H * HEAD_DIM), u=(M, ffn))
+    return {k: torch.empty(v, dtype=torch.bfloat16, device=device) for k, v in shapes.items()}
+
+
+def _stem_struct(stem):
+    for k in ("w1", "w2"):
+        _bf16_dev(stem[k], k)
+    for k in ("b1", "b2"):
+        if stem.get(k) is not None:
+            _bf16_dev(stem[k], k)
+    return _StemW(*[_ptr(stem.get(k)) for k in STEM_KEYS])
+
+
+def _layer_struct(w, H, dm, ffn):
+    shapes = dict(g_attn=(dm,), w_qkv=(3 * H * HEAD_DIM, dm), b_q=(H * HEAD_DIM,),
+                  b_v=(H * HEAD_DIM,), w_o=(dm, H * HEAD_DIM), b_o=(dm,), g_ffn=(dm,),
+                  w_gate=(ffn, dm), w_up=(ffn, dm), w_down=(dm, ffn), b_down=(dm,))
+    for k in LAYER_KEYS:
+        t = w.get(k)
+        if t is None:
+            if not k.startswith("b_"):
+                raise ValueError(f"layer weight {k} is required")
+            continue
+        _bf16_dev(t, k)
+        if tuple(t.shape) != shapes[k]:
+            raise ValueError(f"layer weight {k} must be {shapes[k]}, got {tuple(t.shape)}")
+    return _LayerW(*[_ptr(w.get(k)) for k in LAYER_KEYS])
+
+
+def _work_struct(work, S, n, H, dm, ffn, device):
+    work = dict(work) if work is not None else enc_work(S, n, H, dm, ffn, device)
+    for k in WORK_KEYS:
+        _bf16_dev(work[k], k)
+    return work, _Work(*[_ptr(work[k]) for k in WORK_KEYS])
+
+
+def _stem_shapes(mel_buf, c1_buf):
+    _bf16_dev(mel_buf, "mel_buf")
+    _bf16_dev(c1_buf, "c1_buf")
+    if mel_buf.dim() != 3 or c1_buf.dim() != 3 or mel_buf.shape[:2] != c1_buf.shape[:2]:
+        raise ValueError("mel_buf must be [S, 2n+2, n_mels] and c1_buf [S, 2n+2, d_model]")
+    S, F, n_mels = mel_buf.shape
+    if F < 4 or F % 2:
+        raise ValueError("the buffers hold 2n+2 frame slots (n >= 1)")
+    return S, (F - 2) // 2, n_mels, c1_buf.shape[2]
+
+
+def enc_stem_step(mel_buf, c1_buf, stem, x_out=None):
+    """The stem for one step: both causal convolutions (+ GELU) over the frame
+    buffers, then the move of each buffer's last two slots to slots 0-1.
+
+    mel_buf [S, 2n+2, n_mels] bf16 (slots 2.. hold the step's 2n mel frames),
+    c1_buf [S, 2n+2, d_model] bf16, stem: dict w1 [d_model, 3, n_mels], b1,
+    w2 [d_model, 3, d_model], b2.  Returns x_out [S, n, d_model] float32.
+    """
+    import torch
+    S, n, n_mels, dm = _stem_shapes(mel_buf, c1_buf)
+    if x_out is None:
+        x_out = torch.empty((S, n, dm), dtype=torch.float32, device=mel_buf.device)
+    _dev_tensor(x_out, "x_out")
+    if x_out.dtype != torch.float32 or x_out.shape != (S, n, dm):
+        raise ValueError("x_out must be float32 [S, n, d_model]")
+    sw = _stem_struct(stem)
+    _check(lib().vx_enc_stem_step(_ptr(mel_buf), _ptr(c1_buf), ctypes.byref(sw), _ptr(x_out), S, n,
+                                  n_mels, dm, _stream(mel_buf)), "vx_enc_stem_step")
+    return x_out
+
+
+def _layer_common(x, ring_k, ring_v, pos_in, pos_out, window, H, L=None):
+    import torch
+    _dev_tensor(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 3:
+        raise ValueError("x must be float32 [S, n, d_model]")
+    S, n, dm = x.shape
+    want = (S, H, window, HEAD_DIM) if L is None else (L, S, H, window, HEAD_DIM)
+    for name, t in (("ring_k", ring_k), ("ring_v", ring_v)):
+        _bf16_dev(t, name)
+        if t.shape != want:
+            raise ValueError(f"{name} must be {want}")
+    for name, t in (("pos_in", pos_in), ("pos_out", pos_out)):
+        _dev_tensor(t, name)
+        if t.dtype != torch.int64 or t.shape != (S,):
+            raise ValueError("pos_in and pos_out must be int64 [S]")
+    return S, n, dm
+
+
+def enc_layer_step(x, wts, ring_k, ring_v, pos_in, pos_out, window=WINDOW, theta=THETA, scale=0.0,
+                   H=32, eps=1e-5, work=None):
+    """One pre-norm layer (seven launches), updating the float32 residual x
+    [S, n, d_model] in place: x += attn(rmsnorm(x) g_attn), then
+    x += W_down(silu(h W_gate^T) (h W_up^T)) + b_down, h = rmsnorm(x) g_ffn.
+    wts: dict of bf16 tensors (LAYER_KEYS; biases optional); rings
+    [S, H, W, 64] bf16; pos_in/pos_out int64 [S] (distinct)."""
+    S, n, dm = _layer_common(x, ring_k, ring_v, pos_in, pos_out, window, H)
+    ffn = wts["w_gate"].shape[0]
+    lw = _layer_struct(wts, H, dm, ffn)
+    work, ws = _work_struct(work, S, n, H, dm, ffn, x.device)
+    cfg = Config(window, theta, scale, "bf16", "bf16").c()
+    _check(lib().vx_enc_layer_step(_ptr(x), ctypes.byref(lw), _ptr(ring_k), _ptr(ring_v),
+                                   _ptr(pos_in), _ptr(pos_out), ctypes.byref(ws), S, n, H, dm, ffn,
+                                   float(eps), ctypes.byref(cfg), _stream(x)), "vx_enc_layer_step")
+    return x
+
+
+def enc_step(mel_buf, c1_buf, stem, layers, ring_k, ring_v, pos_in, pos_out, x=None,
+             window=WINDOW, theta=THETA, scale=0.0, H=32, eps=1e-5, work=None):
+    """A whole encoder step: the stem into x [S, n, d_model] float32, then
+    the L = len(layers) layers in order (ring_k, ring_v [L, S, H, W, 64] bf16;
+    every layer reads pos_in and writes pos_out).  Returns x."""
+    import torch
+    S, n, n_mels, dm = _stem_shapes(mel_buf, c1_buf)
+    if x is None:
+        x = torch.empty((S, n, dm), dtype=torch.float32, device=mel_buf.device)
+    L = len(layers)
+    if L < 1:
+        raise ValueError("need at least one layer")
+    _layer_common(x, ring_k, ring_v, pos_in, pos_out, window, H, L)
+    ffn = layers[0]["w_gate"].shape[0]
+    arr = (_LayerW * L)(*[_layer_struct(w, H, dm, ffn) for w in layers])
+    sw = _stem_struct(stem)
+    work, ws = _work_struct(work, S, n, H, dm, ffn, x.device)
+    cfg = Config(window, theta, scale, "bf16", "bf16").c()
+    _check(lib().vx_enc_step(_ptr(mel_buf), _ptr(c1_buf), ctypes.byref(sw), arr, L, _ptr(ring_k),
+                             _ptr(ring_v), _ptr(pos_in), _ptr(pos_out), _ptr(x), ctypes.byref(ws),
+                             S, n, n_mels, H, dm, ffn, float(eps), ctypes.byref(cfg),
+                             _stream(mel_buf)), "vx_enc_step")
+    return x

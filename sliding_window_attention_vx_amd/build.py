@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvx.so")
 SOURCES = ["vx_api.hip", "rope.hip", "prefill_valu.hip", "prefill_mfma.hip", "stream.hip",
-           "gqa_prefill.hip", "gqa_decode.hip", "linear.hip"]
+           "gqa_prefill.hip", "gqa_decode.hip", "linear.hip", "enc_step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

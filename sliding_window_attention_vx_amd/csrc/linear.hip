@@ -37,7 +37,7 @@ struct Tile {
   static_assert(MT * TP * 4 <= 2 * STAGE, "epilogue tile must fit in the staging LDS");
 };
 
-enum class Epi { Plain, QkvRope };
+enum class Epi { Plain, Gelu, Residual, SwiGLU, QkvRope };
 
 template <int MT, int NC, Epi E, typename TO>
 __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(LinearArgs a, RopeFreqs fr) {
@@ -63,22 +63,31 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
   // no address registers are rebuilt per stage (rebuilt 64-bit addresses land
   // in registers of loads still in flight and force waits for them).  Each
   // resource covers the tile's rows exactly.
+  // x rows follow the row map (the host keeps x below 2^30 bytes); w rows of
+  // the tile are rows n0 .. n0+NC-1, or for SwiGLU gate rows n0/2 .. in the
+  // first half of the tile and up rows n0/2 .. in the second.  A stage-load
+  // slot j covers NTH/16 whole rows, so the halves fall on whole slots.
   uint32_t xo[TL::PX], wo[TL::PW];
 #pragma unroll
   for (int j = 0; j < TL::PX; ++j) {
     const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-    xo[j] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2u;
+    const int mm = min(m0 + r, M - 1);
+    xo[j] = (uint32_t)(((int64_t)(mm / a.rpg) * a.xgs + (int64_t)(mm % a.rpg) * a.xrs + 8 * c) * 2);
   }
+  constexpr bool GLU = (E == Epi::SwiGLU);
 #pragma unroll
   for (int j = 0; j < TL::PW; ++j) {
     const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-    wo[j] = (uint32_t)(r * K + 8 * c) * 2u;
+    const int rr = (GLU && j >= TL::PW / 2) ? r - NC / 2 : r;
+    wo[j] = (uint32_t)(rr * K + 8 * c) * 2u;
   }
-  const int xrows = min(MT, M - m0);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(x + (size_t)m0 * K), (short)0, xrows * K * 2, 0x00020000);
+      const_cast<bf16*>(x), (short)0, (int)a.x_bytes, 0x00020000);
+  const int wrow0 = GLU ? n0 / 2 : n0, wrows = GLU ? NC / 2 : NC;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(w + (size_t)n0 * K), (short)0, NC * K * 2, 0x00020000);
+      const_cast<bf16*>(w + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>((GLU ? a.w2 : w) + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
   auto load = [&](int s, Stage& R) {
     const int ko = s * kKS * 2;  // uniform byte offset of the stage
 #pragma unroll
@@ -86,7 +95,8 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
       R.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo[j], ko, 0));
 #pragma unroll
     for (int j = 0; j < TL::PW; ++j)
-      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo[j], ko, 0));
+      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             (GLU && j >= TL::PW / 2) ? wr2 : wr, (int)wo[j], ko, 0));
   };
   auto commit = [&](const Stage& R, int b) {
     char* base = lds + b * TL::STAGE;
@@ -146,7 +156,7 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
   }
   __syncthreads();
 
-  if constexpr (E == Epi::Plain) {
+  if constexpr (E == Epi::Plain || E == Epi::Gelu || E == Epi::Residual) {
     constexpr int C8 = NC / 8;
     for (int u = tid; u < MT * C8; u += TL::NTH) {
       const int r = u / C8, c8 = u % C8, m = m0 + r;
@@ -159,7 +169,32 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
 #pragma unroll
         for (int e = 0; e < 8; ++e) v8[e] += b8[e];
       }
-      store8((TO*)a.y + (size_t)m * a.N + n0 + 8 * c8, v8);
+      const size_t yo = (size_t)((int64_t)(m / a.rpg) * a.ygs + (int64_t)(m % a.rpg) * a.yrs) + n0 + 8 * c8;
+      if constexpr (E == Epi::Gelu) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = 0.5f * v8[e] * (1.0f + erff(v8[e] * 0.70710678118654752f));
+      }
+      if constexpr (E == Epi::Residual) {
+        float r8[8];
+        load8(a.res + yo, r8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] += r8[e];
+      }
+      store8((TO*)a.y + yo, v8);
+    }
+  } else if constexpr (E == Epi::SwiGLU) {
+    // tile columns 0 .. NC/2-1 are gate features n0/2 .., NC/2 .. NC-1 the same up features
+    constexpr int C8 = NC / 16;
+    const int F = a.N / 2;
+    for (int u = tid; u < MT * C8; u += TL::NTH) {
+      const int r = u / C8, c8 = u % C8, m = m0 + r;
+      if (m >= M) continue;
+      float g8[8], u8[8];
+      load8(tile + r * TL::TP + 8 * c8, g8);
+      load8(tile + r * TL::TP + NC / 2 + 8 * c8, u8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g8[e] = g8[e] / (1.0f + __expf(-g8[e])) * u8[e];
+      store8((bf16*)a.y + (size_t)m * F + n0 / 2 + 8 * c8, g8);
     }
   } else {
     static_assert(NC == 64, "the q/k/v epilogue works on one head (64 columns) per tile");
@@ -210,15 +245,27 @@ hipError_t launch_tile(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_linear(const LinearArgs& a, DT out, hipStream_t st) {
+template <Epi E, typename TO>
+hipError_t launch_epi(const LinearArgs& a, hipStream_t st) {
   const RopeFreqs fr{};
   // 64 x 64 tiles when they alone give every CU a workgroup, else 64 x 32
   const bool wide = a.N % 64 == 0 && (int64_t)(a.N / 64) * ((a.M + 63) / 64) >= 256;
-  if (out == DT::BF16)
-    return wide ? launch_tile<64, 64, Epi::Plain, bf16>(a, fr, st)
-                : launch_tile<64, 32, Epi::Plain, bf16>(a, fr, st);
-  return wide ? launch_tile<64, 64, Epi::Plain, float>(a, fr, st)
-              : launch_tile<64, 32, Epi::Plain, float>(a, fr, st);
+  return wide ? launch_tile<64, 64, E, TO>(a, fr, st) : launch_tile<64, 32, E, TO>(a, fr, st);
+}
+
+hipError_t launch_linear(const LinearArgs& a, DT out, hipStream_t st, LinEpi epi) {
+  const bool b16 = out == DT::BF16;
+  switch (epi) {
+    case LinEpi::Plain:
+      return b16 ? launch_epi<Epi::Plain, bf16>(a, st) : launch_epi<Epi::Plain, float>(a, st);
+    case LinEpi::Gelu:
+      return b16 ? launch_epi<Epi::Gelu, bf16>(a, st) : launch_epi<Epi::Gelu, float>(a, st);
+    case LinEpi::Residual:
+      return launch_epi<Epi::Residual, float>(a, st);
+    case LinEpi::SwiGLU:
+      return launch_epi<Epi::SwiGLU, bf16>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_qkv_rope(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st) {

@@ -12,12 +12,23 @@ namespace vx {
 constexpr int kLinKStep = 128;  // K must be a multiple of this
 
 struct LinearArgs {
-  const bf16* x;  // [M, K] row-major
+  const bf16* x;  // rows of K contiguous elements (see the row map below)
   const bf16* w;  // [N, K] row-major: y = x w^T
   int M, N, K;
-  // plain output: y [M, N], optional bias [N]
+  // Row map: row m of x starts at element (m / rpg) * xgs + (m % rpg) * xrs, and
+  // row m of y at (m / rpg) * ygs + (m % rpg) * yrs (rows may overlap: a causal
+  // convolution reads k consecutive frames as one row).  x_bytes bounds x.
+  int rpg = 1;
+  int64_t xgs = 0, xrs = 0, ygs = 0, yrs = 0;
+  int64_t x_bytes = 0;
+  // plain / GELU / residual output: y, optional bias [N]; residual: y (fp32)
+  // = res + x w^T + bias, res (fp32, same map as y) may equal y
   const bf16* bias = nullptr;
   void* y = nullptr;
+  const float* res = nullptr;
+  // SwiGLU: w holds the gate rows, w2 the up rows (both [F, K]); N = 2F and
+  // y [M, F] = silu(x w^T) * (x w2^T), bf16
+  const bf16* w2 = nullptr;
   // q/k/v output (N = 3*HD): columns [0, HD) are q (+ b_q, rotated), [HD, 2HD)
   // k (rotated, no bias), [2HD, 3HD) v (+ b_v); row m sits at position
   // pos[m / n] + m % n; q, k, v are [M, HD] bf16.
@@ -30,7 +41,19 @@ struct LinearArgs {
   bf16* v = nullptr;
 };
 
-hipError_t launch_linear(const LinearArgs& a, DT out, hipStream_t st);
+enum class LinEpi { Plain, Gelu, Residual, SwiGLU };
+
+// Fills the row map of a dense [M, K] -> [M, N] product.
+inline void dense_rows(LinearArgs& a) {
+  a.rpg = a.M > 0 ? a.M : 1;
+  a.xgs = 0;
+  a.xrs = a.K;
+  a.ygs = 0;
+  a.yrs = a.N;
+  a.x_bytes = (int64_t)a.M * a.K * 2;
+}
+
+hipError_t launch_linear(const LinearArgs& a, DT out, hipStream_t st, LinEpi epi = LinEpi::Plain);
 hipError_t launch_qkv_rope(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st);
 
 }  // namespace vx

@@ -8,7 +8,9 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
+#include "enc_launch.h"
 #include "gqa_launch.h"
 #include "linear_launch.h"
 #include "vx.h"
@@ -655,6 +657,7 @@ vx_status vx_linear(const void* x, const void* w, const void* bias, void* y, int
   a.K = K;
   a.bias = (const vx::bf16*)bias;
   a.y = y;
+  vx::dense_rows(a);
   (void)hipGetLastError();
   return launched(vx::launch_linear(a, to_dt(out_dtype), (hipStream_t)stream));
 }
@@ -713,6 +716,7 @@ vx_status vx_enc_qkv_rope(const void* x, const void* w_qkv, const void* b_q, con
   a.q = (vx::bf16*)q;
   a.k = (vx::bf16*)k;
   a.v = (vx::bf16*)v;
+  vx::dense_rows(a);
   (void)hipGetLastError();
   return launched(vx::launch_qkv_rope(a, rope_freqs(cfg->rope_theta), (hipStream_t)stream));
 }
@@ -774,6 +778,7 @@ vx_status vx_enc_attn_step(const void* x, const void* w_qkv, const void* b_q, co
   a.q = (vx::bf16*)q;
   a.k = (vx::bf16*)k;
   a.v = (vx::bf16*)v;
+  vx::dense_rows(a);
   if ((st = launched(vx::launch_qkv_rope(a, fr, hs)))) return st;
   // 2. attention over the ring and the new frames, then the append (q, k already rotated)
   vx::StreamArgs sa{};
@@ -804,7 +809,366 @@ vx_status vx_enc_attn_step(const void* x, const void* w_qkv, const void* b_q, co
   b.K = H * vx::kD;
   b.bias = (const vx::bf16*)b_o;
   b.y = y;
+  vx::dense_rows(b);
   return launched(vx::launch_linear(b, to_dt(cfg->out_dtype), hs));
+}
+
+// ---- the streaming encoder step ---------------------------------------------
+
+namespace {
+
+struct Region {
+  const void* p;
+  size_t bytes;
+  bool written;
+};
+
+// Every region the call writes must be disjoint from every other region it
+// touches (NULL regions, the optional biases left out, are skipped).
+bool regions_disjoint(const std::vector<Region>& r) {
+  for (size_t i = 0; i < r.size(); ++i) {
+    if (!r[i].written || !r[i].p) continue;
+    for (size_t j = 0; j < r.size(); ++j)
+      if (j != i && r[j].p && overlap(r[i].p, r[i].bytes, r[j].p, r[j].bytes)) return false;
+  }
+  return true;
+}
+
+vx_status check_eps(const char* what, float eps) {
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(VX_E_RANGE, "%s: eps must be finite and >= 0", what);
+  return VX_OK;
+}
+
+// Row maps of the two stem convolutions as products over frame windows.
+// conv1: output frame t of stream s (row s*2n + t) reads mel slots t .. t+2,
+// i.e. 3*n_mels contiguous elements from slot t; writes c1 slot t + 2.
+// conv2: output frame t (row s*n + t) reads c1 slots 2t .. 2t+2; writes x.
+void stem_args(vx::LinearArgs& c1, vx::LinearArgs& c2, void* mel_buf, void* c1_buf,
+               const vx_enc_stem_weights* w, float* x_out, int S, int n, int n_mels, int d_model) {
+  const int F = 2 * n + 2;
+  c1 = vx::LinearArgs{};
+  c1.x = (const vx::bf16*)mel_buf;
+  c1.w = (const vx::bf16*)w->w1;
+  c1.M = S * 2 * n;
+  c1.N = d_model;
+  c1.K = 3 * n_mels;
+  c1.rpg = 2 * n;
+  c1.xgs = (int64_t)F * n_mels;
+  c1.xrs = n_mels;
+  c1.ygs = (int64_t)F * d_model;
+  c1.yrs = d_model;
+  c1.x_bytes = (int64_t)S * F * n_mels * 2;
+  c1.bias = (const vx::bf16*)w->b1;
+  c1.y = (vx::bf16*)c1_buf + 2 * (int64_t)d_model;
+  c2 = vx::LinearArgs{};
+  c2.x = (const vx::bf16*)c1_buf;
+  c2.w = (const vx::bf16*)w->w2;
+  c2.M = S * n;
+  c2.N = d_model;
+  c2.K = 3 * d_model;
+  c2.rpg = n;
+  c2.xgs = (int64_t)F * d_model;
+  c2.xrs = 2 * (int64_t)d_model;
+  c2.ygs = (int64_t)n * d_model;
+  c2.yrs = d_model;
+  c2.x_bytes = (int64_t)S * F * d_model * 2;
+  c2.bias = (const vx::bf16*)w->b2;
+  c2.y = x_out;
+}
+
+vx_status check_stem(const char* what, const void* mel_buf, const void* c1_buf,
+                     const vx_enc_stem_weights* w, const float* x_out, int32_t S, int32_t n,
+                     int32_t n_mels, int32_t d_model) {
+  if (S < 0 || n < 1 || n_mels < 1 || d_model < 1)
+    return fail(VX_E_SHAPE, "%s: need S >= 0, n >= 1, n_mels >= 1, d_model >= 1", what);
+  if (n > kMaxDim / 2 || (int64_t)S * (2 * n + 2) > kMaxDim)
+    return fail(VX_E_SHAPE, "%s: S*(2n+2) too large", what);
+  if (n_mels % 128 != 0 || d_model % 128 != 0)
+    return fail(VX_E_SHAPE, "%s: n_mels (%d) and d_model (%d) must be multiples of 128", what,
+                n_mels, d_model);
+  const int64_t F = 2 * (int64_t)n + 2;
+  if ((int64_t)S * F * d_model * 2 >= ((int64_t)1 << 30) ||
+      (int64_t)d_model * 3 * d_model * 2 >= ((int64_t)1 << 30))
+    return fail(VX_E_SHAPE, "%s: buffers and weights must each be smaller than 2^30 bytes", what);
+  vx_status st;
+  if ((st = check_linear_shape(what, S * 2 * n, d_model, 3 * n_mels))) return st;
+  if ((st = check_linear_shape(what, S * n, d_model, 3 * d_model))) return st;
+  if (S == 0) return VX_OK;
+  if (!w) return fail(VX_E_NULL, "%s: stem weights are NULL", what);
+  if (!mel_buf || !c1_buf || !x_out || !w->w1 || !w->w2)
+    return fail(VX_E_NULL, "%s: mel_buf, c1_buf, x_out, w1 and w2 must be non-NULL", what);
+  const void* al[] = {mel_buf, c1_buf, x_out, w->w1, w->w2, w->b1, w->b2};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(VX_E_ALIGN, "%s: tensors must be 16-byte aligned", what);
+  return VX_OK;
+}
+
+vx_status launch_stem(void* mel_buf, void* c1_buf, const vx_enc_stem_weights* w, float* x_out,
+                      int S, int n, int n_mels, int d_model, hipStream_t hs) {
+  vx::LinearArgs c1, c2;
+  stem_args(c1, c2, mel_buf, c1_buf, w, x_out, S, n, n_mels, d_model);
+  vx_status st;
+  if ((st = launched(vx::launch_linear(c1, vx::DT::BF16, hs, vx::LinEpi::Gelu)))) return st;
+  if ((st = launched(vx::launch_linear(c2, vx::DT::F32, hs, vx::LinEpi::Gelu)))) return st;
+  return launched(vx::launch_stem_shift((vx::bf16*)mel_buf, 2 * n + 2, n_mels, (vx::bf16*)c1_buf,
+                                        2 * n + 2, d_model, S, hs));
+}
+
+vx_status check_layer_shape(const char* what, int32_t S, int32_t n, int32_t H, int32_t d_model,
+                            int32_t ffn, float eps, const vx_attn_cfg* cfg) {
+  vx_status st = check_block(what, S, n, H, d_model, cfg);
+  if (st) return st;
+  if ((st = check_stream_common(what, S, n, H, cfg))) return st;
+  if ((st = check_eps(what, eps))) return st;
+  if (n > vx::kStreamFusedMaxNew)
+    return fail(VX_E_RANGE, "%s: at most %d new frames per step (got %d)", what,
+                vx::kStreamFusedMaxNew, n);
+  if ((H * vx::kD) % 128 != 0 || d_model % 128 != 0)
+    return fail(VX_E_SHAPE, "%s: H*64 and d_model must be multiples of 128", what);
+  if (ffn < 1 || ffn % 128 != 0)
+    return fail(VX_E_SHAPE, "%s: ffn (%d) must be a positive multiple of 128", what, ffn);
+  if ((st = check_linear_shape(what, S * n, 2 * ffn, d_model))) return st;
+  if ((st = check_linear_shape(what, S * n, d_model, ffn))) return st;
+  return VX_OK;
+}
+
+vx_status check_layer_weights(const char* what, const vx_enc_layer_weights* w) {
+  if (!w) return fail(VX_E_NULL, "%s: layer weights are NULL", what);
+  if (!w->g_attn || !w->w_qkv || !w->w_o || !w->g_ffn || !w->w_gate || !w->w_up || !w->w_down)
+    return fail(VX_E_NULL, "%s: a required layer weight is NULL", what);
+  const void* al[] = {w->g_attn, w->w_qkv, w->b_q, w->b_v, w->w_o, w->b_o,
+                      w->g_ffn,  w->w_gate, w->w_up, w->w_down, w->b_down};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(VX_E_ALIGN, "%s: weights must be 16-byte aligned", what);
+  return VX_OK;
+}
+
+vx_status check_work(const char* what, const vx_enc_work* wk) {
+  if (!wk) return fail(VX_E_NULL, "%s: work is NULL", what);
+  const void* al[] = {wk->h, wk->q, wk->k, wk->v, wk->o, wk->u};
+  for (const void* p : al) {
+    if (!p) return fail(VX_E_NULL, "%s: a work buffer is NULL", what);
+    if (!aligned16(p)) return fail(VX_E_ALIGN, "%s: work buffers must be 16-byte aligned", what);
+  }
+  return VX_OK;
+}
+
+// Appends the regions of one layer's weights (read) to r.
+void weight_regions(std::vector<Region>& r, const vx_enc_layer_weights* w, int H, int dm, int ffn) {
+  const size_t hd = (size_t)H * vx::kD;
+  const Region add[] = {
+      {w->g_attn, (size_t)dm * 2, false},       {w->w_qkv, 3 * hd * dm * 2, false},
+      {w->b_q, hd * 2, false},                  {w->b_v, hd * 2, false},
+      {w->w_o, (size_t)dm * hd * 2, false},     {w->b_o, (size_t)dm * 2, false},
+      {w->g_ffn, (size_t)dm * 2, false},        {w->w_gate, (size_t)ffn * dm * 2, false},
+      {w->w_up, (size_t)ffn * dm * 2, false},   {w->w_down, (size_t)dm * ffn * 2, false},
+      {w->b_down, (size_t)dm * 2, false}};
+  for (const Region& a : add) r.push_back(a);
+}
+
+// The seven launches of one pre-norm layer (arguments validated).
+vx_status launch_layer(float* x, const vx_enc_layer_weights* w, void* ring_k, void* ring_v,
+                       const int64_t* pos_in, int64_t* pos_out, const vx_enc_work* wk, int S,
+                       int n, int H, int dm, int ffn, float eps, const vx_attn_cfg* cfg,
+                       const vx::RopeFreqs& fr, hipStream_t hs) {
+  const int M = S * n, HD = H * vx::kD;
+  vx_status st;
+  // 1. h = rmsnorm(x) * g_attn
+  if ((st = launched(vx::launch_rmsnorm(x, (const vx::bf16*)w->g_attn, (vx::bf16*)wk->h, M, dm,
+                                        eps, hs))))
+    return st;
+  // 2. q', k' (rotated at pos_in[s] + i), v
+  vx::LinearArgs a{};
+  a.x = (const vx::bf16*)wk->h;
+  a.w = (const vx::bf16*)w->w_qkv;
+  a.M = M;
+  a.N = 3 * HD;
+  a.K = dm;
+  a.HD = HD;
+  a.n = n;
+  a.pos = pos_in;
+  a.b_q = (const vx::bf16*)w->b_q;
+  a.b_v = (const vx::bf16*)w->b_v;
+  a.q = (vx::bf16*)wk->q;
+  a.k = (vx::bf16*)wk->k;
+  a.v = (vx::bf16*)wk->v;
+  vx::dense_rows(a);
+  if ((st = launched(vx::launch_qkv_rope(a, fr, hs)))) return st;
+  // 3. attention over the ring and the new frames, then the append
+  vx::StreamArgs sa{};
+  sa.q = wk->q;
+  sa.k = wk->k;
+  sa.v = wk->v;
+  sa.ring_k = ring_k;
+  sa.ring_v = ring_v;
+  sa.pos = pos_in;
+  sa.o = wk->o;
+  sa.S = S;
+  sa.n = n;
+  sa.H = H;
+  sa.W = cfg->window;
+  sa.rope = false;
+  sa.scale_log2 = scale_log2(cfg);
+  sa.append = true;
+  sa.ring_k_w = ring_k;
+  sa.ring_v_w = ring_v;
+  sa.pos_out = pos_out;
+  if ((st = launched(vx::launch_stream_step(sa, vx::DT::BF16, vx::DT::BF16, fr, hs)))) return st;
+  // 4. x += o W_o^T + b_o
+  vx::LinearArgs b{};
+  b.x = (const vx::bf16*)wk->o;
+  b.w = (const vx::bf16*)w->w_o;
+  b.M = M;
+  b.N = dm;
+  b.K = HD;
+  b.bias = (const vx::bf16*)w->b_o;
+  b.y = x;
+  b.res = x;
+  vx::dense_rows(b);
+  if ((st = launched(vx::launch_linear(b, vx::DT::F32, hs, vx::LinEpi::Residual)))) return st;
+  // 5. h = rmsnorm(x) * g_ffn
+  if ((st = launched(vx::launch_rmsnorm(x, (const vx::bf16*)w->g_ffn, (vx::bf16*)wk->h, M, dm,
+                                        eps, hs))))
+    return st;
+  // 6. u = silu(h W_gate^T) * (h W_up^T)
+  vx::LinearArgs g{};
+  g.x = (const vx::bf16*)wk->h;
+  g.w = (const vx::bf16*)w->w_gate;
+  g.w2 = (const vx::bf16*)w->w_up;
+  g.M = M;
+  g.N = 2 * ffn;
+  g.K = dm;
+  g.y = wk->u;
+  vx::dense_rows(g);
+  if ((st = launched(vx::launch_linear(g, vx::DT::BF16, hs, vx::LinEpi::SwiGLU)))) return st;
+  // 7. x += u W_down^T + b_down
+  vx::LinearArgs d{};
+  d.x = (const vx::bf16*)wk->u;
+  d.w = (const vx::bf16*)w->w_down;
+  d.M = M;
+  d.N = dm;
+  d.K = ffn;
+  d.bias = (const vx::bf16*)w->b_down;
+  d.y = x;
+  d.res = x;
+  vx::dense_rows(d);
+  return launched(vx::launch_linear(d, vx::DT::F32, hs, vx::LinEpi::Residual));
+}
+
+}  // namespace
+
+vx_status vx_rmsnorm(const float* x, const void* g, void* y, int32_t M, int32_t dim, float eps,
+                     void* stream) {
+  const char* what = "rmsnorm";
+  if (M < 0 || dim < 1) return fail(VX_E_SHAPE, "%s: need M >= 0 and dim >= 1", what);
+  if (dim % 8 != 0) return fail(VX_E_SHAPE, "%s: dim (%d) must be a multiple of 8", what, dim);
+  if (M > kMaxDim * 4 || dim > kMaxDim || (int64_t)M * dim > kMaxElems)
+    return fail(VX_E_SHAPE, "%s: size too large", what);
+  vx_status st = check_eps(what, eps);
+  if (st) return st;
+  if (M == 0) return ok();
+  if (!x || !g || !y) return fail(VX_E_NULL, "%s: x, g and y must be non-NULL", what);
+  if (!aligned16(x) || !aligned16(g) || !aligned16(y))
+    return fail(VX_E_ALIGN, "%s: x, g and y must be 16-byte aligned", what);
+  const size_t yb = (size_t)M * dim * 2;
+  if (overlap(y, yb, x, (size_t)M * dim * 4) || overlap(y, yb, g, (size_t)dim * 2))
+    return fail(VX_E_RANGE, "%s: y overlaps an input", what);
+  (void)hipGetLastError();
+  return launched(vx::launch_rmsnorm(x, (const vx::bf16*)g, (vx::bf16*)y, M, dim, eps,
+                                     (hipStream_t)stream));
+}
+
+vx_status vx_enc_stem_step(void* mel_buf, void* c1_buf, const vx_enc_stem_weights* w,
+                           float* x_out, int32_t S, int32_t n, int32_t n_mels, int32_t d_model,
+                           void* stream) {
+  const char* what = "enc_stem_step";
+  vx_status st = check_stem(what, mel_buf, c1_buf, w, x_out, S, n, n_mels, d_model);
+  if (st) return st;
+  if (S == 0) return ok();
+  const size_t F = 2 * (size_t)n + 2;
+  const std::vector<Region> r = {{mel_buf, S * F * n_mels * 2, true},
+                      {c1_buf, S * F * d_model * 2, true},
+                      {x_out, (size_t)S * n * d_model * 4, true},
+                      {w->w1, (size_t)d_model * 3 * n_mels * 2, false},
+                      {w->b1, (size_t)d_model * 2, false},
+                      {w->w2, (size_t)d_model * 3 * d_model * 2, false},
+                      {w->b2, (size_t)d_model * 2, false}};
+  if (!regions_disjoint(r)) return fail(VX_E_RANGE, "%s: buffers overlap", what);
+  (void)hipGetLastError();
+  return launch_stem(mel_buf, c1_buf, w, x_out, S, n, n_mels, d_model, (hipStream_t)stream);
+}
+
+vx_status vx_enc_layer_step(float* x, const vx_enc_layer_weights* w, void* ring_k, void* ring_v,
+                            const int64_t* pos_in, int64_t* pos_out, const vx_enc_work* work,
+                            int32_t S, int32_t n, int32_t H, int32_t d_model, int32_t ffn,
+                            float eps, const vx_attn_cfg* cfg, void* stream) {
+  return vx_enc_step(nullptr, nullptr, nullptr, w, 1, ring_k, ring_v, pos_in, pos_out, x, work, S,
+                     n, 0, H, d_model, ffn, eps, cfg, stream);
+}
+
+vx_status vx_enc_step(void* mel_buf, void* c1_buf, const vx_enc_stem_weights* stem,
+                      const vx_enc_layer_weights* layers, int32_t L, void* ring_k, void* ring_v,
+                      const int64_t* pos_in, int64_t* pos_out, float* x, const vx_enc_work* work,
+                      int32_t S, int32_t n, int32_t n_mels, int32_t H, int32_t d_model,
+                      int32_t ffn, float eps, const vx_attn_cfg* cfg, void* stream) {
+  const bool with_stem = stem != nullptr;
+  const char* what = with_stem ? "enc_step" : "enc_layer_step";
+  vx_status st = check_layer_shape(what, S, n, H, d_model, ffn, eps, cfg);
+  if (st) return st;
+  if (L < 1 || L > 4096) return fail(VX_E_SHAPE, "%s: L (%d) must be in [1, 4096]", what, L);
+  if (with_stem && (st = check_stem(what, mel_buf, c1_buf, stem, x, S, n, n_mels, d_model)))
+    return st;
+  if (S == 0) return ok();
+  if (!layers) return fail(VX_E_NULL, "%s: layers is NULL", what);
+  for (int l = 0; l < L; ++l)
+    if ((st = check_layer_weights(what, &layers[l]))) return st;
+  if (!x || !pos_in || !pos_out || !ring_k || !ring_v)
+    return fail(VX_E_NULL, "%s: x, rings, pos_in and pos_out must be non-NULL", what);
+  if (!aligned16(x) || !aligned16(ring_k) || !aligned16(ring_v))
+    return fail(VX_E_ALIGN, "%s: x and the rings must be 16-byte aligned", what);
+  if (((uintptr_t)pos_in & 7u) != 0 || ((uintptr_t)pos_out & 7u) != 0)
+    return fail(VX_E_ALIGN, "%s: pos_in/pos_out must be 8-byte aligned", what);
+  if ((st = check_work(what, work))) return st;
+  const size_t M = (size_t)S * n, act = M * H * vx::kD * 2;
+  const size_t ring1 = (size_t)S * H * cfg->window * vx::kD * 2, pb = (size_t)S * 8;
+  // every written region against everything else
+  std::vector<Region> r;
+  r.reserve(19 + 11 * (size_t)L);
+  const size_t F = 2 * (size_t)n + 2;
+  r.push_back({x, M * d_model * 4, true});
+  r.push_back({pos_in, pb, false});
+  r.push_back({pos_out, pb, true});
+  r.push_back({ring_k, ring1 * L, true});
+  r.push_back({ring_v, ring1 * L, true});
+  r.push_back({work->h, M * d_model * 2, true});
+  r.push_back({work->q, act, true});
+  r.push_back({work->k, act, true});
+  r.push_back({work->v, act, true});
+  r.push_back({work->o, act, true});
+  r.push_back({work->u, M * ffn * 2, true});
+  if (with_stem) {
+    r.push_back({mel_buf, S * F * n_mels * 2, true});
+    r.push_back({c1_buf, S * F * d_model * 2, true});
+    r.push_back({stem->w1, (size_t)d_model * 3 * n_mels * 2, false});
+    r.push_back({stem->b1, (size_t)d_model * 2, false});
+    r.push_back({stem->w2, (size_t)d_model * 3 * d_model * 2, false});
+    r.push_back({stem->b2, (size_t)d_model * 2, false});
+  }
+  for (int l = 0; l < L; ++l) weight_regions(r, &layers[l], H, d_model, ffn);
+  if (!regions_disjoint(r)) return fail(VX_E_RANGE, "%s: buffers overlap", what);
+  (void)hipGetLastError();
+  const hipStream_t hs = (hipStream_t)stream;
+  if (with_stem && (st = launch_stem(mel_buf, c1_buf, stem, x, S, n, n_mels, d_model, hs)))
+    return st;
+  const vx::RopeFreqs fr = rope_freqs(cfg->rope_theta);
+  for (int l = 0; l < L; ++l) {
+    char* rk = (char*)ring_k + ring1 * l;
+    char* rv = (char*)ring_v + ring1 * l;
+    if ((st = launch_layer(x, &layers[l], rk, rv, pos_in, pos_out, work, S, n, H, d_model, ffn,
+                           eps, cfg, fr, hs)))
+      return st;
+  }
+  return ok();
 }
 
 const char* vx_status_string(vx_status s) {

@@ -338,3 +338,54 @@ def make_enc_block_input(S: int, n: int, d_model: int, *, seed, step: int):
     """Normalised hidden states x [S, n, d_model] (N(0,1), bf16) for streaming step `step`."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77, step])))
     return _store(rng.standard_normal((S, n, d_model), dtype=np.float32), "bf16")
+
+
+# Whole streaming encoder step: stem + L pre-norm layers, 64 streams x 4 new
+# frames (8 mel frames of 128 bins), d_model 1280, 32 heads x 64, FFN 5120.
+ENC_STEP = dict(S=64, n=4, H=32, d_model=1280, ffn=5120, n_mels=128, L=32, W=750, seed=9,
+                pos_lo=750, pos_hi=20000)
+
+
+def make_enc_stem_weights(d_model: int, n_mels: int, *, seed):
+    """Synthetic stem weights (bf16 values in float32 arrays).
+
+    w1 [d_model, 3, n_mels] and w2 [d_model, 3, d_model] (output, tap, input)
+    are N(0, 1/fan_in) with fan_in = 3 * input channels; b1, b2 [d_model] are
+    0.02*N(0,1).  Draw order: w1, b1, w2, b2.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2025])))
+    w1 = rng.standard_normal((d_model, 3, n_mels), dtype=np.float32) * np.float32((3 * n_mels) ** -0.5)
+    b1 = rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.02)
+    w2 = rng.standard_normal((d_model, 3, d_model), dtype=np.float32) * np.float32((3 * d_model) ** -0.5)
+    b2 = rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.02)
+    return {name: _store(a, "bf16") for name, a in (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2))}
+
+
+def make_enc_layer_weights(d_model: int, H: int, ffn: int, *, seed, layer: int):
+    """Synthetic weights of one pre-norm layer (bf16 values in float32 arrays).
+
+    The attention projections are make_enc_block_weights' recipe (seeded by
+    [seed, layer]); the RMSNorm gains g_attn, g_ffn [d_model] are 1 + 0.1*N(0,1);
+    w_gate, w_up [ffn, d_model] are N(0, 1/d_model), w_down [d_model, ffn]
+    N(0, 1/ffn), b_down 0.02*N(0,1).  Draw order: g_attn, g_ffn, w_gate,
+    w_up, w_down, b_down.
+    """
+    wts = make_enc_block_weights(d_model, H, seed=[seed, layer])
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2026, layer])))
+    g_attn = 1 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1)
+    g_ffn = 1 + rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.1)
+    w_gate = rng.standard_normal((ffn, d_model), dtype=np.float32) * np.float32(d_model ** -0.5)
+    w_up = rng.standard_normal((ffn, d_model), dtype=np.float32) * np.float32(d_model ** -0.5)
+    w_down = rng.standard_normal((d_model, ffn), dtype=np.float32) * np.float32(ffn ** -0.5)
+    b_down = rng.standard_normal(d_model, dtype=np.float32) * np.float32(0.02)
+    for name, a in (("g_attn", g_attn), ("g_ffn", g_ffn), ("w_gate", w_gate), ("w_up", w_up),
+                    ("w_down", w_down), ("b_down", b_down)):
+        wts[name] = _store(a, "bf16")
+    return wts
+
+
+def make_mel(S: int, frames: int, n_mels: int, *, seed, step: int):
+    """Log-mel frames [S, frames, n_mels] for streaming step `step`: 0.5*N(0,1)
+    (the spread of normalised log-mel features), bf16."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 79, step])))
+    return _store(rng.standard_normal((S, frames, n_mels), dtype=np.float32) * np.float32(0.5), "bf16")

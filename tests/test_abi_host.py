@@ -42,7 +42,8 @@ def test_header_declares_the_four_calls():
               "vx_swa_attn_stream_step_append", "vx_rope_table", "vx_status_string",
               "vx_last_error", "vx_version", "vx_default_cfg", "vx_swa_attn_prefill_varlen",
               "vx_default_gqa_cfg", "vx_gqa_attn_prefill", "vx_gqa_attn_decode", "vx_linear",
-              "vx_enc_qkv_rope", "vx_enc_attn_step"):
+              "vx_enc_qkv_rope", "vx_enc_attn_step", "vx_rmsnorm", "vx_enc_stem_step",
+              "vx_enc_layer_step", "vx_enc_step"):
         assert f in names
 
 
@@ -493,4 +494,152 @@ def test_enc_qkv_rope_and_attn_step_errors(L):
     assert step(y=z) == E_NULL
     assert step(cc=cfg(flags=1)) == E_RANGE
     assert step(S=0) == OK
+    assert b.untouched()
+
+
+# ---------------------------------------------------------------------------
+# the streaming encoder step
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_argument_errors(L):
+    b = Bufs()
+    z = ctypes.c_void_p(0)
+
+    def call(M=4, dim=128, eps=1e-5, **ov):
+        a = dict(x=b.new(), g=b.new(), y=b.new())
+        a.update(ov)
+        return L.vx_rmsnorm(a["x"], a["g"], a["y"], M, dim, eps, None)
+    assert call(dim=12) == E_SHAPE
+    assert call(dim=0) == E_SHAPE
+    assert call(M=-1) == E_SHAPE
+    assert call(eps=-1.0) == E_RANGE
+    assert call(eps=float("nan")) == E_RANGE
+    assert call(g=z) == E_NULL
+    assert call(y=ctypes.c_void_p(b.new().value + 2)) == E_ALIGN
+    r = b.new()
+    assert call(x=r, y=r) == E_RANGE
+    assert call(M=0) == OK
+    assert b.untouched()
+
+
+def _stem_w(b, **ov):
+    z = ctypes.c_void_p(0)
+    a = dict(w1=b.new(), b1=z, w2=b.new(), b2=z)
+    a.update(ov)
+    return vx._StemW(*[a[k] for k in vx.STEM_KEYS])
+
+
+def test_enc_stem_step_argument_errors(L):
+    b = Bufs(1 << 18)
+    z = ctypes.c_void_p(0)
+
+    def call(S=2, n=2, nm=128, dm=128, w=None, **ov):
+        a = dict(mel=b.new(), c1=b.new(), x=b.new())
+        a.update(ov)
+        w = _stem_w(b) if w is None else w
+        return L.vx_enc_stem_step(a["mel"], a["c1"], None if w is False else ctypes.byref(w),
+                                  a["x"], S, n, nm, dm, None)
+    assert call(nm=100) == E_SHAPE         # 3*n_mels not a multiple of 128
+    assert call(dm=200) == E_SHAPE
+    assert call(n=0) == E_SHAPE
+    assert call(S=-1) == E_SHAPE
+    assert call(w=False) == E_NULL
+    assert call(w=_stem_w(b, w2=z)) == E_NULL
+    assert call(x=z) == E_NULL
+    assert call(w=_stem_w(b, b1=ctypes.c_void_p(b.new().value + 2))) == E_ALIGN
+    r = b.new()
+    assert call(mel=r, c1=r) == E_RANGE
+    r = b.new()
+    assert call(x=r, w=_stem_w(b, w2=r)) == E_RANGE
+    assert call(S=0) == OK
+    assert b.untouched()
+
+
+def _layer_w(b, **ov):
+    z = ctypes.c_void_p(0)
+    a = {k: (z if k.startswith("b_") else b.new()) for k in vx.LAYER_KEYS}
+    a.update(ov)
+    return vx._LayerW(*[a[k] for k in vx.LAYER_KEYS])
+
+
+def _work(b, **ov):
+    a = {k: b.new() for k in vx.WORK_KEYS}
+    a.update(ov)
+    return vx._Work(*[a[k] for k in vx.WORK_KEYS])
+
+
+def test_enc_layer_step_argument_errors(L):
+    b = Bufs(1 << 18)
+    z = ctypes.c_void_p(0)
+    c = cfg(window=8)
+
+    def call(S=1, n=4, H=2, dm=128, ffn=128, eps=1e-5, cc=c, w=None, wk=None, **ov):
+        a = dict(x=b.new(), rk=b.new(), rv=b.new(), pin=b.new(), pout=b.new())
+        a.update(ov)
+        w = _layer_w(b) if w is None else w
+        wk = _work(b) if wk is None else wk
+        return L.vx_enc_layer_step(a["x"], None if w is False else ctypes.byref(w), a["rk"],
+                                   a["rv"], a["pin"], a["pout"],
+                                   None if wk is False else ctypes.byref(wk), S, n, H, dm, ffn,
+                                   eps, ctypes.byref(cc), None)
+    assert call(n=17, cc=cfg(window=32)) == E_RANGE   # above the fused step's 16 frames
+    assert call(n=9) == E_RANGE                        # n > W
+    assert call(ffn=100) == E_SHAPE
+    assert call(ffn=0) == E_SHAPE
+    assert call(H=1) == E_SHAPE                        # H*64 = 64 is not a multiple of 128
+    assert call(dm=200) == E_SHAPE
+    assert call(eps=-1.0) == E_RANGE
+    assert call(eps=float("inf")) == E_RANGE
+    assert call(cc=cfg(window=8, flags=1)) == E_RANGE
+    assert call(cc=cfg(window=8, io_dtype=vx.VX_F32, out_dtype=vx.VX_F32)) == E_DTYPE
+    assert call(w=False) == E_NULL
+    assert call(w=_layer_w(b, w_up=z)) == E_NULL
+    assert call(w=_layer_w(b, g_ffn=z)) == E_NULL
+    assert call(wk=False) == E_NULL
+    assert call(wk=_work(b, u=z)) == E_NULL
+    assert call(wk=_work(b, o=ctypes.c_void_p(b.new().value + 2))) == E_ALIGN
+    assert call(w=_layer_w(b, b_down=ctypes.c_void_p(b.new().value + 4))) == E_ALIGN
+    assert call(pin=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    p = b.new()
+    assert call(pin=p, pout=p) == E_RANGE
+    r = b.new()
+    assert call(rk=r, rv=r) == E_RANGE
+    r = b.new()
+    assert call(x=r, wk=_work(b, h=r)) == E_RANGE
+    r = b.new()
+    assert call(x=r, w=_layer_w(b, w_down=r)) == E_RANGE
+    r = b.new()
+    assert call(wk=_work(b, q=r, k=r)) == E_RANGE
+    assert call(S=0) == OK
+    assert b.untouched()
+
+
+def test_enc_step_argument_errors(L):
+    b = Bufs(1 << 18)
+    z = ctypes.c_void_p(0)
+    c = cfg(window=8)
+
+    def call(S=1, n=2, nm=128, H=2, dm=128, ffn=128, nl=2, layers=None, stem=None, **ov):
+        a = dict(mel=b.new(), c1=b.new(), x=b.new(), rk=b.new(), rv=b.new(), pin=b.new(),
+                 pout=b.new())
+        a.update(ov)
+        if layers is None:
+            layers = [_layer_w(b) for _ in range(max(nl, 1))]
+        arr = (vx._LayerW * len(layers))(*layers) if layers is not False else None
+        stem = _stem_w(b) if stem is None else stem
+        wk = _work(b)
+        return L.vx_enc_step(a["mel"], a["c1"], ctypes.byref(stem), arr, nl, a["rk"], a["rv"],
+                             a["pin"], a["pout"], a["x"], ctypes.byref(wk), S, n, nm, H, dm, ffn,
+                             1e-5, ctypes.byref(c), None)
+    assert call(nl=0) == E_SHAPE
+    assert call(nl=5000) == E_SHAPE
+    assert call(layers=False) == E_NULL
+    assert call(layers=[_layer_w(b), _layer_w(b, w_qkv=z)]) == E_NULL
+    assert call(nm=64) == E_SHAPE
+    assert call(stem=_stem_w(b, w1=z)) == E_NULL
+    r = b.new()
+    assert call(mel=r, x=r) == E_RANGE
+    r = b.new()
+    assert call(c1=r, layers=[_layer_w(b, w_o=r), _layer_w(b)]) == E_RANGE
+    assert call(S=0) == OK
     assert b.untouched()
