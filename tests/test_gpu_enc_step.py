@@ -71,7 +71,8 @@ def _check_resid(got, want, what, exact=None):
 # RMSNorm
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,dim", [(1, 8), (5, 1280), (300, 1280), (7, 5120), (3, 72)])
+@pytest.mark.parametrize("M,dim", [(1, 8), (5, 1280), (300, 1280), (7, 5120), (3, 72), (2, 640),
+                                   (9, 2048), (4, 4096)])
 def test_rmsnorm_matches_oracle(M, dim):
     import torch
     say(f"rmsnorm M{M} dim {dim}")
