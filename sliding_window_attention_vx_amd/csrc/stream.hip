@@ -319,8 +319,10 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreq
 // one wave per ring; the waves' partial (max, sum, O) merge through LDS at the
 // end.  Per block and wave:
 //   S^T = K' Q'^T  two 16-key MFMA pairs; the A operand (16 keys x 8 dims per
-//                  lane) is loaded straight from the ring in HBM; new keys are
-//                  rotated in registers (dims d and d+32 sit in the same lane).
+//                  lane).  Ring keys load as whole 128-byte rows (8 lanes per
+//                  row, like the values) into this wave's LDS (144-byte rows)
+//                  and come back in the operand layout; new keys are rotated
+//                  in registers (dims d and d+32 sit in the same lane).
 //   softmax        lane (q, g) holds query q's scores for keys 4g..4g+3 and
 //                  16+4g..16+4g+3; the row max/sum reduce over the four lanes
 //                  of q with v_permlane16_swap / v_permlane32_swap; lazy
@@ -335,6 +337,9 @@ constexpr int kSQ = 16;                    // query columns per wave
 constexpr int kSWaves = 2;                 // waves per workgroup, each taking half the keys
 constexpr int kSRowV = 160;                // LDS bytes per staged V row (conflict-free)
 constexpr int kSBufV = 32 * kSRowV;        // one 32-key V block
+constexpr int kSRowK = 144;                // LDS bytes per staged K row (conflict-free reads)
+constexpr int kSBufK = 32 * kSRowK;        // one 32-key K block
+constexpr int kSWaveBuf = kSBufV + kSBufK;  // one wave's staging rows
 
 __device__ __forceinline__ float max16x(float x) {  // max over lanes l, l^16
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -374,7 +379,8 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane & 15, g = lane >> 4;
-  char* vbuf = work + wave * 2 * kSBufV;  // this wave's two 32-key V blocks
+  char* vbuf = work + wave * kSWaveBuf;  // this wave's V block, then its K block
+  char* kbuf = vbuf + kSBufV;
 
   const int64_t P = a.pos[s];
   const int64_t lo = max((int64_t)0, P + i0 - W + 1);
@@ -470,16 +476,20 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
     }
   };
 
-  // blocks made only of ring keys (kb + 32 <= nring): unconditional loads
+  // blocks made only of ring keys (kb + 32 <= nring): unconditional loads.
+  // Keys load whole 128-byte rows like the values (k[sb][hf] holds rows
+  // 16sb + 8hf + lane/8, 16-byte chunk lane%8) and reach the A-operand layout
+  // through the wave's LDS rows: a lane's operand needs one key per lane%16,
+  // which would split every row over two load instructions.
   auto load_ring = [&](int kb, Blk& B) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      int slot = lo_slot + kb + 16 * sb + q;
-      if (slot >= W) slot -= W;
-      const bf16* kr = rk + (size_t)slot * kD + 8 * g;
-      B.k[sb][0] = ring_row_load(kr);
-      B.k[sb][1] = ring_row_load(kr + kHalf);
-    }
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int slot = lo_slot + kb + 16 * sb + 8 * hf + (lane >> 3);
+        if (slot >= W) slot -= W;
+        B.k[sb][hf] = ring_row_load(rk + (size_t)slot * kD + 8 * (lane & 7));
+      }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int slot = lo_slot + kb + 8 * j + (lane >> 3);
@@ -503,20 +513,44 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   // One block.  Only the first block (ring keys that leave the window of a
   // later query of the chunk: key index < 15) and the blocks past the ring
   // keys (new frames, padding) can hold masked keys; the others skip the mask.
-  auto step = [&](const Blk& cur, int bi) {
+  // The wave's V and K rows are rewritten every block with no barrier: LDS
+  // instructions of one wave execute in order, so a block's writes land after
+  // the previous block's reads; the asm statements keep the compiler's order.
+  auto step = [&](const Blk& cur, int bi, bool ring_rows) {
     const int kb = 32 * bi;
-    char* vb = vbuf + (bi & 1) * kSBufV;
+    char* vb = vbuf;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<u32x4*>(vb + (8 * j + (lane >> 3)) * kSRowV + 16 * (lane & 7)) = cur.v[j];
+    u32x4 ka[2][2];
+    if (ring_rows) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          *reinterpret_cast<u32x4*>(kbuf + (16 * sb + 8 * hf + (lane >> 3)) * kSRowK +
+                                    16 * (lane & 7)) = cur.k[sb][hf];
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          ka[sb][hf] = *reinterpret_cast<const u32x4*>(kbuf + (16 * sb + q) * kSRowK + 64 * hf +
+                                                       16 * g);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ka[sb][hf] = cur.k[sb][hf];
+    }
 
     f32x4 sc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[sb][0]),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[sb][0]),
                                                     qf[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[sb][1]),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[sb][1]),
                                                     qf[1], acc, 0, 0, 0);
       sc[sb] = acc;
     }
@@ -581,12 +615,12 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   if (b0 < bf) load_ring(32 * b0, cur);
   for (int bi = b0; bi < bf; ++bi) {
     if (bi + 1 < bf) load_ring(32 * (bi + 1), nxt);
-    step(cur, bi);
+    step(cur, bi, true);
     cur = nxt;
   }
   for (int bi = bf; bi < b1; ++bi) {
     load_blk(32 * bi, cur);
-    step(cur, bi);
+    step(cur, bi, false);
   }
 
   // ---- merge the waves' partial (max, sum, O^T) through LDS
@@ -724,7 +758,7 @@ hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreq
   }
   // bf16: matrix-core kernel, one wave per (stream, head, 16-query chunk)
   dim3 grid16((unsigned)(a.S * a.H), (unsigned)((a.n + kSQ - 1) / kSQ));
-  constexpr size_t kVBufs = (size_t)kSWaves * 2 * kSBufV;
+  constexpr size_t kVBufs = (size_t)kSWaves * kSWaveBuf;
   constexpr size_t kMerge = (size_t)kSWaves * (2 * 16 + 16 * kD) * sizeof(float);
   const size_t smem16 = align16((size_t)a.n * kD * sizeof(float)) + (kVBufs > kMerge ? kVBufs : kMerge);
   if (out == DT::BF16)
