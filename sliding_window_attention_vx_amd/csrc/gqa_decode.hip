@@ -11,9 +11,11 @@
 // max(0, P-W+1) .. P-1, then the n new tokens.  The keys are cut into NW
 // contiguous runs of 32-key blocks, one run per wave, and each wave keeps the
 // next block's ring loads in flight while it computes the current one:
-//   S^T = K' Q'^T  four MFMAs per 16 keys (128 dims); K' rows go from the
-//                  ring straight into A-operand registers (lane (key, g)
-//                  holds dims 32m+8g..32m+8g+7 of step m, and the RoPE
+//   S^T = K' Q'^T  four MFMAs per 16 keys (128 dims); the A operand: lane
+//                  (key, g) holds dims 32m+8g..32m+8g+7 of step m.  Ring
+//                  keys load as whole 256-byte rows (16 lanes per row) into
+//                  the wave's LDS rows (272 bytes) and come back in that
+//                  layout; new keys are rotated in registers (the RoPE
 //                  partner dims d+64 sit in the same lane).
 //   softmax        lane (c, g) holds column c's scores of keys 4g..4g+3 and
 //                  16+4g..16+4g+3; the max and the sum reduce over lanes c,
@@ -36,6 +38,9 @@ namespace {
 
 constexpr int kVRow = 288;          // LDS bytes per staged V row (256 + 32)
 constexpr int kVBuf = 32 * kVRow;   // one wave's 32-key V block
+constexpr int kKRow = 272;          // LDS bytes per staged K row (256 + 16: conflict-free reads)
+constexpr int kKBuf = 32 * kKRow;   // one wave's 32-key K block
+constexpr int kWaveBuf = kVBuf + kKBuf;
 constexpr float kLazyMax = 8.0f;    // log2-domain slack of the running max
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
@@ -64,9 +69,12 @@ __device__ __forceinline__ u32x4 ring_load(const bf16* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// One 32-key block in registers: K' A-operand rows and V rows.
+// One 32-key block in registers: K' rows and V rows.  k holds either the
+// A-operand layout ([16-key half][32-dim MFMA step]: key 16*half + lane%16)
+// or, for pure-ring blocks, whole rows (k[sb][m]: row 16sb + 4m + lane/16,
+// 16 bytes at 16*(lane%16)).
 struct KvBlock {
-  u32x4 k[2][4];  // [16-key half][32-dim MFMA step]: key 16*half + (lane%16)
+  u32x4 k[2][4];
   u32x4 v[8];     // row 4j + lane/16, 16 bytes at 16*(lane%16)
 };
 
@@ -82,7 +90,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
   const int c = lane & 15, g = lane >> 4;
   float* cs = (float*)smem;  // [n][128]: cos of pair i at j*128+i, sin at j*128+64+i
   char* work = smem + (size_t)n * kGD * sizeof(float);
-  char* vb = work + wave * kVBuf;
+  char* vb = work + wave * kWaveBuf;
+  char* kbuf = vb + kVBuf;
 
   const int64_t P = a.pos_in[s];
   const int64_t lo = P - W + 1 > 0 ? P - W + 1 : 0;
@@ -149,13 +158,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
   // tokens, no new-token rotation
   auto load_ring = [&](int kb, KvBlock& B) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      int slot = lo_slot + kb + 16 * sb + c;
-      if (slot >= W) slot -= W;
-      const bf16* kr = rk + (size_t)slot * kGD + 8 * g;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) B.k[sb][m] = ring_load(kr + 32 * m);
-    }
+      for (int m = 0; m < 4; ++m) {
+        int slot = lo_slot + kb + 16 * sb + 4 * m + g;
+        if (slot >= W) slot -= W;
+        B.k[sb][m] = ring_load(rk + (size_t)slot * kGD + 8 * c);
+      }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int slot = lo_slot + kb + 4 * j + g;
@@ -214,17 +223,36 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
   for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto compute = [&](const KvBlock& B, int kb, bool masked) {
+  auto compute = [&](const KvBlock& B, int kb, bool masked, bool ring_rows) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x4*>(vb + (4 * j + g) * kVRow + 16 * c) = B.v[j];
+    u32x4 ka[2][4];
+    if (ring_rows) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          *reinterpret_cast<u32x4*>(kbuf + (16 * sb + 4 * m + g) * kKRow + 16 * c) = B.k[sb][m];
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          ka[sb][m] = *reinterpret_cast<const u32x4*>(kbuf + (16 * sb + c) * kKRow + 64 * m + 16 * g);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ka[sb][m] = B.k[sb][m];
+    }
     f32x4 sc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, B.k[sb][m]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[sb][m]),
                                                       qf[m], acc, 0, 0, 0);
       sc[sb] = acc;
     }
@@ -296,17 +324,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
     load_ring(32 * b0, B0);
     for (int bi = b0; bi < bf; bi += 2) {
       if (bi + 1 < bf) load_ring(32 * (bi + 1), B1);
-      compute(B0, 32 * bi, 32 * bi < edge);
+      compute(B0, 32 * bi, 32 * bi < edge, true);
       if (bi + 1 < bf) {
         if (bi + 2 < bf) load_ring(32 * (bi + 2), B0);
-        compute(B1, 32 * (bi + 1), 32 * (bi + 1) < edge);
+        compute(B1, 32 * (bi + 1), 32 * (bi + 1) < edge, true);
       }
     }
   }
   for (int bi = bf; bi < b1; ++bi) {
     KvBlock B;
     load_any(32 * bi, B);
-    compute(B, 32 * bi, true);
+    compute(B, 32 * bi, true, false);
   }
 
   // ---- merge the waves' partial results through LDS
@@ -372,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
   if (kvh == 0 && tid == 0) a.pos_out[s] = P + n;
 }
 
-constexpr int kDecodeWaves = 4;  // 36 KB of LDS; VGPRs allow two waves per SIMD
+constexpr int kDecodeWaves = 4;  // 72 KB of LDS; VGPRs allow two waves per SIMD
 
 }  // namespace
 
@@ -380,7 +408,7 @@ hipError_t launch_gqa_decode(const GqaDecodeArgs& a, DT out, const RopeFreqs128&
                              hipStream_t st) {
   constexpr int NW = kDecodeWaves;
   const size_t merge = (size_t)NW * 32 * sizeof(float) + (size_t)NW * 16 * kGD * sizeof(float);
-  const size_t work = (size_t)NW * kVBuf > merge ? (size_t)NW * kVBuf : merge;
+  const size_t work = (size_t)NW * kWaveBuf > merge ? (size_t)NW * kWaveBuf : merge;
   const size_t smem = (size_t)a.n * kGD * sizeof(float) + work;
   const dim3 grid((unsigned)((int64_t)a.S * a.Hkv)), blk(NW * 64);
   if (out == DT::BF16)
