@@ -4,165 +4,44 @@
 // encoder: 1280 -> 3 x 32 x 64 for q, k, v and 32 x 64 -> 1280 for the output
 // projection; transcribe.cpp "Voxtral" family notes, Architecture).
 //
+// The same kernel runs the streaming encoder step's other products: the two
+// causal convolutions of the stem (a row map reads each output frame's
+// window of input frames as one K-contiguous row), the gate/up projection
+// with SwiGLU, and the output and down projections added into the float32
+// residual stream.
+//
 // One workgroup computes an MT x NC tile of y with (MT/32) x (NC/32) waves,
 // one 32 x 32 block per wave (v_mfma_f32_32x32x16_bf16: A = 32 rows of x,
-// B = 32 rows of w, 16 k per step).  K advances in stages of 128: each stage's
-// x and w rows go global -> registers -> LDS (rows padded to 272 bytes so the
-// 16-byte operand reads of 16 consecutive rows hit distinct banks), with the
-// next two stages' loads in flight in two register sets while the current
-// stage computes (buffer loads with loop-invariant per-lane offsets, all
-// unconditional, so the compiler keeps both stages in flight).  The epilogue
-// parks the fp32 tile in LDS and writes whole 16-byte chunks: either
-// y + bias (bf16 or fp32), or, for the fused q/k/v projection, q + b_q and k
-// rotated at each row's position (RoPE pairs d and d+32 of a head lie in the
-// same 64-column tile), v + b_v, all rounded to bf16.
+// B = 32 rows of w, 16 k per step).  K advances in stages of 64 (64 x 64
+// tiles) or 128 (64 x 32 tiles); each stage's x and w rows go straight from
+// global memory into LDS, three stages deep, and the operand reads come back
+// through a chunk swizzle that keeps them free of bank conflicts.  The
+// epilogue parks the fp32 tile in LDS and writes whole 16-byte chunks: y +
+// bias (bf16 or fp32), GELU(y + bias), res + y + bias (fp32), silu(gate) * up
+// (bf16), or for the fused q/k/v projection q + b_q and k rotated at each
+// row's position (RoPE pairs d and d+32 of a head lie in the same 64-column
+// tile), v + b_v, all rounded to bf16.
 #include "linear_launch.h"
 
 namespace vx {
 
 namespace {
 
-constexpr int kKS = kLinKStep;       // k per stage
-constexpr int kRowB = kKS * 2 + 16;  // LDS bytes per staged row
-
-template <int MT, int NC>
-struct Tile {
-  static constexpr int WM = MT / 32, WN = NC / 32, NW = WM * WN, NTH = NW * 64;
-  static constexpr int CH = kKS / 8;               // 16-byte chunks per staged row
-  static constexpr int PX = MT * CH / NTH;         // x chunks per thread per stage
-  static constexpr int PW = NC * CH / NTH;         // w chunks per thread per stage
-  static constexpr int STAGE = (MT + NC) * kRowB;  // LDS bytes per stage
-  static constexpr int TP = NC + 4;                // fp32 epilogue tile pitch (floats)
-  static_assert(PX * NTH == MT * CH && PW * NTH == NC * CH, "stage chunks must divide evenly");
-  static_assert(MT * TP * 4 <= 2 * STAGE, "epilogue tile must fit in the staging LDS");
-};
-
 enum class Epi { Plain, Gelu, Residual, SwiGLU, QkvRope };
 
-template <int MT, int NC, Epi E, typename TO>
-__global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(LinearArgs a, RopeFreqs fr) {
-  using TL = Tile<MT, NC>;
-  __shared__ __attribute__((aligned(16))) char lds[2 * TL::STAGE];
-  const int n0 = blockIdx.x * NC, m0 = blockIdx.y * MT;
-  const int M = a.M, K = a.K;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % TL::WM, wn = wave / TL::WM;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const bf16* __restrict__ x = a.x;
-  const bf16* __restrict__ w = a.w;
-
-  struct Stage {
-    u32x4 x[TL::PX];
-    u32x4 w[TL::PW];
-  };
-  // chunk u of a stage: row u / CH, 16-byte chunk u % CH (16 consecutive lanes
-  // read one contiguous 256-byte row segment); rows past M repeat row M-1.
-  // Buffer loads: each thread's byte offsets within the tile's rows stay in
-  // VGPRs for the whole K loop and a stage adds its k offset as a scalar, so
-  // no address registers are rebuilt per stage (rebuilt 64-bit addresses land
-  // in registers of loads still in flight and force waits for them).  Each
-  // resource covers the tile's rows exactly.
-  // x rows follow the row map (the host keeps x below 2^30 bytes); w rows of
-  // the tile are rows n0 .. n0+NC-1, or for SwiGLU gate rows n0/2 .. in the
-  // first half of the tile and up rows n0/2 .. in the second.  A stage-load
-  // slot j covers NTH/16 whole rows, so the halves fall on whole slots.
-  uint32_t xo[TL::PX], wo[TL::PW];
-#pragma unroll
-  for (int j = 0; j < TL::PX; ++j) {
-    const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-    const int mm = min(m0 + r, M - 1);
-    xo[j] = (uint32_t)(((int64_t)(mm / a.rpg) * a.xgs + (int64_t)(mm % a.rpg) * a.xrs + 8 * c) * 2);
-  }
-  constexpr bool GLU = (E == Epi::SwiGLU);
-#pragma unroll
-  for (int j = 0; j < TL::PW; ++j) {
-    const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-    const int rr = (GLU && j >= TL::PW / 2) ? r - NC / 2 : r;
-    wo[j] = (uint32_t)(rr * K + 8 * c) * 2u;
-  }
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(x), (short)0, (int)a.x_bytes, 0x00020000);
-  const int wrow0 = GLU ? n0 / 2 : n0, wrows = GLU ? NC / 2 : NC;
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(w + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t wr2 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>((GLU ? a.w2 : w) + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
-  auto load = [&](int s, Stage& R) {
-    const int ko = s * kKS * 2;  // uniform byte offset of the stage
-#pragma unroll
-    for (int j = 0; j < TL::PX; ++j)
-      R.x[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)xo[j], ko, 0));
-#pragma unroll
-    for (int j = 0; j < TL::PW; ++j)
-      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             (GLU && j >= TL::PW / 2) ? wr2 : wr, (int)wo[j], ko, 0));
-  };
-  auto commit = [&](const Stage& R, int b) {
-    char* base = lds + b * TL::STAGE;
-#pragma unroll
-    for (int j = 0; j < TL::PX; ++j) {
-      const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-      *reinterpret_cast<u32x4*>(base + r * kRowB + 16 * c) = R.x[j];
-    }
-#pragma unroll
-    for (int j = 0; j < TL::PW; ++j) {
-      const int u = tid + j * TL::NTH, r = u / TL::CH, c = u % TL::CH;
-      *reinterpret_cast<u32x4*>(base + (MT + r) * kRowB + 16 * c) = R.w[j];
-    }
-  };
-  f32x16 acc = f32x16{};
-  // lane (l32, hh) holds row l32 of its 32-row block, k 8hh .. 8hh+7 of each 16-k step
-  auto compute = [&](int b) {
-    const char* base = lds + b * TL::STAGE;
-    const char* pa = base + (32 * wm + l32) * kRowB + 16 * hh;
-    const char* pb = base + (MT + 32 * wn + l32) * kRowB + 16 * hh;
-#pragma unroll
-    for (int kk = 0; kk < kKS / 16; ++kk) {
-      const bf16x8 A = *reinterpret_cast<const bf16x8*>(pa + 32 * kk);
-      const bf16x8 B = *reinterpret_cast<const bf16x8*>(pb + 32 * kk);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
-    }
-  };
-
-  // Every load is unconditional (past the last stage it repeats the last
-  // stage, which the caches hold): with conditional loads the compiler cannot
-  // count the loads in flight across the branch and waits for all of them
-  // before each commit, which leaves one stage in flight instead of two.
-  const int nk = K / kKS, last = nk - 1;
-  Stage R0, R1;
-  load(0, R0);
-  load(min(1, last), R1);
-  commit(R0, 0);
-  __syncthreads();
-  for (int s = 0; s < nk; s += 2) {
-    load(min(s + 2, last), R0);
-    compute(0);
-    commit(R1, 1);
-    __syncthreads();
-    if (s + 1 >= nk) break;
-    load(min(s + 3, last), R1);
-    compute(1);
-    commit(R0, 0);
-    __syncthreads();
-  }
-
-  // ---- epilogue: the fp32 tile through LDS (the last loop step ended with a barrier)
-  float* tile = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
-    tile[(32 * wm + i) * TL::TP + 32 * wn + l32] = acc[r];
-  }
-  __syncthreads();
-
+// Epilogue from the fp32 tile parked in LDS (pitch TP floats): whole 16-byte
+// chunks of y, or of q, k, v for the fused projection.
+template <int MT, int NC, Epi E, typename TO, int TP>
+__device__ __forceinline__ void epilogue(const LinearArgs& a, const RopeFreqs& fr, const float* tile,
+                                         int n0, int m0, int tid, int NTH) {
+  const int M = a.M;
   if constexpr (E == Epi::Plain || E == Epi::Gelu || E == Epi::Residual) {
     constexpr int C8 = NC / 8;
-    for (int u = tid; u < MT * C8; u += TL::NTH) {
+    for (int u = tid; u < MT * C8; u += NTH) {
       const int r = u / C8, c8 = u % C8, m = m0 + r;
       if (m >= M) continue;
       float v8[8];
-      load8(tile + r * TL::TP + 8 * c8, v8);
+      load8(tile + r * TP + 8 * c8, v8);
       if (a.bias) {
         float b8[8];
         load8(a.bias + n0 + 8 * c8, b8);
@@ -186,12 +65,12 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
     // tile columns 0 .. NC/2-1 are gate features n0/2 .., NC/2 .. NC-1 the same up features
     constexpr int C8 = NC / 16;
     const int F = a.N / 2;
-    for (int u = tid; u < MT * C8; u += TL::NTH) {
+    for (int u = tid; u < MT * C8; u += NTH) {
       const int r = u / C8, c8 = u % C8, m = m0 + r;
       if (m >= M) continue;
       float g8[8], u8[8];
-      load8(tile + r * TL::TP + 8 * c8, g8);
-      load8(tile + r * TL::TP + NC / 2 + 8 * c8, u8);
+      load8(tile + r * TP + 8 * c8, g8);
+      load8(tile + r * TP + NC / 2 + 8 * c8, u8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) g8[e] = g8[e] / (1.0f + __expf(-g8[e])) * u8[e];
       store8((bf16*)a.y + (size_t)m * F + n0 / 2 + 8 * c8, g8);
@@ -202,12 +81,12 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
     const int part = n0 / HD, nb = n0 - part * HD;  // 0: q, 1: k, 2: v; column of the head
     const bf16* bias = part == 0 ? a.b_q : (part == 2 ? a.b_v : nullptr);
     bf16* dst = part == 0 ? a.q : (part == 1 ? a.k : a.v);
-    for (int u = tid; u < MT * 4; u += TL::NTH) {
+    for (int u = tid; u < MT * 4; u += NTH) {
       const int r = u >> 2, pc = u & 3, m = m0 + r;
       if (m >= M) continue;
       float xs[8], ys[8];  // dims 8pc .. 8pc+7 and their partners 32+8pc ..
-      load8(tile + r * TL::TP + 8 * pc, xs);
-      load8(tile + r * TL::TP + 32 + 8 * pc, ys);
+      load8(tile + r * TP + 8 * pc, xs);
+      load8(tile + r * TP + 32 + 8 * pc, ys);
       if (bias) {
         float bx[8], by[8];
         load8(bias + nb + 8 * pc, bx);
@@ -236,10 +115,169 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
   }
 }
 
+// ---- main loop ---------------------------------------------------------------
+// Stage loads go straight from global memory into LDS (buffer_load ... lds:
+// lane i of a load writes 16 bytes at the wave's LDS base + 16 i): no staging
+// registers and no LDS write instructions.  Three stages live in LDS, two in
+// flight while one is computed.
+//
+// Stage layout: rows 0 .. MT-1 are x rows, MT .. MT+NC-1 w rows, KS k each
+// (CH = KS/8 chunks of 16 bytes), unpadded.  Load j of wave w fills the RPI =
+// 64/CH rows RPI (j NW + w) .. +RPI-1; its lane l fills row RPI (j NW + w) +
+// l/CH, slot l%CH with the row's chunk (l%CH) ^ swz(row).  The MFMA operand
+// reads (16 consecutive rows, one chunk) then hit distinct banks, with the
+// LDS serving 16 lanes per cycle from 64 banks or 8 lanes from 32:
+//   CH 8  (128-byte rows): swz(r) = (r ^ r/8) % 8, distinct (r%2, slot) over
+//         16 consecutive rows and distinct slots over 8;
+//   CH 16 (256-byte rows): swz(r) = r % 16, distinct slots over 16 rows and
+//         distinct slots mod 8 over 8.
+constexpr int kDStages = 3;
+
+template <int CH>
+__device__ __forceinline__ int dl_swz(int r) {
+  if constexpr (CH == 8)
+    return (r ^ (r >> 3)) & 7;
+  else
+    return r & 15;
+}
+
+template <int MT, int NC, int KS>
+struct Tile {
+  static constexpr int WM = MT / 32, WN = NC / 32, NW = WM * WN, NTH = NW * 64;
+  static constexpr int CH = KS / 8, RPI = 64 / CH, ROWB = KS * 2;
+  static constexpr int ROWS = MT + NC;
+  static constexpr int STAGE = ROWS * ROWB;
+  static constexpr int NLD = ROWS * CH / NTH;  // 16-byte loads per thread per stage
+  static constexpr int XLD = MT * CH / NTH;    // the first XLD of them are x rows
+  static constexpr int TP = NC + 4;
+  static_assert(CH == 8 || CH == 16, "stages of 64 or 128 k");
+  static_assert(NLD * NTH == ROWS * CH && XLD * NTH == MT * CH, "row groups must divide evenly");
+  static_assert((MT + NC / 2) % (RPI * NW) == 0, "each load takes x, gate or up rows only");
+  static_assert(MT * TP * 4 <= kDStages * STAGE, "epilogue tile must fit in the staging LDS");
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from a buffer into LDS at dst + 16 * lane.  (Called from
+// the kernel's lambdas through this device function: written in a lambda the
+// builtin stops the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt N, expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MT, int NC, int KS, Epi E, typename TO>
+__global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(LinearArgs a, RopeFreqs fr) {
+  using TL = Tile<MT, NC, KS>;
+  constexpr int CH = TL::CH, RPI = TL::RPI;
+  __shared__ __attribute__((aligned(16))) char lds[kDStages * TL::STAGE];
+  const int n0 = blockIdx.x * NC, m0 = blockIdx.y * MT;
+  const int M = a.M, K = a.K;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % TL::WM, wn = wave / TL::WM;
+  const int l32 = lane & 31, hh = lane >> 5;
+  constexpr bool GLU = (E == Epi::SwiGLU);
+
+  // per-load source byte offsets (loop-invariant); rows past M repeat row M-1
+  uint32_t vo[TL::NLD];
+#pragma unroll
+  for (int j = 0; j < TL::NLD; ++j) {
+    const int r = RPI * (j * TL::NW + wave) + lane / CH;
+    const int c = (lane % CH) ^ dl_swz<CH>(r);
+    if (j < TL::XLD) {
+      const int mm = min(m0 + r, M - 1);
+      vo[j] = (uint32_t)(((int64_t)(mm / a.rpg) * a.xgs + (int64_t)(mm % a.rpg) * a.xrs + 8 * c) * 2);
+    } else {
+      const int rw = r - MT;
+      const int rr = (GLU && rw >= NC / 2) ? rw - NC / 2 : rw;
+      vo[j] = (uint32_t)(rr * K + 8 * c) * 2u;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(a.x), (short)0, (int)a.x_bytes, 0x00020000);
+  const int wrow0 = GLU ? n0 / 2 : n0, wrows = GLU ? NC / 2 : NC;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(a.w + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>((GLU ? a.w2 : a.w) + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
+
+  auto issue = [&](int s, int b) {
+    const int ko = s * KS * 2;  // uniform byte offset of the stage
+    char* base = lds + b * TL::STAGE;
+#pragma unroll
+    for (int j = 0; j < TL::NLD; ++j) {
+      char* dst = base + 1024 * (j * TL::NW + wave);
+      if (j < TL::XLD)
+        lds_load16(xr, dst, vo[j], ko);
+      else if (GLU && RPI * (j * TL::NW) >= MT + NC / 2)
+        lds_load16(wr2, dst, vo[j], ko);
+      else
+        lds_load16(wr, dst, vo[j], ko);
+    }
+  };
+  f32x16 acc = f32x16{};
+  auto compute = [&](int b) {
+    const char* base = lds + b * TL::STAGE;
+    const int ra = 32 * wm + l32, rb = MT + 32 * wn + l32;
+    const char* pa = base + ra * TL::ROWB;
+    const char* pb = base + rb * TL::ROWB;
+    const int sa = dl_swz<CH>(ra), sb = dl_swz<CH>(rb);
+#pragma unroll
+    for (int kk = 0; kk < KS / 16; ++kk) {
+      const int ch = 2 * kk + hh;
+      const bf16x8 A = *reinterpret_cast<const bf16x8*>(pa + 16 * (ch ^ sa));
+      const bf16x8 B = *reinterpret_cast<const bf16x8*>(pb + 16 * (ch ^ sb));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+    }
+  };
+
+  const int nk = K / KS;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int s = 0; s < nk; ++s) {
+    // stage s landed for this wave (stage s+1 may still be in flight), then
+    // for every wave; the barrier also ends every wave's reads of stage s-1,
+    // whose buffer the loads of stage s+2 reuse
+    if (s + 1 < nk)
+      wait_vmcnt<TL::NLD>();
+    else
+      wait_vmcnt<0>();
+    // A plain barrier: __syncthreads() also orders this wave's memory
+    // operations, which makes the compiler wait for every load in flight,
+    // including the next stage's.  The wait above covers what the barrier
+    // must publish; the asm statement keeps the compiler's LDS accesses on
+    // their side of it.
+    __asm__ volatile("s_barrier" ::: "memory");
+    if (s + 2 < nk) issue(s + 2, (s + 2) % kDStages);
+    compute(s % kDStages);
+  }
+  __syncthreads();  // every wave is done reading the stages
+
+  float* tile = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
+    tile[(32 * wm + i) * TL::TP + 32 * wn + l32] = acc[r];
+  }
+  __syncthreads();
+  epilogue<MT, NC, E, TO, TL::TP>(a, fr, tile, n0, m0, tid, TL::NTH);
+}
+
 template <int MT, int NC, Epi E, typename TO>
 hipError_t launch_tile(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st) {
   const dim3 grid((unsigned)(a.N / NC), (unsigned)((a.M + MT - 1) / MT));
-  hipLaunchKernelGGL((linear_kernel<MT, NC, E, TO>), grid, dim3(Tile<MT, NC>::NTH), 0, st, a, fr);
+  // 64-wide stages keep three 64 x 64 stages at 48 KB; the two-wave 64 x 32
+  // tiles take 128-wide stages (half the barriers) at 72 KB
+  constexpr int KS = NC >= 64 ? 64 : 128;
+  hipLaunchKernelGGL((linear_kernel<MT, NC, KS, E, TO>), grid, dim3(Tile<MT, NC, KS>::NTH), 0, st, a, fr);
   return hipGetLastError();
 }
 
