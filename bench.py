@@ -301,6 +301,9 @@ def main():
     s_stem_bytes = (sdm * 3 * snm * 2 + sS * sF * snm * 2 + sS * 2 * sn * sdm * 2  # conv1
                     + sdm * 3 * sdm * 2 + sS * sF * sdm * 2 + sM * sdm * 4          # conv2
                     + 2 * sS * 2 * (snm + sdm) * 2 + 2 * 2 * sdm)                   # shift, biases
+    # per layer: each RMSNorm reads x and writes h; the output and down
+    # projections read their weights and inputs and update x (read + write);
+    # the split products' partial sums stay out (an implementation choice)
     s_layer_bytes = (2 * (sM * sdm * 4 + sM * sdm * 2 + sdm * 2)                    # two RMSNorms
                      + qkv_bytes + stream_bytes(sS, sn, sH, cs["W"])                # attention
                      + sdm * sHD * 2 + sM * sHD * 2 + 2 * sM * sdm * 4 + sdm * 2   # out proj
@@ -532,7 +535,7 @@ def main():
         "workload": f"whole streaming encoder step S{sS} x {2 * sn} mel frames -> {sn} frames: "
                     f"causal conv stem ({snm}->{sdm} k3 s1, {sdm}->{sdm} k3 s2, GELU) + {sL} "
                     f"pre-norm layers (d_model {sdm}, H{sH} D64 W{cs['W']}, SwiGLU FFN {sffn}), "
-                    f"bf16 weights/activations, float32 residual, {3 + 7 * sL} launches",
+                    f"bf16 weights/activations, float32 residual, {4 + 7 * sL} launches",
         "us_per_step": round(encs_us, 3),
         "encoder_frames_per_s": round(sM / (encs_us * 1e-6), 1),
         "audio_s_per_s": round(sS * 0.08 / (encs_us * 1e-6), 1),

@@ -324,14 +324,16 @@ typedef struct {
   const void *b_down; /* [d_model] or NULL */
 } vx_enc_layer_weights;
 
-/* Caller-owned bf16 work buffers of a layer step (reused by every layer). */
+/* Caller-owned work buffers of a layer step (reused by every layer). */
 typedef struct {
-  void *h; /* [S*n, d_model] normalised state */
-  void *q; /* [S*n, H*64] rotated queries */
-  void *k; /* [S*n, H*64] rotated keys */
-  void *v; /* [S*n, H*64] values */
-  void *o; /* [S*n, H*64] attention output */
-  void *u; /* [S*n, ffn] SwiGLU hidden state */
+  void *h;   /* [S*n, d_model] bf16 normalised state */
+  void *q;   /* [S*n, H*64] bf16 rotated queries */
+  void *k;   /* [S*n, H*64] bf16 rotated keys */
+  void *v;   /* [S*n, H*64] bf16 values */
+  void *o;   /* [S*n, H*64] bf16 attention output */
+  void *u;   /* [S*n, ffn] bf16 SwiGLU hidden state */
+  void *acc; /* [2, S*n, d_model] float32 partial sums of the projections
+                added into the residual (K split in two parts) */
 } vx_enc_work;
 
 /* y = x / sqrt(mean(x^2) + eps) * g per row: x float32 [M, dim], g bf16
@@ -354,8 +356,11 @@ vx_status vx_enc_stem_step(void *mel_buf, void *c1_buf, const vx_enc_stem_weight
                            float *x_out, int32_t S, int32_t n, int32_t n_mels, int32_t d_model,
                            void *stream);
 
-/* One pre-norm layer for one step, seven launches on `stream`, updating the
- * residual x [S, n, d_model] float32 in place.  ring_k, ring_v [S, H, W, 64]
+/* One pre-norm layer for one step, eight launches on `stream`, updating the
+ * residual x [S, n, d_model] float32 in place.  The output and down
+ * projections each run as two K halves whose fp32 sums a row-wise reduction
+ * adds, in order, with the bias into x; the reduction after the output
+ * projection also writes the FFN's normalised state.  ring_k, ring_v [S, H, W, 64]
  * bf16 rotated keys and values of this layer; frame i of stream s is at
  * position pos_in[s] + i; the call appends the new keys and values and sets
  * pos_out[s] = pos_in[s] + n (distinct arrays).  Requires 1 <= n <=
@@ -370,8 +375,10 @@ vx_status vx_enc_layer_step(float *x, const vx_enc_layer_weights *w, void *ring_
 /* A whole encoder step: vx_enc_stem_step into x, then layers[0 .. L-1] in
  * order as vx_enc_layer_step, layer l on rings ring_k + l*S*H*W*64 (ring_k,
  * ring_v [L, S, H, W, 64] bf16); all layers read positions pos_in and write
- * pos_out.  3 + 7L launches on `stream`; 1 <= L <= 4096.  Same buffer
- * rules as the two calls above. */
+ * pos_out.  The last reduction of layer l also writes layer l+1's normalised
+ * input, so the result equals the calls made one by one, bit for bit, in
+ * 3 + 1 + 7L launches on `stream`; 1 <= L <= 4096, d_model <= 4096.  Same
+ * buffer rules as the two calls above. */
 vx_status vx_enc_step(void *mel_buf, void *c1_buf, const vx_enc_stem_weights *stem,
                       const vx_enc_layer_weights *layers, int32_t L, void *ring_k, void *ring_v,
                       const int64_t *pos_in, int64_t *pos_out, float *x, const vx_enc_work *work,

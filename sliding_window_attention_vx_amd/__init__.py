@@ -58,7 +58,7 @@ _i64 = ctypes.c_int64
 STEM_KEYS = ("w1", "b1", "w2", "b2")
 LAYER_KEYS = ("g_attn", "w_qkv", "b_q", "b_v", "w_o", "b_o", "g_ffn", "w_gate", "w_up", "w_down",
               "b_down")
-WORK_KEYS = ("h", "q", "k", "v", "o", "u")
+WORK_KEYS = ("h", "q", "k", "v", "o", "u", "acc")
 
 
 class _StemW(ctypes.Structure):
@@ -633,12 +633,15 @@ def rmsnorm(x, g, eps=1e-5, out=None):
 
 
 def enc_work(S, n, H, d_model, ffn, device="cuda"):
-    """Work buffers of a layer step (dict of bf16 tensors h, q, k, v, o, u)."""
+    """Work buffers of a layer step: bf16 h, q, k, v, o, u and the float32
+    partial sums acc [2, S*n, d_model]."""
     import torch
     M = S * n
     shapes = dict(h=(M, d_model), q=(M, H * HEAD_DIM), k=(M, H * HEAD_DIM), v=(M, H * HEAD_DIM),
                   o=(M, H * HEAD_DIM), u=(M, ffn))
-    return {k: torch.empty(v, dtype=torch.bfloat16, device=device) for k, v in shapes.items()}
+    work = {k: torch.empty(v, dtype=torch.bfloat16, device=device) for k, v in shapes.items()}
+    work["acc"] = torch.empty((2, M, d_model), dtype=torch.float32, device=device)
+    return work
 
 
 def _stem_struct(stem):
@@ -667,9 +670,13 @@ def _layer_struct(w, H, dm, ffn):
 
 
 def _work_struct(work, S, n, H, dm, ffn, device):
+    import torch
     work = dict(work) if work is not None else enc_work(S, n, H, dm, ffn, device)
-    for k in WORK_KEYS:
+    for k in WORK_KEYS[:-1]:
         _bf16_dev(work[k], k)
+    _dev_tensor(work["acc"], "acc")
+    if work["acc"].dtype != torch.float32 or work["acc"].numel() < 2 * S * n * dm:
+        raise ValueError("work['acc'] must be float32 with 2 * S * n * d_model elements")
     return work, _Work(*[_ptr(work[k]) for k in WORK_KEYS])
 
 

@@ -27,7 +27,7 @@ namespace vx {
 
 namespace {
 
-enum class Epi { Plain, Gelu, Residual, SwiGLU, QkvRope };
+enum class Epi { Plain, Gelu, Residual, SwiGLU, Partial, QkvRope };
 
 // Epilogue from the fp32 tile parked in LDS (pitch TP floats): whole 16-byte
 // chunks of y, or of q, k, v for the fused projection.
@@ -35,7 +35,18 @@ template <int MT, int NC, Epi E, typename TO, int TP>
 __device__ __forceinline__ void epilogue(const LinearArgs& a, const RopeFreqs& fr, const float* tile,
                                          int n0, int m0, int tid, int NTH) {
   const int M = a.M;
-  if constexpr (E == Epi::Plain || E == Epi::Gelu || E == Epi::Residual) {
+  if constexpr (E == Epi::Partial) {
+    // this K part's fp32 sums, dense [M, N] at part blockIdx.z
+    constexpr int C8 = NC / 8;
+    float* yz = (float*)a.y + (size_t)blockIdx.z * M * a.N;
+    for (int u = tid; u < MT * C8; u += NTH) {
+      const int r = u / C8, c8 = u % C8, m = m0 + r;
+      if (m >= M) continue;
+      float v8[8];
+      load8(tile + r * TP + 8 * c8, v8);
+      store8(yz + (size_t)m * a.N + n0 + 8 * c8, v8);
+    }
+  } else if constexpr (E == Epi::Plain || E == Epi::Gelu || E == Epi::Residual) {
     constexpr int C8 = NC / 8;
     for (int u = tid; u < MT * C8; u += NTH) {
       const int r = u / C8, c8 = u % C8, m = m0 + r;
@@ -204,13 +215,15 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16*>(a.x), (short)0, (int)a.x_bytes, 0x00020000);
   const int wrow0 = GLU ? n0 / 2 : n0, wrows = GLU ? NC / 2 : NC;
+  // K part of this workgroup (Partial: gridDim.z parts of nk stages each)
+  const int nk = K / KS / (int)gridDim.z, kz0 = (int)blockIdx.z * nk;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16*>(a.w + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wr2 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16*>((GLU ? a.w2 : a.w) + (size_t)wrow0 * K), (short)0, wrows * K * 2, 0x00020000);
 
   auto issue = [&](int s, int b) {
-    const int ko = s * KS * 2;  // uniform byte offset of the stage
+    const int ko = (s + kz0) * KS * 2;  // uniform byte offset of the stage
     char* base = lds + b * TL::STAGE;
 #pragma unroll
     for (int j = 0; j < TL::NLD; ++j) {
@@ -239,7 +252,6 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
     }
   };
 
-  const int nk = K / KS;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
   for (int s = 0; s < nk; ++s) {
@@ -273,7 +285,8 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
 
 template <int MT, int NC, Epi E, typename TO>
 hipError_t launch_tile(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st) {
-  const dim3 grid((unsigned)(a.N / NC), (unsigned)((a.M + MT - 1) / MT));
+  const unsigned parts = E == Epi::Partial ? (unsigned)a.splits : 1u;
+  const dim3 grid((unsigned)(a.N / NC), (unsigned)((a.M + MT - 1) / MT), parts);
   // 64-wide stages keep three 64 x 64 stages at 48 KB; the two-wave 64 x 32
   // tiles take 128-wide stages (half the barriers) at 72 KB
   constexpr int KS = NC >= 64 ? 64 : 128;
@@ -302,6 +315,8 @@ hipError_t launch_linear(const LinearArgs& a, DT out, hipStream_t st, LinEpi epi
       return launch_epi<Epi::Residual, float>(a, st);
     case LinEpi::SwiGLU:
       return launch_epi<Epi::SwiGLU, bf16>(a, st);
+    case LinEpi::Partial:
+      return launch_epi<Epi::Partial, float>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -29,6 +29,9 @@ struct LinearArgs {
   // SwiGLU: w holds the gate rows, w2 the up rows (both [F, K]); N = 2F and
   // y [M, F] = silu(x w^T) * (x w2^T), bf16
   const bf16* w2 = nullptr;
+  // Partial: K is split in `splits` equal parts; part z writes its fp32 sum
+  // x[:, zK/splits ..) w[:, zK/splits ..)^T to y + z*M*N (dense [M, N])
+  int splits = 1;
   // q/k/v output (N = 3*HD): columns [0, HD) are q (+ b_q, rotated), [HD, 2HD)
   // k (rotated, no bias), [2HD, 3HD) v (+ b_v); row m sits at position
   // pos[m / n] + m % n; q, k, v are [M, HD] bf16.
@@ -41,7 +44,7 @@ struct LinearArgs {
   bf16* v = nullptr;
 };
 
-enum class LinEpi { Plain, Gelu, Residual, SwiGLU };
+enum class LinEpi { Plain, Gelu, Residual, SwiGLU, Partial };
 
 // Fills the row map of a dense [M, K] -> [M, N] product.
 inline void dense_rows(LinearArgs& a) {

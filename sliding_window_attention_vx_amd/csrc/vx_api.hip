@@ -929,6 +929,8 @@ vx_status check_layer_shape(const char* what, int32_t S, int32_t n, int32_t H, i
     return fail(VX_E_SHAPE, "%s: ffn (%d) must be a positive multiple of 128", what, ffn);
   if ((st = check_linear_shape(what, S * n, 2 * ffn, d_model))) return st;
   if ((st = check_linear_shape(what, S * n, d_model, ffn))) return st;
+  if (d_model > vx::kReduceMaxDim)
+    return fail(VX_E_SHAPE, "%s: d_model (%d) must be at most %d", what, d_model, vx::kReduceMaxDim);
   return VX_OK;
 }
 
@@ -945,7 +947,7 @@ vx_status check_layer_weights(const char* what, const vx_enc_layer_weights* w) {
 
 vx_status check_work(const char* what, const vx_enc_work* wk) {
   if (!wk) return fail(VX_E_NULL, "%s: work is NULL", what);
-  const void* al[] = {wk->h, wk->q, wk->k, wk->v, wk->o, wk->u};
+  const void* al[] = {wk->h, wk->q, wk->k, wk->v, wk->o, wk->u, wk->acc};
   for (const void* p : al) {
     if (!p) return fail(VX_E_NULL, "%s: a work buffer is NULL", what);
     if (!aligned16(p)) return fail(VX_E_ALIGN, "%s: work buffers must be 16-byte aligned", what);
@@ -966,16 +968,47 @@ void weight_regions(std::vector<Region>& r, const vx_enc_layer_weights* w, int H
   for (const Region& a : add) r.push_back(a);
 }
 
-// The seven launches of one pre-norm layer (arguments validated).
+// K parts of the output and down projections: two when the K stages split
+// evenly (every tile shape's stage divides 128), else one.
+int residual_splits(int K) { return K % (2 * vx::kLinKStep) == 0 ? 2 : 1; }
+
+// The product x w^T of a projection added into the residual stream: the K
+// parts' fp32 sums into acc, then x += sum + bias, and h = rmsnorm(x) * g_next
+// when g_next is given (the next product's input).
+vx_status residual_product(float* x, const vx::bf16* in, const vx::bf16* w, const vx::bf16* bias,
+                           int M, int N, int K, const vx_enc_work* wk, const vx::bf16* g_next,
+                           float eps, hipStream_t hs) {
+  vx::LinearArgs a{};
+  a.x = in;
+  a.w = w;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = wk->acc;
+  a.splits = residual_splits(K);
+  vx::dense_rows(a);
+  vx_status st;
+  if ((st = launched(vx::launch_linear(a, vx::DT::F32, hs, vx::LinEpi::Partial)))) return st;
+  return launched(vx::launch_residual_reduce(x, (const float*)wk->acc, a.splits, bias, g_next,
+                                             (vx::bf16*)wk->h, M, N, eps, hs));
+}
+
+// One pre-norm layer (arguments validated): [RMSNorm,] q/k/v + RoPE, the
+// attention step with the append, the output projection into the residual
+// with the FFN's RMSNorm, gate/up + SwiGLU, the down projection into the
+// residual, with h = rmsnorm(x) * g_next when g_next is given.  norm_in:
+// compute h = rmsnorm(x) * g_attn first; without it h must already hold that
+// (the previous layer's g_next).
 vx_status launch_layer(float* x, const vx_enc_layer_weights* w, void* ring_k, void* ring_v,
                        const int64_t* pos_in, int64_t* pos_out, const vx_enc_work* wk, int S,
                        int n, int H, int dm, int ffn, float eps, const vx_attn_cfg* cfg,
-                       const vx::RopeFreqs& fr, hipStream_t hs) {
+                       const vx::RopeFreqs& fr, bool norm_in, const void* g_next, hipStream_t hs) {
   const int M = S * n, HD = H * vx::kD;
   vx_status st;
   // 1. h = rmsnorm(x) * g_attn
-  if ((st = launched(vx::launch_rmsnorm(x, (const vx::bf16*)w->g_attn, (vx::bf16*)wk->h, M, dm,
-                                        eps, hs))))
+  if (norm_in &&
+      (st = launched(vx::launch_rmsnorm(x, (const vx::bf16*)w->g_attn, (vx::bf16*)wk->h, M, dm, eps,
+                                        hs))))
     return st;
   // 2. q', k' (rotated at pos_in[s] + i), v
   vx::LinearArgs a{};
@@ -1014,21 +1047,10 @@ vx_status launch_layer(float* x, const vx_enc_layer_weights* w, void* ring_k, vo
   sa.ring_v_w = ring_v;
   sa.pos_out = pos_out;
   if ((st = launched(vx::launch_stream_step(sa, vx::DT::BF16, vx::DT::BF16, fr, hs)))) return st;
-  // 4. x += o W_o^T + b_o
-  vx::LinearArgs b{};
-  b.x = (const vx::bf16*)wk->o;
-  b.w = (const vx::bf16*)w->w_o;
-  b.M = M;
-  b.N = dm;
-  b.K = HD;
-  b.bias = (const vx::bf16*)w->b_o;
-  b.y = x;
-  b.res = x;
-  vx::dense_rows(b);
-  if ((st = launched(vx::launch_linear(b, vx::DT::F32, hs, vx::LinEpi::Residual)))) return st;
-  // 5. h = rmsnorm(x) * g_ffn
-  if ((st = launched(vx::launch_rmsnorm(x, (const vx::bf16*)w->g_ffn, (vx::bf16*)wk->h, M, dm,
-                                        eps, hs))))
+  // 4-5. x += o W_o^T + b_o; h = rmsnorm(x) * g_ffn
+  if ((st = residual_product(x, (const vx::bf16*)wk->o, (const vx::bf16*)w->w_o,
+                             (const vx::bf16*)w->b_o, M, dm, HD, wk, (const vx::bf16*)w->g_ffn,
+                             eps, hs)))
     return st;
   // 6. u = silu(h W_gate^T) * (h W_up^T)
   vx::LinearArgs g{};
@@ -1041,18 +1063,10 @@ vx_status launch_layer(float* x, const vx_enc_layer_weights* w, void* ring_k, vo
   g.y = wk->u;
   vx::dense_rows(g);
   if ((st = launched(vx::launch_linear(g, vx::DT::BF16, hs, vx::LinEpi::SwiGLU)))) return st;
-  // 7. x += u W_down^T + b_down
-  vx::LinearArgs d{};
-  d.x = (const vx::bf16*)wk->u;
-  d.w = (const vx::bf16*)w->w_down;
-  d.M = M;
-  d.N = dm;
-  d.K = ffn;
-  d.bias = (const vx::bf16*)w->b_down;
-  d.y = x;
-  d.res = x;
-  vx::dense_rows(d);
-  return launched(vx::launch_linear(d, vx::DT::F32, hs, vx::LinEpi::Residual));
+  // 7. x += u W_down^T + b_down [; h = rmsnorm(x) * g_next]
+  return residual_product(x, (const vx::bf16*)wk->u, (const vx::bf16*)w->w_down,
+                          (const vx::bf16*)w->b_down, M, dm, ffn, wk,
+                          (const vx::bf16*)g_next, eps, hs);
 }
 
 }  // namespace
@@ -1146,6 +1160,7 @@ vx_status vx_enc_step(void* mel_buf, void* c1_buf, const vx_enc_stem_weights* st
   r.push_back({work->v, act, true});
   r.push_back({work->o, act, true});
   r.push_back({work->u, M * ffn * 2, true});
+  r.push_back({work->acc, 2 * M * d_model * 4, true});
   if (with_stem) {
     r.push_back({mel_buf, S * F * n_mels * 2, true});
     r.push_back({c1_buf, S * F * d_model * 2, true});
@@ -1161,11 +1176,13 @@ vx_status vx_enc_step(void* mel_buf, void* c1_buf, const vx_enc_stem_weights* st
   if (with_stem && (st = launch_stem(mel_buf, c1_buf, stem, x, S, n, n_mels, d_model, hs)))
     return st;
   const vx::RopeFreqs fr = rope_freqs(cfg->rope_theta);
+  // layer l > 0 takes its normalised input from layer l-1's last reduction
   for (int l = 0; l < L; ++l) {
     char* rk = (char*)ring_k + ring1 * l;
     char* rv = (char*)ring_v + ring1 * l;
+    const void* g_next = l + 1 < L ? layers[l + 1].g_attn : nullptr;
     if ((st = launch_layer(x, &layers[l], rk, rv, pos_in, pos_out, work, S, n, H, d_model, ffn,
-                           eps, cfg, fr, hs)))
+                           eps, cfg, fr, l == 0, g_next, hs)))
       return st;
   }
   return ok();
