@@ -107,6 +107,38 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
   const bf16* rv = a.ring_v + rbase;
   const bool rope = a.rope;
 
+  // blocks made only of ring keys: no mask except the window edge of later
+  // tokens, no new-token rotation
+  auto load_ring = [&](int kb, KvBlock& B) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        int slot = lo_slot + kb + 16 * sb + 4 * m + g;
+        if (slot >= W) slot -= W;
+        B.k[sb][m] = ring_load(rk + (size_t)slot * kGD + 8 * c);
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int slot = lo_slot + kb + 4 * j + g;
+      if (slot >= W) slot -= W;
+      B.v[j] = ring_load(rv + (size_t)slot * kGD + 8 * c);
+    }
+  };
+  // this wave's blocks [b0, b1): first the pure-ring ones [b0, bf), two
+  // register sets in turn so that one block's loads fly while the other
+  // computes, then the (at most two) blocks that hold new tokens or padding
+  const int nblk = (nk + 31) >> 5;
+  const int b0 = (int)((int64_t)wave * nblk / NW);
+  const int b1 = (int)((int64_t)(wave + 1) * nblk / NW);
+  const int nfull = nring >> 5;
+  const int bf = min(b1, max(b0, nfull));
+  const int edge = n - 1;  // ring keys kk < n-1 can fall out of a later token's window
+  // The first pure-ring block's loads go out before the cos/sin below (float64
+  // angles) so that the ring stream starts at once.
+  KvBlock B0, B1;
+  if (b0 < bf) load_ring(32 * b0, B0);
+
   if (rope) {
     for (int u = tid; u < n * kGHalf; u += NW * 64) {
       const int j = u / kGHalf, i = u % kGHalf;
@@ -154,24 +186,6 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
     qf[m + 2] = __builtin_bit_cast(bf16x8, y);
   }
 
-  // blocks made only of ring keys: no mask except the window edge of later
-  // tokens, no new-token rotation
-  auto load_ring = [&](int kb, KvBlock& B) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        int slot = lo_slot + kb + 16 * sb + 4 * m + g;
-        if (slot >= W) slot -= W;
-        B.k[sb][m] = ring_load(rk + (size_t)slot * kGD + 8 * c);
-      }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int slot = lo_slot + kb + 4 * j + g;
-      if (slot >= W) slot -= W;
-      B.v[j] = ring_load(rv + (size_t)slot * kGD + 8 * c);
-    }
-  };
   // any block: ring keys, new tokens (rotated here) and zero padding past nk
   auto load_any = [&](int kb, KvBlock& B) {
 #pragma unroll
@@ -310,18 +324,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_kernel(GqaDecodeArgs a, Ro
     __asm__ volatile("" ::: "memory");
   };
 
-  // this wave's blocks [b0, b1): first the pure-ring ones [b0, bf), two
-  // register sets in turn so that one block's loads fly while the other
-  // computes, then the (at most two) blocks that hold new tokens or padding
-  const int nblk = (nk + 31) >> 5;
-  const int b0 = (int)((int64_t)wave * nblk / NW);
-  const int b1 = (int)((int64_t)(wave + 1) * nblk / NW);
-  const int nfull = nring >> 5;
-  const int bf = min(b1, max(b0, nfull));
-  const int edge = n - 1;  // ring keys kk < n-1 can fall out of a later token's window
   if (b0 < bf) {
-    KvBlock B0, B1;
-    load_ring(32 * b0, B0);
     for (int bi = b0; bi < bf; bi += 2) {
       if (bi + 1 < bf) load_ring(32 * (bi + 1), B1);
       compute(B0, 32 * bi, 32 * bi < edge, true);

@@ -397,6 +397,42 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   const bf16* rv = (const bf16*)a.ring_v + rbase;
   const bool rope = a.rope;
 
+  // per-block loads: K A-operand rows (2 sub-blocks x 2 dim halves) and V rows
+  struct Blk {
+    u32x4 k[2][2];  // [sub-block][dim half]
+    u32x4 v[4];     // 4 x (8 rows x 16 bytes) of the 32 V rows
+  };
+  // blocks made only of ring keys (kb + 32 <= nring): unconditional loads.
+  // Keys load whole 128-byte rows like the values (k[sb][hf] holds rows
+  // 16sb + 8hf + lane/8, 16-byte chunk lane%8) and reach the A-operand layout
+  // through the wave's LDS rows: a lane's operand needs one key per lane%16,
+  // which would split every row over two load instructions.
+  auto load_ring = [&](int kb, Blk& B) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int slot = lo_slot + kb + 16 * sb + 8 * hf + (lane >> 3);
+        if (slot >= W) slot -= W;
+        B.k[sb][hf] = ring_row_load(rk + (size_t)slot * kD + 8 * (lane & 7));
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int slot = lo_slot + kb + 8 * j + (lane >> 3);
+      if (slot >= W) slot -= W;
+      B.v[j] = ring_row_load(rv + (size_t)slot * kD + 8 * (lane & 7));
+    }
+  };
+
+  // the keys' 32-key blocks are split into kSWaves contiguous runs, one per wave
+  const int nblk = (nk + 31) / 32;
+  const int b0 = wave * nblk / kSWaves, b1 = (wave + 1) * nblk / kSWaves;
+  // The first pure-ring block's loads go out before the cos/sin below (float64
+  // angles) so that the ring stream starts at once.
+  const int bf = min(b1, max(b0, nring >> 5));
+  Blk cur, nxt;
+  if (b0 < bf) load_ring(32 * b0, cur);
+
   // cos/sin of the new positions P .. P+i1-1 (float64 angle, as everywhere)
   if (rope) {
     for (int u = tid; u < i1 * kHalf; u += kSWaves * 64) {
@@ -438,11 +474,6 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
     qf[1] = __builtin_bit_cast(bf16x8, y);
   }
 
-  // per-block loads: K A-operand rows (2 sub-blocks x 2 dim halves) and V rows
-  struct Blk {
-    u32x4 k[2][2];  // [sub-block][dim half]
-    u32x4 v[4];     // 4 x (8 rows x 16 bytes) of the 32 V rows
-  };
   auto load_blk = [&](int kb, Blk& B) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -476,28 +507,6 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
     }
   };
 
-  // blocks made only of ring keys (kb + 32 <= nring): unconditional loads.
-  // Keys load whole 128-byte rows like the values (k[sb][hf] holds rows
-  // 16sb + 8hf + lane/8, 16-byte chunk lane%8) and reach the A-operand layout
-  // through the wave's LDS rows: a lane's operand needs one key per lane%16,
-  // which would split every row over two load instructions.
-  auto load_ring = [&](int kb, Blk& B) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        int slot = lo_slot + kb + 16 * sb + 8 * hf + (lane >> 3);
-        if (slot >= W) slot -= W;
-        B.k[sb][hf] = ring_row_load(rk + (size_t)slot * kD + 8 * (lane & 7));
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int slot = lo_slot + kb + 8 * j + (lane >> 3);
-      if (slot >= W) slot -= W;
-      B.v[j] = ring_row_load(rv + (size_t)slot * kD + 8 * (lane & 7));
-    }
-  };
-
   // tr16 read address: lane L of group g points at row 4g + L/4, dims 4*(L%4)
   const int v_off = (4 * g + (q >> 2)) * kSRowV + 4 * (q & 3) * 2;
   const float c2 = a.scale_log2;
@@ -507,9 +516,6 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   for (int db = 0; db < 4; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // the keys' 32-key blocks are split into kSWaves contiguous runs, one per wave
-  const int nblk = (nk + 31) / 32;
-  const int b0 = wave * nblk / kSWaves, b1 = (wave + 1) * nblk / kSWaves;
   // One block.  Only the first block (ring keys that leave the window of a
   // later query of the chunk: key index < 15) and the blocks past the ring
   // keys (new frames, padding) can hold masked keys; the others skip the mask.
@@ -608,11 +614,8 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
     __asm__ volatile("" ::: "memory");
   };
   // this wave's pure-ring blocks [b0, bf) with the next block's loads in
-  // flight while one computes, then the (at most two) blocks that hold new
-  // frames or padding
-  const int bf = min(b1, max(b0, nring >> 5));
-  Blk cur, nxt;
-  if (b0 < bf) load_ring(32 * b0, cur);
+  // flight while one computes (the first block's loads were issued at the
+  // start), then the (at most two) blocks that hold new frames or padding
   for (int bi = b0; bi < bf; ++bi) {
     if (bi + 1 < bf) load_ring(32 * (bi + 1), nxt);
     step(cur, bi, true);
