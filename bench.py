@@ -17,7 +17,9 @@ back-to-back launches on the launch stream.  The streaming step is reported
 in microseconds and GB/s of algorithmic HBM bytes.  The CPU baseline is the
 float64 oracle timed on the host on the same prefill workload.
 
-Beside the step, the same line reports the batched first-chunk prefill, the
+Beside the step, the same line reports the 32-layer attention stack (B4
+T1500 per layer) and the long-form prefill (B8 T6000), the batched first-chunk
+prefill, the
 text decoder's grouped-query attention (32 query / 8 key-value heads,
 head_dim 128, window 8192): one decode step of 64 streams over full 8192-slot
 rings (ring append fused) and a 16384-token prompt prefill, each with its
@@ -49,20 +51,20 @@ MEASURED_TRAFFIC = {
                 "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
                 21_649_408 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
-               "71bc428d942d578cac790a4e7a73817ee39e50bfdbfd7b0388e37b83138c833e",
-               396_091_691 + 3_146_731),
+               "95d1d5b13d35cc99fb57042be5d3a40dc6c347c74bdda9b9d02adc8f3e80c33a",
+               396_090_112 + 3_146_698),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
                     "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
                     156_001_485 + 107_364_352),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
-                   "013df8d5d4b9f64716f8f610e003b9359a3ca4ad75eb592a358e2865094e7ab4",
-                   2_148_391_125 + 786_944),
+                   "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",
+                   2_148_394_965 + 786_981),
     "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"),
-            "c8d2c9e2e93053cabe67b29c939a74c210ec2dd5189de35ce458ddc44358c4a3",
-            21_203_712 + 3_145_728),
+            "1e9826ec5eca0957949286babffadeab92eeb0fd37092cd66d13d72c566d4a98",
+            21_206_378 + 3_145_728),
     "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"),
-              "c8d2c9e2e93053cabe67b29c939a74c210ec2dd5189de35ce458ddc44358c4a3",
-              13_713_237 + 655_360),
+              "1e9826ec5eca0957949286babffadeab92eeb0fd37092cd66d13d72c566d4a98",
+              13_714_517 + 655_360),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
                     "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
                     450_898_048 + 134_419_720),
@@ -131,6 +133,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--enc-layers", type=int, default=None,
                     help="layers of the whole encoder step (default: the model's 32)")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 32-layer stack and long-form prefill legs (their inputs take "
+                         "about 30 s to draw on the host)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -211,6 +216,30 @@ def main():
     fc_bytes = (4 * fc_tot * fc["H"] * 128
                 + 2 * sum(min(int(t), fc["W"]) for t in fc_len) * fc["H"] * 128 + 8 * fc["S"])
     fc_slices = [(int(xf["cu"][i]), int(xf["cu"][i + 1])) for i in range(fc["S"])]
+
+    # ---- 32-layer attention stack (B4 T1500, fresh seeded Q/K/V per layer) and long-form
+    # prefill (B8 T6000, 1 % of key rows x8), both with fused RoPE
+    stack_in, long_in = [], None
+    if not args.no_stack and args.only is None:
+        stc, lgc = synth.CONFIGS["stack"], synth.CONFIGS["long"]
+        for l in range(stc.layers):
+            xx = synth.make_config("stack", layer=l)
+            stack_in.append((to(xx["q"]), to(xx["k"]), to(xx["v"])))
+        stack_o = torch.empty_like(stack_in[0][0])
+        xx = synth.make_config("long")
+        long_in = (to(xx["q"]), to(xx["k"]), to(xx["v"]))
+        del xx
+        long_o = torch.empty_like(long_in[0])
+        long_tab = vx.rope_table(0, lgc.T)
+        stack_flops = band_flops(stc.B, stc.T, stc.H, stc.W) * stc.layers
+        long_flops = band_flops(lgc.B, lgc.T, lgc.H, lgc.W)
+
+    def stack_pass(i):
+        for sq, sk, sv in stack_in:
+            vx.prefill(sq, sk, sv, window=stc.W, table=table, out=stack_o)
+
+    def long_pass(i):
+        vx.prefill(*long_in, window=lgc.W, table=long_tab, out=long_o)
 
     # ---- text decoder (grouped-query attention, head_dim 128)
     dc = synth.GQA_CONFIGS["dec_decode"]
@@ -417,6 +446,9 @@ def main():
     qkv_us = per_launch_us(qkv, reps)
     oproj_us = per_launch_us(oproj, reps)
     encs_us = per_launch_us(enc_step, max(K // 5, 5))
+    if stack_in:
+        stack_us = per_launch_us(stack_pass, max(K // 10, 3))
+        long_us = per_launch_us(long_pass, max(K // 5, 5))
     dec_us = per_launch_us(gqa_decode, reps)
     gpre_us = per_launch_us(gqa_prefill, max(K // 5, 5))
     gpre_fused_us = per_launch_us(gqa_prefill_fused, max(K // 5, 5))
@@ -529,6 +561,29 @@ def main():
                                             4),
                               "traffic": measured_traffic("oproj")},
     }
+
+    if stack_in:
+        stack_tf = stack_flops / (stack_us * 1e-6) / 1e12
+        long_tf = long_flops / (long_us * 1e-6) / 1e12
+        out["stack"] = {
+            "workload": f"{stc.layers} layers x prefill B{stc.B} T{stc.T} H{stc.H} D64 W{stc.W} bf16, "
+                        "fresh Q/K/V per layer, RoPE fused, one call per layer",
+            "us_per_stack": round(stack_us, 3),
+            "us_per_layer": round(stack_us / stc.layers, 3),
+            "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
+                         "achieved": round(stack_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(stack_tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+        }
+        out["long"] = {
+            "workload": f"prefill B{lgc.B} T{lgc.T} H{lgc.H} D64 W{lgc.W} bf16, 1 % of key rows x8, "
+                        "RoPE fused",
+            "us_per_call": round(long_us, 3),
+            "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
+                         "achieved": round(long_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(long_tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None},
+        }
 
     encs_gbs = s_bytes / (encs_us * 1e-6) / 1e9
     out["enc_step"] = {
