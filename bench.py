@@ -471,6 +471,33 @@ def main():
     qkv_us = per_launch_us(qkv, reps)
     oproj_us = per_launch_us(oproj, reps)
     encs_us = per_launch_us(enc_step, max(K // 5, 5))
+
+    # the same step captured as a HIP graph: two steps (the position arrays
+    # ping-pong), so every replay advances the streams like the eager loop
+    def enc_step_graph_us(replays):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            enc_step(0)
+            enc_step(1)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            s_state["c"] = 0
+            enc_step(0)
+            enc_step(1)
+        graph.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            graph.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3 / (2 * replays)
+
+    encs_graph_us = enc_step_graph_us(max(K // 10, 3))
     if stack_in:
         stack_us = per_launch_us(stack_pass, max(K // 10, 3))
         long_us = per_launch_us(long_pass, max(K // 5, 5))
@@ -618,6 +645,7 @@ def main():
                     f"pre-norm layers (d_model {sdm}, H{sH} D64 W{cs['W']}, SwiGLU FFN {sffn}), "
                     f"bf16 weights/activations, float32 residual, {4 + 7 * sL} launches",
         "us_per_step": round(encs_us, 3),
+        "us_per_step_graph": round(encs_graph_us, 3),
         "encoder_frames_per_s": round(sM / (encs_us * 1e-6), 1),
         "audio_s_per_s": round(sS * 0.08 / (encs_us * 1e-6), 1),
         "bytes_algorithmic": int(s_bytes),
