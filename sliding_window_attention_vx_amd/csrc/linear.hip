@@ -152,9 +152,10 @@ __device__ __forceinline__ int dl_swz(int r) {
     return r & 15;
 }
 
-template <int MT, int NC, int KS>
+template <int MT, int NC, int KS, int WB = 1>
 struct Tile {
-  static constexpr int WM = MT / 32, WN = NC / 32, NW = WM * WN, NTH = NW * 64;
+  // waves WM x WN, each WB 32 x 32 blocks side by side (32 x 32*WB outputs)
+  static constexpr int WM = MT / 32, WN = NC / (32 * WB), NW = WM * WN, NTH = NW * 64;
   static constexpr int CH = KS / 8, RPI = 64 / CH, ROWB = KS * 2;
   static constexpr int ROWS = MT + NC;
   static constexpr int STAGE = ROWS * ROWB;
@@ -184,9 +185,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int MT, int NC, int KS, Epi E, typename TO>
-__global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(LinearArgs a, RopeFreqs fr) {
-  using TL = Tile<MT, NC, KS>;
+template <int MT, int NC, int KS, int WB, Epi E, typename TO>
+__global__ __launch_bounds__((MT / 32) * (NC / 32 / WB) * 64) void linear_kernel(LinearArgs a, RopeFreqs fr) {
+  using TL = Tile<MT, NC, KS, WB>;
   constexpr int CH = TL::CH, RPI = TL::RPI;
   __shared__ __attribute__((aligned(16))) char lds[kDStages * TL::STAGE];
   const int n0 = blockIdx.x * NC, m0 = blockIdx.y * MT;
@@ -236,19 +237,25 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
         lds_load16(wr, dst, vo[j], ko);
     }
   };
-  f32x16 acc = f32x16{};
+  f32x16 acc[WB];
+#pragma unroll
+  for (int nb = 0; nb < WB; ++nb) acc[nb] = f32x16{};
   auto compute = [&](int b) {
     const char* base = lds + b * TL::STAGE;
-    const int ra = 32 * wm + l32, rb = MT + 32 * wn + l32;
+    const int ra = 32 * wm + l32;
     const char* pa = base + ra * TL::ROWB;
-    const char* pb = base + rb * TL::ROWB;
-    const int sa = dl_swz<CH>(ra), sb = dl_swz<CH>(rb);
+    const int sa = dl_swz<CH>(ra);
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
       const int ch = 2 * kk + hh;
       const bf16x8 A = *reinterpret_cast<const bf16x8*>(pa + 16 * (ch ^ sa));
-      const bf16x8 B = *reinterpret_cast<const bf16x8*>(pb + 16 * (ch ^ sb));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < WB; ++nb) {
+        const int rb = MT + 32 * (WB * wn + nb) + l32;
+        const bf16x8 B =
+            *reinterpret_cast<const bf16x8*>(base + rb * TL::ROWB + 16 * (ch ^ dl_swz<CH>(rb)));
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[nb], 0, 0, 0);
+      }
     }
   };
 
@@ -275,22 +282,25 @@ __global__ __launch_bounds__((MT / 32) * (NC / 32) * 64) void linear_kernel(Line
 
   float* tile = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
-    tile[(32 * wm + i) * TL::TP + 32 * wn + l32] = acc[r];
-  }
+  for (int nb = 0; nb < WB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
+      tile[(32 * wm + i) * TL::TP + 32 * (WB * wn + nb) + l32] = acc[nb][r];
+    }
   __syncthreads();
   epilogue<MT, NC, E, TO, TL::TP>(a, fr, tile, n0, m0, tid, TL::NTH);
 }
 
-template <int MT, int NC, Epi E, typename TO>
+template <int MT, int NC, Epi E, typename TO, int WB = 1>
 hipError_t launch_tile(const LinearArgs& a, const RopeFreqs& fr, hipStream_t st) {
   const unsigned parts = E == Epi::Partial ? (unsigned)a.splits : 1u;
   const dim3 grid((unsigned)(a.N / NC), (unsigned)((a.M + MT - 1) / MT), parts);
   // 64-wide stages keep three 64 x 64 stages at 48 KB; the two-wave 64 x 32
   // tiles take 128-wide stages (half the barriers) at 72 KB
   constexpr int KS = NC >= 64 ? 64 : 128;
-  hipLaunchKernelGGL((linear_kernel<MT, NC, KS, E, TO>), grid, dim3(Tile<MT, NC, KS>::NTH), 0, st, a, fr);
+  hipLaunchKernelGGL((linear_kernel<MT, NC, KS, WB, E, TO>), grid, dim3(Tile<MT, NC, KS, WB>::NTH), 0,
+                     st, a, fr);
   return hipGetLastError();
 }
 
@@ -301,6 +311,12 @@ hipError_t launch_epi(const LinearArgs& a, hipStream_t st) {
   const RopeFreqs fr{};
   // 64 x 64 tiles when they alone give every CU a workgroup, else 64 x 32
   const bool wide = a.N % 64 == 0 && (int64_t)(a.N / 64) * ((a.M + 63) / 64) >= 256;
+  // gate/up + SwiGLU over many columns: 64 x 128 tiles, each wave 32 x 64 (an
+  // A-operand read feeds two MFMAs, and half as many tiles re-read x)
+  if constexpr (E == Epi::SwiGLU) {
+    if (a.N % 128 == 0 && (int64_t)(a.N / 128) * ((a.M + 63) / 64) >= 256)
+      return launch_tile<64, 128, E, TO, 2>(a, fr, st);
+  }
   return wide ? launch_tile<64, 64, E, TO>(a, fr, st) : launch_tile<64, 32, E, TO>(a, fr, st);
 }
 
