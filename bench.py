@@ -60,11 +60,11 @@ MEASURED_TRAFFIC = {
                    "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",
                    2_148_394_965 + 786_981),
     "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"),
-            "1e9826ec5eca0957949286babffadeab92eeb0fd37092cd66d13d72c566d4a98",
-            21_206_378 + 3_145_728),
+            "ae016fb04b70096e287909df76377577f041d02b6a6932ec7cfbf8ecf1b0d73d",
+            21_202_517 + 3_145_728),
     "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"),
-              "1e9826ec5eca0957949286babffadeab92eeb0fd37092cd66d13d72c566d4a98",
-              13_714_517 + 655_360),
+              "ae016fb04b70096e287909df76377577f041d02b6a6932ec7cfbf8ecf1b0d73d",
+              13_718_698 + 655_360),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
                     "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
                     450_898_048 + 134_419_720),
