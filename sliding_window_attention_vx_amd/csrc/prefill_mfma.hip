@@ -79,6 +79,57 @@ __device__ __forceinline__ void v_unit(int u, int& r, int& c) {
   c = 4 * ((u >> 4) & 1) + (u & 3);
 }
 
+__device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, int hx, int cpx,
+                                          int& bh, int& qt) {
+  // Work order.  The dispatcher deals workgroups round-robin to the 8 XCDs
+  // (workgroup id mod 8), and each XCD has its own L2.  With at least 8
+  // (batch, head) pairs, XCD x owns pairs [x*hx, (x+1)*hx).  Its N = hx *
+  // n_qtiles tiles, ranked by work (the n_short leading query tiles, whose
+  // band is cut at key 0, shortest first, then the full-length ones pair by
+  // pair so that neighbouring tiles share K/V in its L2), are dealt to its
+  // cpx CUs as follows.
+  //  - N <= 2 cpx: the first cpx workgroups land one per CU and the other
+  //    R = N - cpx join CUs 0 .. R-1 in the same order; so the largest N - R
+  //    tiles go first in ascending order and the R smallest follow in
+  //    descending order: the largest of the late ones shares a CU with the
+  //    smallest of the early ones, which evens out the work per CU.
+  //  - larger grids: full-length tiles first, then the short ones longest
+  //    first, which arrive last and pair up with a long workgroup on a CU
+  //    that still has room.
+  // With fewer pairs every XCD takes query tiles of every pair, longest first.
+  if (hx > 0) {
+    const int i = blockIdx.x >> 3;
+    const int n_long = n_qtiles - n_short;
+    const int N = hx * n_qtiles;
+    int bl;
+    if (N <= 2 * cpx) {
+      const int R = max(N - cpx, 0);
+      const int k = i < N - R ? R + i : R - 1 - (i - (N - R));
+      if (k < hx * n_short) {
+        qt = k / hx;
+        bl = k % hx;
+      } else {
+        const int j = k - hx * n_short;
+        bl = j / n_long;
+        qt = n_short + j % n_long;
+      }
+    } else if (i < hx * n_long) {
+      bl = i / n_long;
+      qt = n_short + i % n_long;
+    } else {
+      const int j = i - hx * n_long;
+      qt = n_short - 1 - j / hx;
+      bl = j % hx;
+    }
+    bh = (blockIdx.x & 7) * hx + bl;
+  } else {
+    const int i = blockIdx.x;
+    qt = n_qtiles - 1 - i / n_bh;
+    bh = i % n_bh;
+  }
+  return bh < n_bh;
+}
+
 template <int NW>
 struct Stage {
   static constexpr int NT = NW * 64;
@@ -89,39 +140,87 @@ struct Stage {
   u32x4 v[UV];
 };
 
-// Global loads of the next tile into registers.  Rows at or past T are
-// clamped to T-1 instead of being skipped: their keys lie after every stored
-// query, so causality masks them, and the clamped values are finite.  The
-// loads are unconditional on purpose: conditional loads merged with zero fills
-// made the compiler copy the landing registers right after issuing them, which
-// waited for the loads and serialized the double buffering.
+// Global loads of the next tile into registers, as buffer loads: each tile's
+// rows get a descriptor (scalar registers) whose size ends at row T, so rows
+// at or past T read as zeros (their keys lie after every stored query and
+// causality masks them), and every thread keeps fixed byte offsets, so a
+// tile costs no vector address arithmetic.  A tile past the end (kt0 >= T)
+// gets an empty descriptor: its loads return zeros without touching memory.
+// Callers issue the loads unconditionally, past the last tile too: the wait
+// counters are counted per wave in issue order, and a load that is issued on
+// one path only makes the compiler wait for every load at the join.
 template <int NW>
-__device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
-                                           const bf16* __restrict__ v, size_t rs, int T, int kt0,
-                                           bool rope, const float* __restrict__ table,
-                                           int64_t row0, int tid) {
+struct StageOffs {
+  uint32_t k[Stage<NW>::UK], t[Stage<NW>::UK], v[Stage<NW>::UV];
+};
+
+template <int NW>
+__device__ __forceinline__ StageOffs<NW> stage_offsets(int tid, size_t rs) {
   constexpr int NT = Stage<NW>::NT;
+  const uint32_t rb = (uint32_t)(rs * sizeof(bf16));
+  StageOffs<NW> so;
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UK; ++j) {
     int r, cp;
     k_unit(tid + j * NT, r, cp);
-    const int key = min(kt0 + r, T - 1);
-    const bf16* kp = k + (size_t)key * rs + 8 * cp;
-    st.kx[j] = *reinterpret_cast<const u32x4*>(kp);
-    st.ky[j] = *reinterpret_cast<const u32x4*>(kp + kHalf);
-    if (rope) {
-      const float* cs = table + (row0 + key) * kD + 8 * cp;
-      load8(cs, st.kc[j]);
-      load8(cs + kHalf, st.ks[j]);
-    }
+    so.k[j] = r * rb + 16 * cp;
+    so.t[j] = r * (kD * 4) + 32 * cp;
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
     int r, c;
     v_unit(tid + j * NT, r, c);
-    const int key = min(kt0 + r, T - 1);
-    st.v[j] = *reinterpret_cast<const u32x4*>(v + (size_t)key * rs + 8 * c);
+    so.v[j] = r * rb + 16 * c;
   }
+  return so;
+}
+
+// Descriptor of nbytes at p; both are the same in every lane, and reading
+// them from lane 0 lets the compiler keep the descriptor in scalar registers
+// (a descriptor it cannot prove uniform costs a loop around every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, uint32_t nbytes) {
+  const uint64_t u = (uint64_t)p;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)nbytes),
+                                           0x00020000);
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
+                                           const bf16* __restrict__ v, size_t rs, int T, int kt0,
+                                           bool rope, const float* __restrict__ table,
+                                           int64_t row0, const StageOffs<NW>& so) {
+  const uint32_t nrows = (uint32_t)max(min(T - kt0, kBN), 0);
+  const uint32_t rb = (uint32_t)(rs * sizeof(bf16));
+  const auto kr = rows_rsrc(k + (size_t)kt0 * rs, nrows * rb);
+  const auto vr = rows_rsrc(v + (size_t)kt0 * rs, nrows * rb);
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UK; ++j) {
+    st.kx[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j], 0, 0);
+    st.ky[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j] + 2 * kHalf, 0, 0);
+    {
+      // without RoPE the table loads still go out, against an empty
+      // descriptor (zeros, no memory access), so the count of loads per tile
+      // does not depend on a runtime flag
+      const auto tr = rows_rsrc(table + (row0 + kt0) * kD, rope ? nrows * (kD * 4) : 0u);
+      const f32x4 c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j], 0, 0));
+      const f32x4 c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j] + 16, 0, 0));
+      const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j] + 4 * kHalf, 0, 0));
+      const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j] + 4 * kHalf + 16, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st.kc[j][e] = c0[e];
+        st.kc[j][4 + e] = c1[e];
+        st.ks[j][e] = s0[e];
+        st.ks[j][4 + e] = s1[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<NW>::UV; ++j)
+    st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, so.v[j], 0, 0);
 }
 
 // Ring seeding by the staging threads: the rotated key rows and value rows of
@@ -183,40 +282,12 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
 
 template <int NW, typename TO, bool SEED>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
-                                                                  int n_short, int hx) {
+                                                                  int n_short, int hx, int cpx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   constexpr int BM = NW * 32;
 
-  // Work order.  The dispatcher deals workgroups round-robin to the 8 XCDs
-  // (workgroup id mod 8), and each XCD has its own L2.  With at least 8
-  // (batch, head) pairs, XCD x owns pairs [x*hx, (x+1)*hx) and runs first
-  // their full-length query tiles, pair by pair so that neighbouring tiles
-  // share K/V in its L2, then the n_short leading query tiles, whose band is
-  // cut at key 0, longest first.  The short ones thus arrive last and pair up
-  // with a long workgroup on a CU that still has room, instead of two long
-  // workgroups sharing one CU.  With fewer pairs every XCD takes query tiles
-  // of every pair, in the same longest-first order.
-  const int n_bh = a.B * a.H;
   int bh, qt;
-  if (hx > 0) {
-    const int i = blockIdx.x >> 3;
-    const int n_long = n_qtiles - n_short;
-    int bl;
-    if (i < hx * n_long) {
-      bl = i / n_long;
-      qt = n_short + i % n_long;
-    } else {
-      const int j = i - hx * n_long;
-      qt = n_short - 1 - j / hx;
-      bl = j % hx;
-    }
-    bh = (blockIdx.x & 7) * hx + bl;
-    if (bh >= n_bh) return;
-  } else {
-    const int i = blockIdx.x;
-    qt = n_qtiles - 1 - i / n_bh;
-    bh = i % n_bh;
-  }
+  if (!work_item(a.B * a.H, n_qtiles, n_short, hx, cpx, bh, qt)) return;
   const int h = bh % a.H, b = bh / a.H;
 
   const int tid = threadIdx.x;
@@ -234,6 +305,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     if (SEED && h == 0 && qt == 0 && threadIdx.x == 0) a.pos_out[b] = T;
     if (qt * NW * 32 >= T) return;
   }
+  // T and row0 are the same in every lane; saying so keeps the buffer
+  // descriptors built from them in scalar registers
+  T = __builtin_amdgcn_readfirstlane(T);
+  row0 = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(row0 >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)row0);
   const int W = a.W;
   const size_t rs = (size_t)a.H * kD;
   const size_t base = row0 * rs + (size_t)h * kD;
@@ -247,6 +323,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const int qw = q0 + wave * 32;
   const int tq = qw + l32;  // this lane's query
 
+  const int kbeg = max(0, q0 - W + 1);
+  const int klast = min(T, q0 + BM) - 1;
+  const int it0 = kbeg / kBN, it1 = klast / kBN;
+
   // ---- Q' fragments (B operand of S^T = K' Q'^T) -------------------------
   // MFMA step m covers dims 16m .. 16m+15; lane half hh holds dims 16m+8hh+(0..7),
   // i.e. chunk 2m+hh of 8 dims.  Chunks c and c+4 are RoPE partners.
@@ -255,52 +335,68 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   // per-lane reads of a lane's own row would touch one 256-byte row per lane.
   // Rows are padded to kRowQT bytes so the per-lane LDS reads below hit
   // distinct banks.  The region is reused by the first K/V tile afterwards.
+  // The table rows, the raw query rows and the first K/V tile are all
+  // requested before the first wait, so their memory latencies overlap.
   constexpr int kRowQT = 4 * kD + 16;
+  constexpr int NT = NW * 64;
+  constexpr int NQT = BM * 16 / NT;  // table chunks per thread
   static_assert(BM * kRowQT <= 2 * kStageBytes, "Q table rows must fit in LDS");
+  u32x4 tq_rows[NQT];
   if (rope) {
-    constexpr int NT = NW * 64;
 #pragma unroll
-    for (int j = 0; j < BM * 16 / NT; ++j) {
+    for (int j = 0; j < NQT; ++j) {
       const int i = tid + j * NT;
       const int r = i >> 4, c = i & 15;
       const int row = min(q0 + r, T - 1);
-      const u32x4 val =
-          *reinterpret_cast<const u32x4*>(a.table + (a.table_row0 + row) * kD + 4 * c);
-      *reinterpret_cast<u32x4*>(lds + r * kRowQT + 16 * c) = val;
+      tq_rows[j] = *reinterpret_cast<const u32x4*>(a.table + (a.table_row0 + row) * kD + 4 * c);
+    }
+  }
+  u32x4 qx[2], qy[2];
+  {
+    const bf16* qp = q + (size_t)min(tq, T - 1) * rs;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int c = 2 * pr + hh;
+      qx[pr] = *reinterpret_cast<const u32x4*>(qp + 8 * c);
+      qy[pr] = *reinterpret_cast<const u32x4*>(qp + kHalf + 8 * c);
+    }
+  }
+  Stage<NW> st;
+  const StageOffs<NW> so = stage_offsets<NW>(tid, rs);
+  stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, so);
+  if (rope) {
+#pragma unroll
+    for (int j = 0; j < NQT; ++j) {
+      const int i = tid + j * NT;
+      *reinterpret_cast<u32x4*>(lds + (i >> 4) * kRowQT + 16 * (i & 15)) = tq_rows[j];
     }
     __syncthreads();
   }
   bf16x8 qf[4];
-  if (tq < T) {
-    const bf16* qp = q + (size_t)tq * rs;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      const int c = 2 * pr + hh;
-      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 8 * c);
-      u32x4 y = *reinterpret_cast<const u32x4*>(qp + kHalf + 8 * c);
-      if (rope) {
-        const float* cs = reinterpret_cast<const float*>(lds + (tq - q0) * kRowQT) + 8 * c;
-        float cc[8], ss[8], xf[8], yf[8];
-        load8(cs, cc);
-        load8(cs + kHalf, ss);
-        unpack8(x, xf);
-        unpack8(y, yf);
+  for (int pr = 0; pr < 2; ++pr) {
+    const int c = 2 * pr + hh;
+    u32x4 x = qx[pr], y = qy[pr];
+    if (rope) {
+      const float* cs = reinterpret_cast<const float*>(lds + (min(tq, T - 1) - q0) * kRowQT) + 8 * c;
+      float cc[8], ss[8], xf[8], yf[8];
+      load8(cs, cc);
+      load8(cs + kHalf, ss);
+      unpack8(x, xf);
+      unpack8(y, yf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float xo, yo;
-          rope_pair(xf[e], yf[e], cc[e], ss[e], &xo, &yo);
-          xf[e] = xo;
-          yf[e] = yo;
-        }
-        x = pack8(xf);
-        y = pack8(yf);
+      for (int e = 0; e < 8; ++e) {
+        float xo, yo;
+        rope_pair(xf[e], yf[e], cc[e], ss[e], &xo, &yo);
+        xf[e] = xo;
+        yf[e] = yo;
       }
-      qf[pr] = __builtin_bit_cast(bf16x8, x);
-      qf[pr + 2] = __builtin_bit_cast(bf16x8, y);
+      x = pack8(xf);
+      y = pack8(yf);
     }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) qf[m] = bf16x8{};
+    if (tq >= T) x = y = u32x4{0u, 0u, 0u, 0u};
+    qf[pr] = __builtin_bit_cast(bf16x8, x);
+    qf[pr + 2] = __builtin_bit_cast(bf16x8, y);
   }
 
   // per-lane LDS offsets: K' fragment row/col, and the transpose-read address
@@ -316,12 +412,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const float c2 = a.scale_log2;
   const unsigned wm1 = (unsigned)(W - 1);
 
-  const int kbeg = max(0, q0 - W + 1);
-  const int klast = min(T, q0 + BM) - 1;
-  const int it0 = kbeg / kBN, it1 = klast / kBN;
-
-  Stage<NW> st;
-  stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, tid);
   if (rope) __syncthreads();  // every wave has read its Q table rows
   // ring seeding: this workgroup writes its own query rows, as keys, for
   // frames in the stream's last W
@@ -344,8 +434,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
 
   for (int it = it0; it <= it1; ++it) {
     const int buf = (it - it0) & 1;
-    const bool more = it < it1;
-    if (more) stage_load<NW>(st, k, v, rs, T, (it + 1) * kBN, rope, a.table, a.table_row0, tid);
+    // the next tile's loads (past the last tile: an empty descriptor)
+    stage_load<NW>(st, k, v, rs, T, (it + 1) * kBN, rope, a.table, a.table_row0, so);
 
     const char* Kb = lds + buf * kStageBytes;
     const char* Vb = Kb + kTileK;
@@ -439,8 +529,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       }
     }
 
-    if (more) stage_commit<NW, SEED>(st, lds + (buf ^ 1) * kStageBytes,
-                               lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid, seed_for((it + 1) * kBN));
+    if (it < it1)
+      stage_commit<NW, SEED>(st, lds + (buf ^ 1) * kStageBytes,
+                             lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid,
+                             seed_for((it + 1) * kBN));
     __syncthreads();
   }
 
@@ -470,6 +562,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
 }
 
+// Compute units per XCD of the current device (the chip deals workgroups to
+// its 8 XCDs round-robin), cached per device.
+int cus_per_xcd() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  int c = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (c == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 8)
+      n = 256;
+    c = n / 8;
+    __atomic_store_n(&cache[dev], c, __ATOMIC_RELAXED);
+  }
+  return c;
+}
+
 template <int NW>
 hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   constexpr int BM = NW * 32;
@@ -477,18 +587,19 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   const int n_short = min(n_qtiles, (a.W - 1 + BM - 1) / BM);  // tiles with q0 < W-1
   const int n_bh = a.B * a.H;
   const int hx = n_bh >= 8 ? (n_bh + 7) / 8 : 0;
+  const int cpx = cus_per_xcd();
   const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
   const dim3 g((unsigned)grid), blk(NW * 64);
   if (a.ring_k) {
     if (out == DT::BF16)
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, true>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, true>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, true>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, true>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
   } else {
     if (out == DT::BF16)
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, false>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, false>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
     else
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, false>), g, blk, 0, st, a, n_qtiles, n_short, hx);
+      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, false>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
   }
   return hipGetLastError();
 }

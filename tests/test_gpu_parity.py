@@ -159,6 +159,23 @@ def test_prefill_edge_shapes(T, W):
     check_f32(got32, oracle.prefill(x32["q"], x32["k"], x32["v"], W), f"fp32 T{T} W{W}")
 
 
+@pytest.mark.parametrize("B,T,H,W", [(4, 64, 64, 64), (1, 129, 128, 16), (2, 300, 48, 97),
+                                     (1, 1000, 40, 750), (1, 2000, 20, 1), (2, 1501, 16, 751)])
+def test_prefill_many_heads_edge_shapes(B, T, H, W):
+    """Grids of at least 256 query tiles (sixteen-query waves): ragged T, T below one
+    tile, W = 1, W not a multiple of 32, W above T; sampled (b, h) against the oracle."""
+    say(f"many heads B{B} T{T} H{H} W{W}")
+    x = synth.make_prefill(B, T, H, seed=300 + T + W, dtype="bf16", scale=0.5)
+    got = run_prefill(x, W, "bf16")
+    rng = np.random.default_rng(T + W)
+    picks = [(0, 0), (B - 1, H - 1)] + [tuple(int(v) for v in rng.integers([0, 0], [B, H]))
+                                        for _ in range(2)]
+    for b, h in picks:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        want = oracle.prefill(x["q"][sl], x["k"][sl], x["v"][sl], W, bf16=True)
+        check_bf16(got[sl], want, f"B{B} T{T} H{H} W{W} b{b} h{h}")
+
+
 def test_prefill_position_offset_and_table_window():
     say("prefill pos0 12345, table 12000..14000")
     x = synth.make_prefill(1, 400, 4, seed=13, dtype="bf16", scale=0.5)
