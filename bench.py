@@ -48,14 +48,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
-                21_649_408 + 6_144_000),
+                "b09050268f16709deb56363fa35ca0c5bebaf15874aa44cea3478fe061f89fe7",
+                21_651_392 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
                "95d1d5b13d35cc99fb57042be5d3a40dc6c347c74bdda9b9d02adc8f3e80c33a",
                396_090_112 + 3_146_698),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                    "3144529381ea3d9e4cd89bdb533dd37eb511de7cdcadd230a35ad17dd2332e28",
-                    156_001_485 + 107_364_352),
+                    "b09050268f16709deb56363fa35ca0c5bebaf15874aa44cea3478fe061f89fe7",
+                    160_871_019 + 107_365_088),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",
                    2_148_394_965 + 786_981),
