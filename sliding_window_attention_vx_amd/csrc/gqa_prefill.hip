@@ -40,6 +40,7 @@ constexpr int kTileV = kBN * kRowV;
 constexpr int kStage = kTileK + kTileV;  // 37,888 bytes
 constexpr int kRowQT = 4 * kGD + 16;     // LDS bytes per staged cos/sin table row
 constexpr float kLazy = 8.0f;
+constexpr float kNoMax = -3.0e38f;          // running max before the first score
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_g;
 
@@ -285,7 +286,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // the running max starts at a finite floor, not -inf: the first finite
+  // score always moves it, exp2(floor - m) is 0 (not NaN), and a half whose
+  // scores are all masked gives exp2(-inf) = 0 against it, so no selects
+  float m_run = kNoMax, l_run = 0.f;
   const float c2 = a.scale_log2;
   const unsigned wm1 = (unsigned)(W - 1);
 
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
       const bool need = mxs > m_run + kLazy;
       if (__any(need)) {
         const float m_new = need ? mxs : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void gqa_prefill_kernel(GqaPrefill
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
         if (sb == 0 && act[1]) s_nxt = s_half(1);
         update_max(mx);
-        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+        const float mu = m_run;
         pv_half(s_cur, sb, mu);
         s_cur = s_nxt;
       }

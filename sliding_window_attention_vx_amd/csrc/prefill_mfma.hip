@@ -47,6 +47,7 @@ constexpr int kTileK = 64 * kRowK;         // one K' tile
 constexpr int kTileV = 64 * kRowV;         // one V tile
 constexpr int kStageBytes = kTileK + kTileV;
 constexpr float kLazy = 8.0f;              // log2-domain slack of the running max
+constexpr float kNoMax = -3.0e38f;          // running max before the first score
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -408,7 +409,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   f32x16 oacc[2];
   oacc[0] = f32x16{};
   oacc[1] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // the running max starts at a finite floor, not -inf: the first finite
+  // score always moves it, exp2(floor - m) is 0 (not NaN), and a half whose
+  // scores are all masked gives exp2(-inf) = 0 against it, so no selects
+  float m_run = kNoMax, l_run = 0.f;
   const float c2 = a.scale_log2;
   const unsigned wm1 = (unsigned)(W - 1);
 
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       if (__any(need)) {
         const float m_new = need ? mxs : m_run;
         // a lane whose keys were all masked so far has nothing to rescale
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
         if (sb == 0 && act[1]) s_nxt = s_half(1);
         update_max(mx);
-        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+        const float mu = m_run;
         pv_half(s_cur, sb, mu);
         s_cur = s_nxt;
       }
