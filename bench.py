@@ -48,14 +48,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                "b09050268f16709deb56363fa35ca0c5bebaf15874aa44cea3478fe061f89fe7",
-                21_651_392 + 6_144_000),
+                "5c751f7cbfacb1d04823b0a59a54185f594ce56137e5e81b73066b487552284f",
+                21_652_096 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
                "95d1d5b13d35cc99fb57042be5d3a40dc6c347c74bdda9b9d02adc8f3e80c33a",
                396_090_112 + 3_146_698),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                    "b09050268f16709deb56363fa35ca0c5bebaf15874aa44cea3478fe061f89fe7",
-                    160_871_019 + 107_365_088),
+                    "5c751f7cbfacb1d04823b0a59a54185f594ce56137e5e81b73066b487552284f",
+                    160_879_808 + 107_364_696),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",
                    2_148_394_965 + 786_981),
@@ -66,8 +66,8 @@ MEASURED_TRAFFIC = {
               "ae016fb04b70096e287909df76377577f041d02b6a6932ec7cfbf8ecf1b0d73d",
               13_718_698 + 655_360),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
-                    "6bceb9110066c810ac35445ac45d3e376d2289f0323a03ae4b026033455eca84",
-                    450_898_048 + 134_419_720),
+                    "9842b7b822612279c8760871b962db02dbe480fc29226d8aa415db66670e0f96",
+                    450_901_056 + 134_630_400),
 }
 
 
