@@ -463,6 +463,10 @@ def main():
                        table=ftab, out=fo[a_:b_][None])
     fc_serial_us = per_launch_us(serial_first_chunks, max(K // 4, 5))
     pre_us = per_launch_us(lambda j: prefill(), reps)
+    # the same attention with q and k rotated upstream, as when the q/k/v
+    # projection's epilogue applies RoPE (reported beside the fused figure)
+    pre_rot_us = per_launch_us(
+        lambda j: vx.prefill(q, k, v, window=pc.W, rope_applied=True, out=o), reps)
     step_us = per_launch_us(stream_fused, reps)
     attend_us = per_launch_us(lambda j: stream(j), reps)
     two_call_us = per_launch_us(lambda j: append(stream(j)), reps)
@@ -530,6 +534,7 @@ def main():
         },
         "prefill_us": round(pre_us, 3),
         "prefill_us_graph": round(pre_graph_us, 3),
+        "prefill_us_rope_upstream": round(pre_rot_us, 3),
         "stream_step_us": round(step_us, 3),
         "stream_step_two_calls_us": round(two_call_us, 3),
         "stream_attend_only_us": round(attend_us, 3),
