@@ -17,8 +17,9 @@
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *     allocates nothing, frees nothing and keeps no pointer after a call
- *     returns.  It holds no state and may be called from several host
- *     threads at once.
+ *     returns.  Its only state is a per-device cache of the CU count (read
+ *     once, to order the prefill's workgroups); it may be called from several
+ *     host threads at once.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work on it and never synchronise; a fault in a
  *     kernel surfaces at the caller's next synchronising HIP call.
