@@ -48,13 +48,13 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                "5c751f7cbfacb1d04823b0a59a54185f594ce56137e5e81b73066b487552284f",
+                "b7d76de672f04327ab5d81353d8c274815dd1c5fb756443519ad93d0e7006def",
                 21_652_096 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
                "95d1d5b13d35cc99fb57042be5d3a40dc6c347c74bdda9b9d02adc8f3e80c33a",
                396_090_112 + 3_146_698),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                    "5c751f7cbfacb1d04823b0a59a54185f594ce56137e5e81b73066b487552284f",
+                    "b7d76de672f04327ab5d81353d8c274815dd1c5fb756443519ad93d0e7006def",
                     160_879_808 + 107_364_696),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",

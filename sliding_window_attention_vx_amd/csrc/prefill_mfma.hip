@@ -27,8 +27,9 @@
 // values are rounded to bf16 (the storage type of a rotated tensor).
 // LDS rows are padded (K' 144 bytes, V 192 bytes) and the staging threads
 // are mapped to rows so that the MFMA operand reads and the staging writes
-// hit distinct banks.  K/V staging is double buffered: the next tile's global loads are
-// issued before the current tile's MFMAs.  Masks are applied only to the
+// hit distinct banks.  K/V staging is double buffered: the next tile's buffer
+// loads (per-tile descriptors in scalar registers) are issued before the
+// current tile's MFMAs.  Masks are applied only to the
 // 32-key halves that straddle a band edge, as one unsigned range test per
 // score.  Accumulators stay in VGPRs (the build asks for the VGPR form of
 // MFMA) so the softmax never moves them between register files.
