@@ -176,6 +176,20 @@ def test_prefill_many_heads_edge_shapes(B, T, H, W):
         check_bf16(got[sl], want, f"B{B} T{T} H{H} W{W} b{b} h{h}")
 
 
+def test_prefill_at_the_head_and_batch_limits():
+    """H = 65535 and B = 65535, the largest the boundary accepts, with short
+    chunks: sampled (b, h) against the oracle."""
+    for B, T, H, W, picks in ((1, 3, 65535, 2, [(0, 0), (0, 1), (0, 32767), (0, 65534)]),
+                              (65535, 2, 1, 750, [(0, 0), (12345, 0), (65534, 0)])):
+        say(f"limits: B{B} T{T} H{H} W{W}")
+        x = synth.make_prefill(B, T, H, seed=400 + T, dtype="bf16", scale=0.5)
+        got = run_prefill(x, W, "bf16")
+        for b, h in picks:
+            sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+            want = oracle.prefill(x["q"][sl], x["k"][sl], x["v"][sl], W, bf16=True)
+            check_bf16(got[sl], want, f"B{B} T{T} H{H} b{b} h{h}")
+
+
 def test_prefill_position_offset_and_table_window():
     say("prefill pos0 12345, table 12000..14000")
     x = synth.make_prefill(1, 400, 4, seed=13, dtype="bf16", scale=0.5)
@@ -267,6 +281,32 @@ def test_stream_step_full_workload(io, out):
     else:
         assert np.all(np.abs(gk - rk_o) <= np.abs(rk_o) * 2.0 ** -7 + 1e-30)
         assert (gk != rk_o).mean() < 1e-3
+
+
+def test_stream_step_at_the_stream_limit():
+    """S = 65535 streams, the largest the boundary accepts: sampled streams of
+    the step and of the append against the oracle."""
+    S, n, H, W = 65535, 1, 1, 4
+    say(f"stream limits: S{S} n{n} H{H} W{W}")
+    st = synth.make_stream_state(S, H, W, seed=71, pos_lo=W, pos_hi=20000)
+    fr = synth.make_stream_frames(S, n, H, seed=71, step=0)
+    rk, rv, pos = _stream_state_dev(st, "bf16")
+    qn, kn, vn = (dev(fr[c], "bf16") for c in ("q", "k", "v"))
+    o = host(vx.stream_step(qn, kn, vn, rk, rv, pos, window=W, out_dtype="f32"))
+    vx.ring_append(rk, rv, kn, vn, pos, window=W)
+    grk, grv, gpos = host(rk), host(rv), host(pos.double())
+    for s in (0, 1, 40000, S - 1):
+        sl = slice(s, s + 1)
+        want = oracle.stream_step(fr["q"][sl], fr["k"][sl], fr["v"][sl], st["ring_k"][sl],
+                                  st["ring_v"][sl], st["pos"][sl], W, bf16=True)
+        check_bf16(o[sl], want, f"stream {s}")
+        rk_o = st["ring_k"][sl].astype(np.float64)
+        rv_o = st["ring_v"][sl].astype(np.float64)
+        pos_o = st["pos"][sl].copy()
+        oracle.ring_append(rk_o, rv_o, fr["k"][sl], fr["v"][sl], pos_o, W, bf16=True)
+        np.testing.assert_array_equal(gpos[sl], pos_o)
+        np.testing.assert_array_equal(grv[sl], rv_o)
+        assert np.all(np.abs(grk[sl] - rk_o) <= np.abs(rk_o) * 2.0 ** -7 + 4 * 2.0 ** -24 * 8.0)
 
 
 def feed_stream(q, k, v, W, chunks, S=1, ring_fill=np.nan, io="bf16"):
