@@ -96,7 +96,10 @@ __global__ __launch_bounds__(kNormWaves * 64) void rmsnorm_kernel(const float* _
 // The end of a split product added into the residual stream, one wave per
 // row: x = x + (P_0 + .. + P_{np-1} + bias) with the K parts' fp32 sums in
 // order, then optionally h = rmsnorm(x) * g (bf16) for the next product.
-template <int CPL, bool NORM>
+// With NP > 0 (np == NP) every load of the row (parts, bias, x) is issued
+// before the first add, so the row costs one memory round trip; NP == 0
+// takes any np.
+template <int CPL, bool NORM, int NP>
 __global__ __launch_bounds__(kNormWaves * 64) void residual_reduce_kernel(
     float* __restrict__ x, const float* __restrict__ parts, int np, const bf16* __restrict__ bias,
     const bf16* __restrict__ g, bf16* __restrict__ h, int M, int dim, float eps) {
@@ -107,26 +110,58 @@ __global__ __launch_bounds__(kNormWaves * 64) void residual_reduce_kernel(
   const size_t pstride = (size_t)M * dim;
   float* xr = x + row * dim;
   float v[CPL][8];
+  if constexpr (NP > 0) {
+    float pv[NP][CPL][8], bv[CPL][8];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
-    if (c >= c8) continue;
-    float acc[8], t[8];
-    load8(parts + row * dim + 8 * c, acc);
-    for (int p = 1; p < np; ++p) {
-      load8(parts + p * pstride + row * dim + 8 * c, t);
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= c8) continue;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += t[e];
+      for (int p = 0; p < NP; ++p) load8(parts + p * pstride + row * dim + 8 * c, pv[p][j]);
+      if (bias) load8(bias + 8 * c, bv[j]);
+      load8(xr + 8 * c, v[j]);
     }
-    if (bias) {
-      load8(bias + 8 * c, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += t[e];
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= c8) continue;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = pv[0][j][e];
+#pragma unroll
+      for (int p = 1; p < NP; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += pv[p][j][e];
+      if (bias) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += bv[j][e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = acc[e] + v[j][e];
+      store8(xr + 8 * c, v[j]);
     }
-    load8(xr + 8 * c, t);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[j][e] = acc[e] + t[e];
-    store8(xr + 8 * c, v[j]);
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= c8) continue;
+      float acc[8], t[8];
+      load8(parts + row * dim + 8 * c, acc);
+      for (int p = 1; p < np; ++p) {
+        load8(parts + p * pstride + row * dim + 8 * c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += t[e];
+      }
+      if (bias) {
+        load8(bias + 8 * c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += t[e];
+      }
+      load8(xr + 8 * c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = acc[e] + t[e];
+      store8(xr + 8 * c, v[j]);
+    }
   }
   if constexpr (NORM) norm_row_store<CPL>(v, g, h + row * dim, lane, c8, dim, eps);
 }
@@ -172,13 +207,21 @@ hipError_t launch_residual_reduce(float* x, const float* parts, int np, const bf
   const unsigned blocks = (unsigned)((M + kNormWaves - 1) / kNormWaves);
   const dim3 grid(blocks), blk(kNormWaves * 64);
   const int cpl = (dim / 8 + 63) / 64;
-#define VX_RR(C)                                                                              \
+#define VX_RR3(C, P)                                                                          \
   if (g)                                                                                      \
-    hipLaunchKernelGGL((residual_reduce_kernel<C, true>), grid, blk, 0, st, x, parts, np, bias, g, \
-                       h, M, dim, eps);                                                       \
+    hipLaunchKernelGGL((residual_reduce_kernel<C, true, P>), grid, blk, 0, st, x, parts, np, bias, \
+                       g, h, M, dim, eps);                                                    \
   else                                                                                        \
-    hipLaunchKernelGGL((residual_reduce_kernel<C, false>), grid, blk, 0, st, x, parts, np, bias,   \
-                       g, h, M, dim, eps);
+    hipLaunchKernelGGL((residual_reduce_kernel<C, false, P>), grid, blk, 0, st, x, parts, np,     \
+                       bias, g, h, M, dim, eps);
+#define VX_RR(C)                                                                              \
+  if (np == 2) {                                                                              \
+    VX_RR3(C, 2)                                                                              \
+  } else if (np == 1) {                                                                       \
+    VX_RR3(C, 1)                                                                              \
+  } else {                                                                                    \
+    VX_RR3(C, 0)                                                                              \
+  }
   if (cpl <= 1) {
     VX_RR(1)
   } else if (cpl <= 2) {
@@ -186,9 +229,10 @@ hipError_t launch_residual_reduce(float* x, const float* parts, int np, const bf
   } else if (cpl <= 4) {
     VX_RR(4)
   } else {
-    VX_RR(8)
+    VX_RR3(8, 0)  // rows past 4 chunks per lane: loads in two rounds, fewer registers
   }
 #undef VX_RR
+#undef VX_RR3
   return hipGetLastError();
 }
 
