@@ -71,15 +71,25 @@ typedef struct {
   int32_t io_dtype;      /* vx_dtype of q, k, v and of the rings                    */
   int32_t out_dtype;     /* vx_dtype of o; pairs: bf16->bf16, bf16->f32, f32->f32   */
   uint32_t flags;        /* VX_FLAG_* bits, 0 by default                            */
+  /* Optional device scratch owned by the caller (NULL/0 = none, 16-byte
+   * aligned), used by vx_swa_attn_prefill when it is given no rope_table:
+   * the cos/sin rows of the call's positions are built there (see
+   * vx_swa_attn_prefill_workspace_size).  No contents are kept between
+   * calls; calls that overlap in time must not share a workspace.  Other
+   * entry points ignore it. */
+  void *workspace;
+  size_t workspace_bytes;
 } vx_attn_cfg;
 
 /* Fills `cfg` with the Voxtral Realtime encoder defaults: head_dim 64,
- * window 750, theta 1e6, scale 1/8, bf16 in and out, no flags. */
+ * window 750, theta 1e6, scale 1/8, bf16 in and out, no flags, no workspace. */
 void vx_default_cfg(vx_attn_cfg *cfg);
 
 /* RoPE cosine/sine table for `count` consecutive positions starting at
- * `p_begin` (>= 0), for head_dim 64 or 128.  table: device float32
- * [count][2][head_dim/2]:
+ * `p_begin` (>= 0), for head_dim 64 or 128: the RoPE cache of the rotation
+ * defined at the top of this file (transcribe.cpp "Voxtral" family notes,
+ * Architecture: RoPE theta 1e6 on the encoder's queries and keys).
+ * table: device float32 [count][2][head_dim/2]:
  * table[j][0][i] = cos((p_begin+j) * theta^(-2i/D)), table[j][1][i] = sin(...).
  * Only cfg->head_dim and cfg->rope_theta are read.  The table depends on
  * nothing else, so one table serves every layer and call that uses these
@@ -87,32 +97,65 @@ void vx_default_cfg(vx_attn_cfg *cfg);
 vx_status vx_rope_table(float *table, int64_t p_begin, int32_t count, const vx_attn_cfg *cfg,
                         void *stream);
 
-/* In-place RoPE of q and k, both [B,T,H,D] of cfg->io_dtype; row t of every
- * batch entry sits at absolute position pos0 + t (pos0 >= 0).  Either q or k
- * may be NULL (not both).  V is never rotated. */
-vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, int64_t pos0,
+/* In-place RoPE of q and k, both [B,T,H,D] of cfg->io_dtype: the rotation
+ * the encoder applies to its queries and keys before attention
+ * (transcribe.cpp "Voxtral" family notes, Architecture, Voxtral Realtime
+ * 2602: RoPE theta 1e6, head_dim 64).  Row t of batch entry b sits at
+ * absolute position pos0[b] + t.
+ * pos0: device int64 [B] (8-byte aligned), or NULL for position t.  The
+ *   values are read on the device, so they are not checked here: an entry
+ *   with pos0[b] < 0 has its q and k rows set to NaN (loud, never partial).
+ * Either q or k may be NULL (not both).  V is never rotated. */
+vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, const int64_t *pos0,
                      const vx_attn_cfg *cfg, void *stream);
 
-/* Causal sliding-window attention over whole chunks (no history):
+/* Causal sliding-window attention over whole chunks (no history), the
+ * encoder's self-attention in its whole-chunk form (transcribe.cpp "Voxtral"
+ * family notes, Architecture, Voxtral Realtime 2602: causal sliding window
+ * of 750 frames, 32 heads x 64, RoPE; run as one call per chunk like the
+ * Core AI port's batched first-chunk encoder, "Voxtral Mini 4B Realtime -
+ * Core AI", "Why two encoders?"):
  *   o[b,t,h] = sum_j softmax_j(scale * q'[b,t,h] . k'[b,j,h]) v[b,j,h],
  *   j = max(0, t-W+1) .. t,
- * where q', k' are q, k rotated at positions pos0 + t (pos0 >= 0).
+ * where q', k' are q, k rotated at positions pos0[b] + t.
  * q, k, v: [B,T,H,D] cfg->io_dtype; o: [B,T,H,D] cfg->out_dtype (must not
  * alias the inputs).
- * rope_applied != 0: q and k are already rotated; `rope_table` is ignored.
- * rope_applied == 0: the kernel rotates q and k as it loads them, reading
- *   cos/sin from `rope_table` (made by vx_rope_table) which covers positions
- *   table_p0 .. table_p0 + table_len - 1; those must include
- *   pos0 .. pos0 + T - 1, else VX_E_RANGE. */
+ * pos0: device int64 [B] (8-byte aligned), or NULL for positions 0 .. T-1.
+ * rope_applied != 0: q and k are already rotated; the table is ignored.
+ * rope_applied == 0: the kernel rotates q and k as it loads them, with
+ *   cos/sin from
+ *   - rope_table (made by vx_rope_table) covering positions table_p0 ..
+ *     table_p0 + table_len - 1, which must include every pos0[b] .. pos0[b]
+ *     + T - 1: checked here when pos0 is NULL (VX_E_RANGE), on the device
+ *     otherwise;
+ *   - rope_table == NULL: a table of the call's positions built in the
+ *     workspace (one extra launch) when cfg->workspace has room for it,
+ *     else cos/sin computed in the kernel from the same float64 angle (the
+ *     same values, at a higher cost per tile).
+ * A batch entry whose positions are invalid on the device (pos0[b] < 0, or
+ * rows outside the given table) gets NaN in all its outputs (loud, never
+ * partial); the other entries are unaffected.
+ * cfg->workspace (optional): with at least
+ * vx_swa_attn_prefill_workspace_size() bytes, a NULL rope_table is served
+ * from a table built in it (one extra launch); the results are the same bits
+ * as with a caller table or cos/sin computed in the kernel. */
 vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
-                              int32_t T, int32_t H, int64_t pos0, int32_t rope_applied,
+                              int32_t T, int32_t H, const int64_t *pos0, int32_t rope_applied,
                               const float *rope_table, int64_t table_p0, int64_t table_len,
                               const vx_attn_cfg *cfg, void *stream);
 
+/* Workspace bytes (cfg->workspace_bytes) with which vx_swa_attn_prefill of
+ * this shape, given no rope_table, keeps its cos/sin table in the workspace:
+ * B*T rows of 256 bytes (row b*T + t for position pos0[b] + t).  Returns 0
+ * for invalid arguments. */
+size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
+                                          const vx_attn_cfg *cfg);
+
 /* Batched first-chunk prefill over streams of different lengths, which can
  * also seed each stream's KV ring for the streaming step (Voxtral Mini 4B
- * Realtime Core AI page: the batched first-chunk encoder, one call for the
- * whole first chunk, then the streaming encoder for later chunks).
+ * Realtime Core AI page, "Why two encoders?" and the Streaming table: the
+ * batched first-chunk encoder, one call for the whole first chunk, then the
+ * streaming encoder for later chunks).
  * Stream s has T_s = cu_seqlens[s+1] - cu_seqlens[s] frames at positions
  * 0 .. T_s - 1, packed along the frame axis: q, k, v and o are
  * [total, H, D] with stream s at rows cu_seqlens[s] .. cu_seqlens[s+1]-1;
@@ -122,11 +165,14 @@ vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void 
  *   cu_seqlens[S] = total.  The kernel clamps every offset to [0, total] and
  *   a negative length counts as 0, so a wrong array cannot reach outside
  *   the buffers.
- * max_T: host bound with T_s <= max_T for every s (rows of a longer stream
- *   past max_T are not computed); max_T <= W is the full-causal case.
+ * max_T: host bound on every T_s.  A stream with T_s > max_T is an error
+ *   found on the device: all its output rows are NaN and its ring and pos
+ *   are left untouched (loud, never partial).  max_T <= W is the
+ *   full-causal case.
  * bf16 input only (VX_E_DTYPE otherwise); o is bf16 or float32.
- * RoPE as in vx_swa_attn_prefill with pos0 = 0: the table must cover
- *   positions 0 .. max_T - 1 unless rope_applied != 0.
+ * RoPE as in vx_swa_attn_prefill with pos0 = NULL: a given table must
+ *   cover positions 0 .. max_T - 1 (VX_E_RANGE otherwise); a NULL table
+ *   means cos/sin computed in the kernel.
  * ring_k, ring_v: [S, H, W, D] bf16 rings, or both NULL for no seeding.
  *   When given, the rotated keys and the values of frames
  *   t >= T_s - W are written to slot t mod W of stream s (other slots keep
@@ -140,14 +186,23 @@ vx_status vx_swa_attn_prefill_varlen(const void *q, const void *k, const void *v
                                      void *ring_v, int64_t *pos, const vx_attn_cfg *cfg,
                                      void *stream);
 
-/* One streaming step for S independent streams with n new frames each
- * (1 <= n <= min(W, 64); a longer first chunk goes through the prefill).
- * q_new, k_new, v_new, o: [S,n,H,D]; ring_k (rotated keys) and ring_v: [S,H,W,D] in cfg->io_dtype; slot j of a ring holds the frame at
- * absolute position p with p mod W == j.  pos: device int64 [S], the absolute
+/* One streaming step for S independent streams with n new frames each: the
+ * encoder's incremental form (transcribe.cpp "Voxtral" family notes,
+ * Streaming schedule: each 80 ms step brings 8 mel frames = 4 encoder frames
+ * per stream, attending causally within the 750-frame window over state
+ * carried from earlier steps; the Core AI port's streaming encoder, "Why two
+ * encoders?").  1 <= n <= min(W, 64): a longer increment is the same
+ * computation as consecutive steps of at most 64 frames, each followed by
+ * its append (the step attends before it appends, so the ring then holds
+ * exactly the keys a longer step would read from the new frames).
+ * q_new, k_new, v_new, o: [S,n,H,D]; ring_k (rotated keys) and ring_v:
+ * [S,H,W,D] in cfg->io_dtype; slot j of a ring holds the frame at absolute
+ * position p with p mod W == j.  pos: device int64 [S], the absolute
  * position of the first new frame of each stream (= frames appended so far;
  * a stream starts at 0 with any ring contents, since slots of positions < 0
- * are never read; negative values count as 0 history).  New query i of
- * stream s (position P = pos[s] + i) attends to ring frames at positions
+ * are never read).  A negative pos[s] is an invalid state found on the
+ * device: that stream's outputs are NaN (loud, never partial).  New query i
+ * of stream s (position P = pos[s] + i) attends to ring frames at positions
  * max(0, P-W+1) .. pos[s]-1 and to new frames pos[s] .. P.  New q and k are
  * rotated here unless rope_applied != 0.  Reads the ring and pos, never
  * writes them: call vx_kv_ring_append afterwards, on the same stream. */
@@ -156,12 +211,16 @@ vx_status vx_swa_attn_stream_step(const void *q_new, const void *k_new, const vo
                                   void *o, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
                                   const vx_attn_cfg *cfg, void *stream);
 
-/* Appends n new frames per stream: rotates k_new (unless rope_applied != 0)
- * at positions pos[s] + i, writes it and v_new to slot (pos[s] + i) mod W of
- * ring_k / ring_v, then sets pos[s] += n on the device.  Shapes and dtypes as
- * in vx_swa_attn_stream_step.  Must follow every read of the ring for this
- * step (same stream): the slots it overwrites still hold keys that the
- * step's queries need. */
+/* Appends n new frames per stream to the W-slot ring that carries the
+ * streaming state (the encoder's cache of past rotated keys and values; the
+ * Core AI port keeps an append-only buffer instead, "Voxtral Mini 4B
+ * Realtime - Core AI", Usage / Known limitations): rotates k_new (unless
+ * rope_applied != 0) at positions pos[s] + i, writes it and v_new to slot
+ * (pos[s] + i) mod W of ring_k / ring_v, then sets pos[s] += n on the
+ * device.  A stream with pos[s] < 0 is left as it is (nothing written, pos
+ * kept).  Shapes and dtypes as in vx_swa_attn_stream_step.  Must follow
+ * every read of the ring for this step (same stream): the slots it
+ * overwrites still hold keys that the step's queries need. */
 vx_status vx_kv_ring_append(void *ring_k, void *ring_v, const void *k_new, const void *v_new,
                             int64_t *pos, int32_t S, int32_t n, int32_t H, int32_t rope_applied,
                             const vx_attn_cfg *cfg, void *stream);
@@ -169,11 +228,14 @@ vx_status vx_kv_ring_append(void *ring_k, void *ring_v, const void *k_new, const
 /* One streaming step and its ring append in one call (one launch for bf16):
  * the attention of vx_swa_attn_stream_step, then the rotated new keys and the
  * new values are written to slots (pos_in[s] + i) mod W of the rings, and
- * pos_out[s] = pos_in[s] + n.  Same shapes and dtypes as the two separate
- * calls, and the same results bit for bit.  Requires 1 <= n <= min(W, 16)
- * (one workgroup per ring, which writes it only after all its reads).
- * pos_in and pos_out must be distinct arrays: some workgroups still read
- * pos_in while another writes pos_out; swap the two for the next step. */
+ * pos_out[s] = pos_in[s] + n (the per-step schedule of transcribe.cpp
+ * "Voxtral" family notes, Streaming schedule).  Same shapes and dtypes as
+ * the two separate calls, and the same results bit for bit.  Requires
+ * 1 <= n <= min(W, 16) (one workgroup per ring, which writes it only after
+ * all its reads).  A stream with pos_in[s] < 0 gets NaN outputs, no ring
+ * write and pos_out[s] = pos_in[s].  pos_in and pos_out must be distinct
+ * arrays: some workgroups still read pos_in while another writes pos_out;
+ * swap the two for the next step. */
 vx_status vx_swa_attn_stream_step_append(const void *q_new, const void *k_new, const void *v_new,
                                          void *ring_k, void *ring_v, const int64_t *pos_in,
                                          int64_t *pos_out, void *o, int32_t S, int32_t n,

@@ -14,7 +14,8 @@ import ctypes
 import os
 
 __all__ = [
-    "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "stream_step", "ring_append",
+    "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "prefill_workspace_size",
+    "prefill_workspace", "prefill_varlen", "stream_step", "ring_append",
     "stream_step_append", "gqa_prefill", "gqa_decode", "linear", "enc_qkv_rope",
     "enc_attn_step", "rmsnorm", "enc_work", "enc_stem_step", "enc_layer_step", "enc_step",
     "LAYER_KEYS", "STEM_KEYS",
@@ -47,7 +48,9 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
                 ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
 
 
 _vp = ctypes.c_void_p
@@ -75,9 +78,11 @@ class _Work(ctypes.Structure):
 _SIGS = {
     "vx_default_cfg": (None, [ctypes.POINTER(_Cfg)]),
     "vx_rope_table": (ctypes.c_int, [_vp, _i64, _i32, ctypes.POINTER(_Cfg), _vp]),
-    "vx_rope_qk": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i64, ctypes.POINTER(_Cfg), _vp]),
-    "vx_swa_attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp,
+    "vx_rope_qk": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
                                            _i64, _i64, ctypes.POINTER(_Cfg), _vp]),
+    "vx_swa_attn_prefill_workspace_size": (ctypes.c_size_t, [_i32, _i32, _i32,
+                                                             ctypes.POINTER(_Cfg)]),
     "vx_swa_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
     "vx_kv_ring_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -136,7 +141,7 @@ class Config:
     """Attention parameters (mirrors vx_attn_cfg)."""
 
     def __init__(self, window=WINDOW, theta=THETA, scale=0.0, io_dtype="bf16", out_dtype=None,
-                 valu=False, head_dim=HEAD_DIM):
+                 valu=False, head_dim=HEAD_DIM, workspace=None):
         self.head_dim = int(head_dim)
         self.window = int(window)
         self.theta = float(theta)
@@ -144,11 +149,15 @@ class Config:
         self.io_dtype = io_dtype
         self.out_dtype = out_dtype or io_dtype
         self.valu = bool(valu)
+        self.workspace = workspace  # device tensor or None
 
     def c(self):
         d = {"bf16": VX_BF16, "f32": VX_F32}
+        ws = self.workspace
         return _Cfg(self.head_dim, self.window, self.theta, self.scale, d[self.io_dtype],
-                    d[self.out_dtype], VX_FLAG_VALU_KERNEL if self.valu else 0)
+                    d[self.out_dtype], VX_FLAG_VALU_KERNEL if self.valu else 0,
+                    None if ws is None else ws.data_ptr(),
+                    0 if ws is None else ws.numel() * ws.element_size())
 
 
 def _check(status, func):
@@ -195,8 +204,35 @@ def rope_table(p_begin, count, theta=THETA, device="cuda", out=None, head_dim=HE
     return out
 
 
-def rope_qk(q, k, pos0=0, theta=THETA):
-    """Rotate q and k [B,T,H,64] in place (either may be None)."""
+def _pos0(pos0, B, device):
+    """pos0 as a device int64 [B] tensor (None: positions start at 0)."""
+    import torch
+    if pos0 is None:
+        return None
+    if isinstance(pos0, torch.Tensor):
+        _dev_tensor(pos0, "pos0")
+        if pos0.dtype != torch.int64 or pos0.shape != (B,):
+            raise ValueError(f"pos0 must be an int64 tensor of shape ({B},)")
+        return pos0
+    return torch.full((B,), int(pos0), dtype=torch.int64, device=device)
+
+
+def _table(table, head_dim):
+    """A caller's cos/sin table: float32 [rows, 2, head_dim/2] on the GPU."""
+    import torch
+    _dev_tensor(table, "table")
+    if table.dtype != torch.float32 or table.dim() != 3 or table.shape[1:] != (2, head_dim // 2):
+        raise ValueError(f"table must be float32 [rows, 2, {head_dim // 2}] (from rope_table "
+                         f"with head_dim {head_dim})")
+    return table
+
+
+def rope_qk(q, k, pos0=None, theta=THETA):
+    """Rotate q and k [B,T,H,64] in place (either may be None).
+
+    pos0: None (row t at position t), an int (the same first position for
+    every batch entry) or a device int64 tensor [B] (entry b starts at pos0[b]).
+    """
     t = q if q is not None else k
     for name, x in (("q", q), ("k", k)):
         if x is not None:
@@ -206,18 +242,38 @@ def rope_qk(q, k, pos0=0, theta=THETA):
     if t.dim() != 4 or t.shape[-1] != HEAD_DIM:
         raise ValueError("expected [B, T, H, 64]")
     B, T, H, _ = t.shape
+    p0 = _pos0(pos0, B, t.device)
     cfg = Config(theta=theta, io_dtype=_dt(t)).c()
-    _check(lib().vx_rope_qk(_ptr(q), _ptr(k), B, T, H, int(pos0), ctypes.byref(cfg), _stream(t)),
+    _check(lib().vx_rope_qk(_ptr(q), _ptr(k), B, T, H, _ptr(p0), ctypes.byref(cfg), _stream(t)),
            "vx_rope_qk")
 
 
-def prefill(q, k, v, window=WINDOW, pos0=0, theta=THETA, scale=0.0, rope_applied=False,
-            table=None, table_p0=0, out=None, out_dtype=None, valu=False):
+def prefill_workspace_size(B, T, H, window=WINDOW, theta=THETA):
+    """Bytes of workspace in which prefill() of this shape keeps its cos/sin table."""
+    cfg = Config(window, theta).c()
+    return int(lib().vx_swa_attn_prefill_workspace_size(int(B), int(T), int(H), ctypes.byref(cfg)))
+
+
+def prefill_workspace(B, T, H, window=WINDOW, device="cuda"):
+    """A workspace of prefill_workspace_size() bytes (reusable across calls)."""
+    import torch
+    n = prefill_workspace_size(B, T, H, window)
+    return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_applied=False,
+            table=None, table_p0=0, out=None, out_dtype=None, valu=False, workspace=None,
+            auto_table=True):
     """Causal sliding-window attention over whole chunks; q,k,v [B,T,H,64] -> o [B,T,H,64].
 
-    With rope_applied=False the kernel rotates q and k using `table` (from
-    rope_table, covering positions pos0..pos0+T-1 starting at table_p0); if no
-    table is given one is made for exactly those positions.
+    pos0: None (positions 0..T-1), an int, or a device int64 tensor [B] (entry b
+    at positions pos0[b] .. pos0[b]+T-1).  With rope_applied=False the kernel
+    rotates q and k with cos/sin from `table` (rope_table rows starting at
+    position table_p0).  Without a table: for pos0 None or an int a table of
+    the chunk's positions is made here (auto_table=True); otherwise the
+    library builds one in the workspace if it has room, else computes cos/sin
+    in the kernel.  workspace: a uint8 device tensor (prefill_workspace), reused
+    across calls; None runs without one.
     """
     import torch
     for name, x in (("q", q), ("k", k), ("v", v)):
@@ -235,17 +291,26 @@ def prefill(q, k, v, window=WINDOW, pos0=0, theta=THETA, scale=0.0, rope_applied
     _dev_tensor(out, "out")
     if out.shape != q.shape or _dt(out) != od:
         raise ValueError("out has the wrong shape or dtype")
+    p0 = _pos0(pos0, B, q.device)
     tlen = 0
-    if not rope_applied:
-        if table is None:
-            table = rope_table(pos0, T, theta, device=q.device)
-            table_p0 = pos0
-        _dev_tensor(table, "table")
+    if not rope_applied and table is None and not isinstance(pos0, torch.Tensor) and auto_table:
+        # one position range for every entry: a table of exactly those rows
+        first = 0 if pos0 is None else int(pos0)
+        table = rope_table(first, max(T, 1), theta, device=q.device)
+        table_p0 = first
+    if not rope_applied and table is not None:
+        _table(table, HEAD_DIM)
         tlen = table.shape[0]
-    cfg = Config(window, theta, scale, io, od, valu).c()
-    _check(lib().vx_swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, int(pos0),
-                                     int(bool(rope_applied)), _ptr(table), int(table_p0), int(tlen),
-                                     ctypes.byref(cfg), _stream(q)), "vx_swa_attn_prefill")
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace")
+        if workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor (see prefill_workspace)")
+    cfg = Config(window, theta, scale, io, od, valu, workspace=workspace).c()
+    _check(lib().vx_swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, _ptr(p0),
+                                     int(bool(rope_applied)),
+                                     _ptr(table) if not rope_applied else None, int(table_p0),
+                                     int(tlen), ctypes.byref(cfg), _stream(q)),
+           "vx_swa_attn_prefill")
     return out
 
 
@@ -277,10 +342,8 @@ def prefill_varlen(q, k, v, cu_seqlens, max_T, window=WINDOW, theta=THETA, scale
     if out.shape != q.shape or _dt(out) != od:
         raise ValueError("out has the wrong shape or dtype")
     tlen = 0
-    if not rope_applied:
-        if table is None:
-            table = rope_table(0, max(int(max_T), 1), theta, device=q.device)
-        _dev_tensor(table, "table")
+    if not rope_applied and table is not None:
+        _table(table, HEAD_DIM)
         tlen = table.shape[0]
     if ring_k is not None:
         for name, x in (("ring_k", ring_k), ("ring_v", ring_v), ("pos", pos)):
@@ -294,7 +357,8 @@ def prefill_varlen(q, k, v, cu_seqlens, max_T, window=WINDOW, theta=THETA, scale
     cfg = Config(window, theta, scale, io, od).c()
     _check(lib().vx_swa_attn_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(cu_seqlens), S, q.shape[0], int(max_T), H,
-        int(bool(rope_applied)), _ptr(table), 0, int(tlen), _ptr(ring_k), _ptr(ring_v), _ptr(pos),
+        int(bool(rope_applied)), _ptr(table) if not rope_applied else None, 0, int(tlen),
+        _ptr(ring_k), _ptr(ring_v), _ptr(pos),
         ctypes.byref(cfg), _stream(q)), "vx_swa_attn_prefill_varlen")
     return out
 
@@ -329,6 +393,8 @@ def stream_step(q_new, k_new, v_new, ring_k, ring_v, pos, window=WINDOW, theta=T
         out = torch.empty(q_new.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
                           device=q_new.device)
     _dev_tensor(out, "out")
+    if out.shape != q_new.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
     cfg = Config(window, theta, scale, io, od).c()
     _check(lib().vx_swa_attn_stream_step(_ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k),
                                          _ptr(ring_v), _ptr(pos), _ptr(out), S, n, H,
@@ -372,6 +438,8 @@ def stream_step_append(q_new, k_new, v_new, ring_k, ring_v, pos_in, pos_out, win
         out = torch.empty(q_new.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
                           device=q_new.device)
     _dev_tensor(out, "out")
+    if out.shape != q_new.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
     cfg = Config(window, theta, scale, io, od).c()
     _check(lib().vx_swa_attn_stream_step_append(
         _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(ring_k), _ptr(ring_v), _ptr(pos_in),
@@ -418,7 +486,7 @@ def gqa_prefill(q, k, v, window=DEC_WINDOW, pos0=0, theta=THETA, scale=0.0, rope
         if table is None:
             table = rope_table(pos0, max(T, 1), theta, device=q.device, head_dim=DEC_HEAD_DIM)
             table_p0 = pos0
-        _dev_tensor(table, "table")
+        _table(table, DEC_HEAD_DIM)
         tlen = table.shape[0]
     if ring_k is not None or ring_v is not None:
         for name, x in (("ring_k", ring_k), ("ring_v", ring_v), ("pos", pos)):

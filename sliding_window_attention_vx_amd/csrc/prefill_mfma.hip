@@ -23,8 +23,12 @@
 //                    the normaliser matches the weights the MFMA multiplies.
 // RoPE is fused into the loads: each lane rotates its own Q' row halves
 // (pairs (i, i+32) are lane-local) and the staging threads rotate each K
-// tile once per workgroup, reading cos/sin from the float32 table; rotated
-// values are rounded to bf16 (the storage type of a rotated tensor).
+// tile once per workgroup, reading cos/sin from the float32 table or, with
+// no table, computing them from the same float64 angle (the same values);
+// rotated values are rounded to bf16 (the storage type of a rotated tensor).
+// Frame t of batch entry b sits at position pos0[b] + t; an entry whose
+// positions are negative or outside the table, or a varlen stream longer
+// than the call allows, gets NaN outputs (loud, never a silent partial).
 // LDS rows are padded (K' 144 bytes, V 192 bytes) and the staging threads
 // are mapped to rows so that the MFMA operand reads and the staging writes
 // hit distinct banks.  K/V staging is double buffered: the next tile's buffer
@@ -79,6 +83,29 @@ __device__ __forceinline__ void k_unit(int u, int& r, int& cp) {
 __device__ __forceinline__ void v_unit(int u, int& r, int& c) {
   r = 8 * (u >> 6) + 4 * ((u >> 5) & 1) + ((u >> 2) & 3);
   c = 4 * ((u >> 4) & 1) + (u & 3);
+}
+
+// Frequency of pair 8c+e, c in 0..3 chosen per lane: selects between
+// constant offsets of the kernel argument, so the array is never indexed
+// dynamically (that would copy it to scratch memory).
+__device__ __forceinline__ double freq8(const RopeFreqs& fr, int c, int e) {
+  double f = fr.f[e];
+  f = c == 1 ? fr.f[8 + e] : f;
+  f = c == 2 ? fr.f[16 + e] : f;
+  f = c == 3 ? fr.f[24 + e] : f;
+  return f;
+}
+
+// Writes NaN over rows [r0, r1) of one head: the loud result for a batch
+// entry whose positions are invalid or a stream longer than the call allows.
+template <typename TO>
+__device__ void poison_rows(TO* o, size_t rs, int r0, int r1) {
+  const int n = (r1 - r0) * 16;  // 4-element units
+  for (int u = threadIdx.x; u < n; u += blockDim.x) {
+    TO* p = o + (size_t)(r0 + u / 16) * rs + 4 * (u % 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = (TO)__builtin_nanf("");
+  }
 }
 
 __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, int hx, int cpx,
@@ -154,6 +181,7 @@ struct Stage {
 template <int NW>
 struct StageOffs {
   uint32_t k[Stage<NW>::UK], t[Stage<NW>::UK], v[Stage<NW>::UV];
+  int kr[Stage<NW>::UK], kcp[Stage<NW>::UK];  // row and chunk pair of each K unit
 };
 
 template <int NW>
@@ -167,6 +195,8 @@ __device__ __forceinline__ StageOffs<NW> stage_offsets(int tid, size_t rs) {
     k_unit(tid + j * NT, r, cp);
     so.k[j] = r * rb + 16 * cp;
     so.t[j] = r * (kD * 4) + 32 * cp;
+    so.kr[j] = r;
+    so.kcp[j] = cp;
   }
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
@@ -189,11 +219,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, uint3
                                            0x00020000);
 }
 
-template <int NW>
+// With OTF the cos/sin of the staged keys are computed from their positions
+// (p0 = position of frame 0) instead of read from the table.
+template <int NW, bool OTF>
 __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
                                            const bf16* __restrict__ v, size_t rs, int T, int kt0,
-                                           bool rope, const float* __restrict__ table,
-                                           int64_t row0, const StageOffs<NW>& so) {
+                                           bool rope, const PrefillArgs& a, int64_t trow0,
+                                           int64_t p0, const StageOffs<NW>& so) {
   const uint32_t nrows = (uint32_t)max(min(T - kt0, kBN), 0);
   const uint32_t rb = (uint32_t)(rs * sizeof(bf16));
   const auto kr = rows_rsrc(k + (size_t)kt0 * rs, nrows * rb);
@@ -202,11 +234,17 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
   for (int j = 0; j < Stage<NW>::UK; ++j) {
     st.kx[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j], 0, 0);
     st.ky[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j] + 2 * kHalf, 0, 0);
-    {
+    if (OTF) {
+      if (rope) {
+        const int64_t p = p0 + kt0 + so.kr[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rope_cs(p, freq8(a.fr, so.kcp[j], e), &st.kc[j][e], &st.ks[j][e]);
+      }
+    } else {
       // without RoPE the table loads still go out, against an empty
       // descriptor (zeros, no memory access), so the count of loads per tile
       // does not depend on a runtime flag
-      const auto tr = rows_rsrc(table + (row0 + kt0) * kD, rope ? nrows * (kD * 4) : 0u);
+      const auto tr = rows_rsrc(a.table + (trow0 + kt0) * kD, rope ? nrows * (kD * 4) : 0u);
       const f32x4 c0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j], 0, 0));
       const f32x4 c1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j] + 16, 0, 0));
       const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, so.t[j] + 4 * kHalf, 0, 0));
@@ -282,7 +320,7 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
   }
 }
 
-template <int NW, typename TO, bool SEED>
+template <int NW, typename TO, bool SEED, bool OTF>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
                                                                   int n_short, int hx, int cpx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
@@ -299,13 +337,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   // fixed batch: stream b at rows b*T ..; varlen: rows cu[b] .. cu[b+1]-1
   int T = a.T;
   size_t row0 = (size_t)b * a.T;
+  bool bad = false;
   if (a.cu) {
     const int c0 = min(max(a.cu[b], 0), a.total);
     const int c1 = min(max(a.cu[b + 1], c0), a.total);
     row0 = (size_t)c0;
-    T = min(c1 - c0, a.T);
-    if (SEED && h == 0 && qt == 0 && threadIdx.x == 0) a.pos_out[b] = T;
-    if (qt * NW * 32 >= T) return;
+    T = c1 - c0;
+    if (T > a.T) {
+      bad = true;  // a stream longer than the call's bound: NaN rows, pos untouched
+    } else {
+      if (SEED && h == 0 && qt == 0 && threadIdx.x == 0) a.pos_out[b] = T;
+      if (qt * NW * 32 >= T) return;
+    }
   }
   // T and row0 are the same in every lane; saying so keeps the buffer
   // descriptors built from them in scalar registers
@@ -320,6 +363,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const bf16* __restrict__ v = (const bf16*)a.v + base;
   TO* __restrict__ o = (TO*)a.o + base;
   const bool rope = a.rope;
+
+  // positions: frame t at p0 + t; its cos/sin at table row trow0 + t
+  const int64_t p0 = a.pos0 ? a.pos0[b] : 0;
+  const int64_t trow0 = a.table_bstride * b + (a.table_pos ? p0 : 0) + a.table_off;
+  if (p0 < 0) bad = true;
+  if (!OTF && rope && (trow0 < 0 || trow0 + T > a.table_len)) bad = true;
+  if (bad) {
+    // every row of this entry and head is NaN, written by query tile 0
+    if (qt == 0) poison_rows<TO>(o, rs, 0, T);
+    return;
+  }
 
   const int q0 = qt * BM;
   const int qw = q0 + wave * 32;
@@ -344,13 +398,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   constexpr int NQT = BM * 16 / NT;  // table chunks per thread
   static_assert(BM * kRowQT <= 2 * kStageBytes, "Q table rows must fit in LDS");
   u32x4 tq_rows[NQT];
-  if (rope) {
+  if (rope && !OTF) {
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
       const int i = tid + j * NT;
       const int r = i >> 4, c = i & 15;
       const int row = min(q0 + r, T - 1);
-      tq_rows[j] = *reinterpret_cast<const u32x4*>(a.table + (a.table_row0 + row) * kD + 4 * c);
+      tq_rows[j] = *reinterpret_cast<const u32x4*>(a.table + (trow0 + row) * kD + 4 * c);
     }
   }
   u32x4 qx[2], qy[2];
@@ -365,8 +419,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
   Stage<NW> st;
   const StageOffs<NW> so = stage_offsets<NW>(tid, rs);
-  stage_load<NW>(st, k, v, rs, T, it0 * kBN, rope, a.table, a.table_row0, so);
-  if (rope) {
+  stage_load<NW, OTF>(st, k, v, rs, T, it0 * kBN, rope, a, trow0, p0, so);
+  if (rope && !OTF) {
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
       const int i = tid + j * NT;
@@ -380,10 +434,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     const int c = 2 * pr + hh;
     u32x4 x = qx[pr], y = qy[pr];
     if (rope) {
-      const float* cs = reinterpret_cast<const float*>(lds + (min(tq, T - 1) - q0) * kRowQT) + 8 * c;
       float cc[8], ss[8], xf[8], yf[8];
-      load8(cs, cc);
-      load8(cs + kHalf, ss);
+      if (OTF) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rope_cs(p0 + min(tq, T - 1), freq8(a.fr, c, e), &cc[e], &ss[e]);
+      } else {
+        const float* cs =
+            reinterpret_cast<const float*>(lds + (min(tq, T - 1) - q0) * kRowQT) + 8 * c;
+        load8(cs, cc);
+        load8(cs + kHalf, ss);
+      }
       unpack8(x, xf);
       unpack8(y, yf);
 #pragma unroll
@@ -417,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const float c2 = a.scale_log2;
   const unsigned wm1 = (unsigned)(W - 1);
 
-  if (rope) __syncthreads();  // every wave has read its Q table rows
+  if (rope && !OTF) __syncthreads();  // every wave has read its Q table rows
   // ring seeding: this workgroup writes its own query rows, as keys, for
   // frames in the stream's last W
   Seed sd0{};
@@ -440,7 +500,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   for (int it = it0; it <= it1; ++it) {
     const int buf = (it - it0) & 1;
     // the next tile's loads (past the last tile: an empty descriptor)
-    stage_load<NW>(st, k, v, rs, T, (it + 1) * kBN, rope, a.table, a.table_row0, so);
+    stage_load<NW, OTF>(st, k, v, rs, T, (it + 1) * kBN, rope, a, trow0, p0, so);
 
     const char* Kb = lds + buf * kStageBytes;
     const char* Vb = Kb + kTileK;
@@ -585,6 +645,13 @@ int cus_per_xcd() {
   return c;
 }
 
+template <int NW, typename TO, bool SEED, bool OTF>
+void launch_k(dim3 g, dim3 blk, hipStream_t st, const PrefillArgs& a, int n_qtiles, int n_short,
+              int hx, int cpx) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF>), g, blk, 0, st, a, n_qtiles, n_short,
+                     hx, cpx);
+}
+
 template <int NW>
 hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   constexpr int BM = NW * 32;
@@ -595,16 +662,27 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   const int cpx = cus_per_xcd();
   const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
   const dim3 g((unsigned)grid), blk(NW * 64);
+  const bool otf = a.rope && !a.table;  // no table: cos/sin computed in the kernel
   if (a.ring_k) {
-    if (out == DT::BF16)
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, true>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
-    else
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, true>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
+    // (seeding with in-kernel cos/sin runs four-wave workgroups only: the
+    // two-wave variant would need more than 256 VGPRs)
+    if constexpr (NW == 4) {
+      if (otf) {
+        if (out == DT::BF16) launch_k<NW, bf16, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+        else launch_k<NW, float, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+        return hipGetLastError();
+      }
+    }
+    if (out == DT::BF16) launch_k<NW, bf16, true, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    else launch_k<NW, float, true, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
   } else {
-    if (out == DT::BF16)
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, bf16, false>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
-    else
-      hipLaunchKernelGGL((prefill_mfma_kernel<NW, float, false>), g, blk, 0, st, a, n_qtiles, n_short, hx, cpx);
+    if (out == DT::BF16) {
+      if (otf) launch_k<NW, bf16, false, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+      else launch_k<NW, bf16, false, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    } else {
+      if (otf) launch_k<NW, float, false, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+      else launch_k<NW, float, false, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    }
   }
   return hipGetLastError();
 }
@@ -616,7 +694,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st) {
   // queries; two-wave ones keep enough workgroups to cover the 256 CUs when
   // the problem is small.
   const int64_t wg4 = (int64_t)((a.T + 127) / 128) * a.H * a.B;
-  if (wg4 >= 256) return launch_nw<4>(a, out, st);
+  if (wg4 >= 256 || (a.ring_k && a.rope && !a.table)) return launch_nw<4>(a, out, st);
   return launch_nw<2>(a, out, st);
 }
 

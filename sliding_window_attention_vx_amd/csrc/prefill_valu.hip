@@ -14,6 +14,19 @@ namespace {
 
 constexpr int kTile = 64;
 
+// cos/sin of position p: the table row, or the same float64 angle computed
+// here when there is no table (frequencies from LDS, fr_lds).
+__device__ __forceinline__ void row_cs(const PrefillArgs& a, const double* fr_lds, int64_t trow,
+                                       int64_t p, float cs[kD]) {
+  if (a.table) {
+#pragma unroll
+    for (int i = 0; i < kD; i += 8) load8(a.table + trow * kD + i, cs + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) rope_cs(p, fr_lds[i], &cs[i], &cs[kHalf + i]);
+  }
+}
+
 template <typename TI>
 __device__ __forceinline__ void load_rot_row(const TI* __restrict__ src, const float* __restrict__ cs,
                                              bool rope, float out[kD]) {
@@ -50,11 +63,31 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
   const int t = q0 + lane;
   const size_t rs = (size_t)H * kD;  // stride between frames
   const size_t base = (size_t)b * T * rs + (size_t)h * kD;
+  // frame t at position p0 + t, its cos/sin at table row trow0 + t; invalid
+  // positions or table rows make every output of the tile NaN
+  const int64_t p0 = a.pos0 ? a.pos0[b] : 0;
+  const int64_t trow0 = a.table_bstride * b + (a.table_pos ? p0 : 0) + a.table_off;
+  if (p0 < 0 || (a.rope && a.table && (trow0 < 0 || trow0 + T > a.table_len))) {
+    if (t < T) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_nanf("");
+#pragma unroll
+      for (int c = 0; c < 8; ++c) store8(o + base + (size_t)t * rs + 8 * c, x);
+    }
+    return;
+  }
+  float cs[kD];
+  // the frequencies, for cos/sin computed here (a table-less call): read
+  // from LDS, not held in registers across the kernel
+  __shared__ double fr_lds[kHalf];
+  if (lane < kHalf) fr_lds[lane] = a.fr.f[lane];
+  __syncthreads();
 
   float qr[kD];
   if (t < T) {
-    load_rot_row<TI>(q + base + (size_t)t * rs, a.rope ? a.table + (a.table_row0 + t) * kD : nullptr,
-                     a.rope, qr);
+    if (a.rope) row_cs(a, fr_lds, trow0 + t, p0 + t, cs);
+    load_rot_row<TI>(q + base + (size_t)t * rs, cs, a.rope, qr);
   } else {
 #pragma unroll
     for (int d = 0; d < kD; ++d) qr[d] = 0.f;
@@ -70,8 +103,8 @@ __global__ __launch_bounds__(64) void prefill_valu_kernel(PrefillArgs a) {
     const int key = k0 + lane;
     if (key < kend) {
       float row[kD];
-      load_rot_row<TI>(k + base + (size_t)key * rs,
-                       a.rope ? a.table + (a.table_row0 + key) * kD : nullptr, a.rope, row);
+      if (a.rope) row_cs(a, fr_lds, trow0 + key, p0 + key, cs);
+      load_rot_row<TI>(k + base + (size_t)key * rs, cs, a.rope, row);
 #pragma unroll
       for (int d = 0; d < kD; ++d) Ks[lane][d] = row[d];
       const TI* vp = v + base + (size_t)key * rs;

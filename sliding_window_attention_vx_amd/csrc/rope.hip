@@ -17,17 +17,41 @@ __global__ void rope_table_kernel(float* __restrict__ table, int64_t p_begin, in
   table[j * kD + kHalf + i] = s;
 }
 
+// Rows b*T + t of a table for batch entries at their own positions:
+// cos/sin of position pos0[b] + t (pos0 nullptr = 0).  Used as the prefill's
+// cos/sin cache when the caller gives a workspace instead of a table.
+__global__ void rope_table_batched_kernel(float* __restrict__ table,
+                                          const int64_t* __restrict__ pos0, int T, int64_t rows,
+                                          RopeFreqs fr) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * kHalf) return;
+  const int64_t j = idx / kHalf;
+  const int i = (int)(idx % kHalf);
+  const int64_t b = j / T;
+  const int64_t p = (pos0 ? pos0[b] : 0) + (j - b * T);
+  float c, s;
+  rope_cs(p, fr.f[i], &c, &s);
+  table[j * kD + i] = c;
+  table[j * kD + kHalf + i] = s;
+}
+
 // One workgroup per (b, t) row: the row's 32 cos/sin pairs go to LDS once and
 // serve every head of q and k.  A thread rotates 8 pairs (two 8-element chunks).
+// Frame t of batch entry b is at position pos0[b] + t; a negative pos0[b]
+// is an invalid position and makes the entry's rows NaN (loud, not partial).
 template <typename T>
 __global__ __launch_bounds__(128) void rope_qk_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                      int T_, int H, int64_t pos0, RopeFreqs fr) {
+                                                      int T_, int H,
+                                                      const int64_t* __restrict__ pos0,
+                                                      RopeFreqs fr) {
   __shared__ float cs[2][kHalf];
   const int64_t row = blockIdx.x;  // b * T + t
   const int t = (int)(row % T_);
+  const int64_t p0 = pos0 ? pos0[row / T_] : 0;
   if (threadIdx.x < kHalf) {
     float c, s;
-    rope_cs(pos0 + t, fr.f[threadIdx.x], &c, &s);
+    rope_cs(p0 + t, fr.f[threadIdx.x], &c, &s);
+    if (p0 < 0) c = s = __builtin_nanf("");
     cs[0][threadIdx.x] = c;
     cs[1][threadIdx.x] = s;
   }
@@ -64,7 +88,17 @@ hipError_t launch_rope_table(float* table, int64_t p_begin, int count, const Rop
   return hipGetLastError();
 }
 
-hipError_t launch_rope_qk(void* q, void* k, int B, int T, int H, int64_t pos0, DT io,
+hipError_t launch_rope_table_batched(float* table, const int64_t* pos0, int B, int T,
+                                     const RopeFreqs& fr, hipStream_t st) {
+  const int64_t rows = (int64_t)B * T;
+  const int threads = 256;
+  const int64_t blocks = (rows * kHalf + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_table_batched_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
+                     table, pos0, T, rows, fr);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_qk(void* q, void* k, int B, int T, int H, const int64_t* pos0, DT io,
                           const RopeFreqs& fr, hipStream_t st) {
   const unsigned blocks = (unsigned)((int64_t)B * T);
   if (io == DT::BF16)

@@ -60,6 +60,17 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// NaN over the outputs of new queries i0 .. i1-1 of one (stream, head).
+template <typename TO>
+__device__ void poison_queries(TO* o, size_t frs, int i0, int i1) {
+  for (int u = threadIdx.x; u < (i1 - i0) * 8; u += blockDim.x) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __builtin_nanf("");
+    store8(o + (size_t)(i0 + u / 8) * frs + 8 * (u % 8), x);
+  }
+}
+
 // Dynamic LDS layout of stream_step_kernel for i1 new keys.
 struct StepLds {
   size_t cs, knew, qs, sc, red, total;
@@ -92,12 +103,17 @@ __global__ __launch_bounds__(256) void stream_step_kernel(StreamArgs a, RopeFreq
   float* red = (float*)(smem + L.red);
 
   const int64_t P = a.pos[s];
+  const size_t frs = (size_t)H * kD;
+  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
+  if (P < 0) {
+    // an invalid position: the stream's outputs are NaN (loud, not partial)
+    poison_queries<TO>((TO*)a.o + fbase, frs, i0, i1);
+    return;
+  }
   const int64_t lo = max((int64_t)0, P + i0 - W + 1);
   const int nring = (int)max((int64_t)0, P - lo);  // ring keys at positions lo .. P-1
   const int nk = nring + i1;
   const int lo_slot = (int)(lo % W);  // ring key kk sits at slot lo_slot + kk (mod W), kk < W
-  const size_t frs = (size_t)H * kD;
-  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
   const TI* __restrict__ qn = (const TI*)a.q + fbase;
   const TI* __restrict__ kn = (const TI*)a.k + fbase;
   const TI* __restrict__ vn = (const TI*)a.v + fbase;
@@ -383,12 +399,19 @@ __global__ __launch_bounds__(kSWaves * 64, 4) void stream_step_mfma_kernel(Strea
   char* kbuf = vbuf + kSBufV;
 
   const int64_t P = a.pos[s];
+  const size_t frs = (size_t)H * kD;
+  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
+  if (P < 0) {
+    // an invalid position: the stream's outputs are NaN, its ring is not
+    // written and its position stays as it was (loud, not partial)
+    poison_queries<TO>((TO*)a.o + fbase, frs, i0, i1);
+    if (a.append && h == 0 && i0 == 0 && tid == 0) a.pos_out[s] = P;
+    return;
+  }
   const int64_t lo = max((int64_t)0, P + i0 - W + 1);
   const int nring = (int)max((int64_t)0, P - lo);  // ring keys at positions lo .. P-1
   const int nk = nring + i1;                       // then new frames 0 .. i1-1
   const int lo_slot = (int)(lo % W);
-  const size_t frs = (size_t)H * kD;
-  const size_t fbase = (size_t)s * n * frs + (size_t)h * kD;
   const bf16* __restrict__ qn = (const bf16*)a.q + fbase;
   const bf16* __restrict__ kn = (const bf16*)a.k + fbase;
   const bf16* __restrict__ vn = (const bf16*)a.v + fbase;
@@ -699,7 +722,12 @@ __global__ __launch_bounds__(256) void ring_append_kernel(AppendArgs a, RopeFreq
   const int H = a.H, W = a.W, n = a.n;
   const int tid = threadIdx.x;
   const int64_t P = a.pos[s];
-  const int p_slot = (int)(((P % W) + W) % W);  // slot of position P
+  if (P < 0) {
+    // an invalid position: nothing is appended and the position is kept
+    if (tid == 0) a.pos_out[s] = P;
+    return;
+  }
+  const int p_slot = (int)(P % W);  // slot of position P
   if (a.rope) {
     for (int u = tid; u < n * kHalf; u += blockDim.x) {
       const int i = u / kHalf, f = u % kHalf;

@@ -61,6 +61,10 @@ vx_status check_cfg(const vx_attn_cfg* cfg) {
   if (io == VX_F32 && out == VX_BF16)
     return fail(VX_E_DTYPE, "float32 inputs with bfloat16 output is not supported");
   if (cfg->flags & ~VX_FLAG_VALU_KERNEL) return fail(VX_E_RANGE, "unknown flag bits 0x%x", cfg->flags);
+  if (cfg->workspace_bytes > 0 && !cfg->workspace)
+    return fail(VX_E_NULL, "workspace is NULL but workspace_bytes is %zu", cfg->workspace_bytes);
+  if (cfg->workspace && !aligned16(cfg->workspace))
+    return fail(VX_E_ALIGN, "workspace is not 16-byte aligned");
   return VX_OK;
 }
 
@@ -137,6 +141,8 @@ void vx_default_cfg(vx_attn_cfg* cfg) {
   cfg->io_dtype = VX_BF16;
   cfg->out_dtype = VX_BF16;
   cfg->flags = 0;
+  cfg->workspace = nullptr;
+  cfg->workspace_bytes = 0;
 }
 
 void vx_default_gqa_cfg(vx_attn_cfg* cfg) {
@@ -148,6 +154,8 @@ void vx_default_gqa_cfg(vx_attn_cfg* cfg) {
   cfg->io_dtype = VX_BF16;
   cfg->out_dtype = VX_BF16;
   cfg->flags = 0;
+  cfg->workspace = nullptr;
+  cfg->workspace_bytes = 0;
 }
 
 vx_status vx_rope_table(float* table, int64_t p_begin, int32_t count, const vx_attn_cfg* cfg,
@@ -170,12 +178,12 @@ vx_status vx_rope_table(float* table, int64_t p_begin, int32_t count, const vx_a
                                         (hipStream_t)stream));
 }
 
-vx_status vx_rope_qk(void* q, void* k, int32_t B, int32_t T, int32_t H, int64_t pos0,
+vx_status vx_rope_qk(void* q, void* k, int32_t B, int32_t T, int32_t H, const int64_t* pos0,
                      const vx_attn_cfg* cfg, void* stream) {
   vx_status st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_dims("rope_qk", B, T, H))) return st;
-  if (pos0 < 0 || pos0 > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "pos0 out of range");
+  if (pos0 && ((uintptr_t)pos0 & 7u) != 0) return fail(VX_E_ALIGN, "pos0 is not 8-byte aligned");
   if ((int64_t)B * T == 0) return ok();
   if (H < 1) return fail(VX_E_SHAPE, "H must be >= 1");
   if ((int64_t)B * T * H > kMaxRows) return fail(VX_E_SHAPE, "B*T*H too large");
@@ -188,14 +196,19 @@ vx_status vx_rope_qk(void* q, void* k, int32_t B, int32_t T, int32_t H, int64_t 
                                      rope_freqs(cfg->rope_theta), (hipStream_t)stream));
 }
 
+// Bytes of the cos/sin table the prefill builds in the workspace: B*T rows.
+size_t prefill_table_bytes(int32_t B, int32_t T) {
+  return (size_t)B * T * vx::kD * sizeof(float);
+}
+
 vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t B,
-                              int32_t T, int32_t H, int64_t pos0, int32_t rope_applied,
+                              int32_t T, int32_t H, const int64_t* pos0, int32_t rope_applied,
                               const float* rope_table, int64_t table_p0, int64_t table_len,
                               const vx_attn_cfg* cfg, void* stream) {
   vx_status st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_dims("prefill", B, T, H))) return st;
-  if (pos0 < 0 || pos0 > ((int64_t)1 << 52)) return fail(VX_E_RANGE, "pos0 out of range");
+  if (pos0 && ((uintptr_t)pos0 & 7u) != 0) return fail(VX_E_ALIGN, "pos0 is not 8-byte aligned");
   if ((int64_t)B * T == 0) return ok();
   if (H < 1) return fail(VX_E_SHAPE, "H must be >= 1");
   if (B > 65535 || H > 65535) return fail(VX_E_SHAPE, "B and H must be <= 65535");
@@ -207,6 +220,12 @@ vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void*
   const size_t ib = n * elem_size(cfg->io_dtype), ob = n * elem_size(cfg->out_dtype);
   if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib))
     return fail(VX_E_RANGE, "o overlaps an input");
+  if (cfg->workspace &&
+      (overlap(cfg->workspace, cfg->workspace_bytes, o, ob) ||
+       overlap(cfg->workspace, cfg->workspace_bytes, q, ib) ||
+       overlap(cfg->workspace, cfg->workspace_bytes, k, ib) ||
+       overlap(cfg->workspace, cfg->workspace_bytes, v, ib)))
+    return fail(VX_E_RANGE, "the workspace overlaps a tensor");
   vx::PrefillArgs a{};
   a.q = q;
   a.k = k;
@@ -219,23 +238,45 @@ vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void*
   a.pos0 = pos0;
   a.rope = rope_applied == 0;
   a.scale_log2 = scale_log2(cfg);
+  a.fr = rope_freqs(cfg->rope_theta);
+  const bool valu = (cfg->flags & VX_FLAG_VALU_KERNEL) || cfg->io_dtype == VX_F32;
+  bool build_table = false;
   if (a.rope) {
-    if (!rope_table) return fail(VX_E_NULL, "rope_table is NULL and rope_applied == 0");
-    if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "rope_table is not 16-byte aligned");
-    if (table_p0 < 0 || table_len < 0 || pos0 < table_p0 || pos0 + T > table_p0 + table_len)
-      return fail(VX_E_RANGE,
-                  "rope_table covers positions [%lld, %lld) but the chunk needs [%lld, %lld)",
-                  (long long)table_p0, (long long)(table_p0 + table_len), (long long)pos0,
-                  (long long)(pos0 + T));
-    a.table = rope_table;
-    a.table_row0 = pos0 - table_p0;
+    if (rope_table) {
+      if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "rope_table is not 16-byte aligned");
+      if (table_p0 < 0 || table_len < 0) return fail(VX_E_RANGE, "table_p0 and table_len must be >= 0");
+      if (!pos0 && (table_p0 > 0 || table_len < T))
+        return fail(VX_E_RANGE,
+                    "rope_table covers positions [%lld, %lld) but the chunk needs [0, %d)",
+                    (long long)table_p0, (long long)(table_p0 + table_len), T);
+      a.table = rope_table;
+      a.table_off = -table_p0;
+      a.table_len = table_len;
+    } else if (cfg->workspace && cfg->workspace_bytes >= prefill_table_bytes(B, T)) {
+      // a table of exactly the call's positions, row b*T + t, in the workspace
+      build_table = true;
+      a.table = (const float*)cfg->workspace;
+      a.table_bstride = T;
+      a.table_pos = false;
+      a.table_len = (int64_t)B * T;
+    }  // else: cos/sin computed in the kernel
   }
   (void)hipGetLastError();
-  const bool valu = (cfg->flags & VX_FLAG_VALU_KERNEL) || cfg->io_dtype == VX_F32;
+  if (build_table) {
+    vx_status s1 = launched(vx::launch_rope_table_batched((float*)a.table, pos0, B, T, a.fr,
+                                                          (hipStream_t)stream));
+    if (s1) return s1;
+  }
   if (valu)
     return launched(vx::launch_prefill_valu(a, to_dt(cfg->io_dtype), to_dt(cfg->out_dtype),
                                             (hipStream_t)stream));
   return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
+}
+
+size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
+                                          const vx_attn_cfg* cfg) {
+  if (check_cfg(cfg) != VX_OK || check_dims("prefill", B, T, H) != VX_OK) return 0;
+  return prefill_table_bytes(B, T);
 }
 
 vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
@@ -289,9 +330,9 @@ vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v
   a.T = max_T;
   a.H = H;
   a.W = cfg->window;
-  a.pos0 = 0;
   a.rope = rope_applied == 0;
   a.scale_log2 = scale_log2(cfg);
+  a.fr = rope_freqs(cfg->rope_theta);
   a.cu = cu_seqlens;
   a.total = total;
   if (seed) {
@@ -299,15 +340,15 @@ vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v
     a.ring_v = ring_v;
     a.pos_out = pos;
   }
-  if (a.rope) {
-    if (!rope_table) return fail(VX_E_NULL, "rope_table is NULL and rope_applied == 0");
+  if (a.rope && rope_table) {  // without a table: cos/sin computed in the kernel
     if (!aligned16(rope_table)) return fail(VX_E_ALIGN, "rope_table is not 16-byte aligned");
     if (table_p0 < 0 || table_len < 0 || table_p0 > 0 || max_T > table_p0 + table_len)
       return fail(VX_E_RANGE,
                   "rope_table covers positions [%lld, %lld) but the chunks need [0, %d)",
                   (long long)table_p0, (long long)(table_p0 + table_len), max_T);
     a.table = rope_table;
-    a.table_row0 = -table_p0;
+    a.table_off = -table_p0;
+    a.table_len = table_len;
   }
   (void)hipGetLastError();
   return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));

@@ -17,16 +17,29 @@ struct PrefillArgs {
   const void* v;
   void* o;
   int B, T, H, W;
-  int64_t pos0;
-  bool rope;            // rotate q, k on load (table must be valid)
-  const float* table;   // [.., 2, 32] cos/sin rows
-  int64_t table_row0;   // table row of position pos0 (= pos0 - table_p0)
+  // Frame t of batch entry b sits at position pos0[b] + t (pos0: device int64
+  // [B], nullptr = 0).  A negative pos0[b] makes that entry's outputs NaN.
+  const int64_t* pos0 = nullptr;
+  bool rope;            // rotate q, k on load
+  // cos/sin of frame t of batch entry b: table row
+  //   b * table_bstride + (table_pos ? pos0[b] : 0) + t + table_off
+  // of a [rows][2][32] float32 table with table_len rows; an entry whose rows
+  // fall outside [0, table_len) gets NaN outputs.  table == nullptr with rope:
+  // cos/sin are computed on the fly from fr (the same float64 angle, so the
+  // same values as a table).
+  const float* table = nullptr;
+  int64_t table_off = 0;
+  int64_t table_bstride = 0;
+  bool table_pos = true;
+  int64_t table_len = 0;
+  RopeFreqs fr;
   float scale_log2;     // softmax scale * log2(e)
   // Varlen batch (cu != nullptr): B streams packed along the frame axis,
-  // stream b at rows cu[b] .. cu[b+1]-1 (length at most T), each at positions
-  // pos0 .. pos0 + length - 1.  Ring seeding (ring_k != nullptr): the rotated
-  // keys and the values of frames t >= length - W go to slot t mod W of the
-  // stream's [H, W, 64] rings, and pos_out[b] = length.
+  // stream b at rows cu[b] .. cu[b+1]-1, each at positions 0 .. length - 1.
+  // A stream longer than T gets NaN outputs and its pos_out is left alone.
+  // Ring seeding (ring_k != nullptr): the rotated keys and the values of
+  // frames t >= length - W go to slot t mod W of the stream's [H, W, 64]
+  // rings, and pos_out[b] = length.
   const int32_t* cu = nullptr;
   int total = 0;        // packed rows (offsets are clamped to [0, total])
   void* ring_k = nullptr;
@@ -66,8 +79,13 @@ struct AppendArgs {
 
 hipError_t launch_rope_table(float* table, int64_t p_begin, int count, const RopeFreqs& fr,
                              hipStream_t st);
-hipError_t launch_rope_qk(void* q, void* k, int B, int T, int H, int64_t pos0, DT io,
+// In-place rotation; frame t of batch entry b at position pos0[b] + t
+// (pos0: device int64 [B] or nullptr = 0; a negative entry makes its rows NaN).
+hipError_t launch_rope_qk(void* q, void* k, int B, int T, int H, const int64_t* pos0, DT io,
                           const RopeFreqs& fr, hipStream_t st);
+// Table rows b*T + t = cos/sin of position pos0[b] + t (pos0 nullptr = 0).
+hipError_t launch_rope_table_batched(float* table, const int64_t* pos0, int B, int T,
+                                     const RopeFreqs& fr, hipStream_t st);
 hipError_t launch_prefill_valu(const PrefillArgs& a, DT io, DT out, hipStream_t st);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st);
 hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreqs& fr,

@@ -43,7 +43,7 @@ def test_header_declares_the_four_calls():
               "vx_last_error", "vx_version", "vx_default_cfg", "vx_swa_attn_prefill_varlen",
               "vx_default_gqa_cfg", "vx_gqa_attn_prefill", "vx_gqa_attn_decode", "vx_linear",
               "vx_enc_qkv_rope", "vx_enc_attn_step", "vx_rmsnorm", "vx_enc_stem_step",
-              "vx_enc_layer_step", "vx_enc_step"):
+              "vx_enc_layer_step", "vx_enc_step", "vx_swa_attn_prefill_workspace_size"):
         assert f in names
 
 
@@ -77,6 +77,7 @@ def test_default_cfg(L):
     L.vx_default_cfg(ctypes.byref(c))
     assert (c.head_dim, c.window, c.rope_theta, c.softmax_scale, c.io_dtype, c.out_dtype, c.flags) \
         == (64, 750, 1e6, 0.125, vx.VX_BF16, vx.VX_BF16, 0)
+    assert (c.workspace, c.workspace_bytes) == (None, 0)
     assert L.vx_version() >= 100
 
 
@@ -112,7 +113,7 @@ def cfg(**kw):
     return c
 
 
-def prefill(L, b, c, q=None, k=None, v=None, o=None, B=1, T=8, H=2, pos0=0, rope_applied=1,
+def prefill(L, b, c, q=None, k=None, v=None, o=None, B=1, T=8, H=2, pos0=None, rope_applied=1,
             table=None, tp0=0, tlen=0):
     q = q if q is not None else b.new()
     k = k if k is not None else b.new()
@@ -150,15 +151,37 @@ def test_prefill_argument_errors(L):
     assert prefill(L, b, c, v=mis) == E_ALIGN
     q = b.new()
     assert prefill(L, b, c, q=q, o=q) == E_RANGE  # o aliases q
-    assert prefill(L, b, c, pos0=-1) == E_RANGE
-    # rope on load needs a table covering pos0 .. pos0+T-1
-    assert prefill(L, b, c, rope_applied=0) == E_NULL
+    # pos0 is a device int64 array: only its alignment is checked on the host
+    assert prefill(L, b, c, pos0=ctypes.c_void_p(b.new().value + 4)) == E_ALIGN
+    # a table must cover the chunk's positions 0 .. T-1 when pos0 is NULL
     t = b.new()
     assert prefill(L, b, c, rope_applied=0, table=t, tp0=0, tlen=7) == E_RANGE
-    assert prefill(L, b, c, rope_applied=0, table=t, tp0=5, tlen=100, pos0=4) == E_RANGE
+    assert prefill(L, b, c, rope_applied=0, table=t, tp0=5, tlen=100) == E_RANGE
+    assert prefill(L, b, c, rope_applied=0, table=t, tp0=-1, tlen=100) == E_RANGE
     assert prefill(L, b, c, rope_applied=0, table=ctypes.c_void_p(t.value + 4), tp0=0,
                    tlen=100) == E_ALIGN
     assert b.untouched()
+
+
+def test_prefill_workspace_checks(L):
+    b = Bufs()
+    ws = b.new()
+    assert prefill(L, b, cfg(workspace=None, workspace_bytes=64)) == E_NULL
+    assert prefill(L, b, cfg(workspace=ctypes.c_void_p(ws.value + 8), workspace_bytes=64)) == E_ALIGN
+    q = b.new()
+    assert prefill(L, b, cfg(workspace=q, workspace_bytes=64), q=q) == E_RANGE  # overlaps q
+    assert b.untouched()
+
+
+def test_prefill_workspace_size(L):
+    size = L.vx_swa_attn_prefill_workspace_size
+    c = cfg()
+    # a cos/sin table of B*T rows of 256 bytes
+    assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256
+    assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256
+    assert size(1, 1500, 32, None) == 0
+    assert size(-1, 1500, 32, ctypes.byref(c)) == 0
+    assert size(1, 1500, 32, ctypes.byref(cfg(window=0))) == 0
 
 
 def test_prefill_empty_is_ok_without_launch(L):
@@ -204,7 +227,6 @@ def test_prefill_varlen_argument_errors(L):
     assert prefill_varlen(L, b, c, seed=True, max_T=0, total=0) == E_SHAPE
     # the table must start at position 0 and cover max_T positions
     t = b.new()
-    assert prefill_varlen(L, b, c, rope_applied=0) == E_NULL
     assert prefill_varlen(L, b, c, rope_applied=0, table=t, tp0=0, tlen=7) == E_RANGE
     assert prefill_varlen(L, b, c, rope_applied=0, table=t, tp0=1, tlen=100) == E_RANGE
     assert b.untouched()
@@ -294,7 +316,7 @@ def test_rope_qk_and_table_errors(L):
     assert L.vx_rope_qk(z, z, 1, 4, 2, 0, ctypes.byref(c), z) == E_NULL
     q = b.new()
     assert L.vx_rope_qk(q, q, 1, 4, 2, 0, ctypes.byref(c), z) == E_RANGE
-    assert L.vx_rope_qk(q, z, 1, 4, 2, -1, ctypes.byref(c), z) == E_RANGE
+    assert L.vx_rope_qk(q, z, 1, 4, 2, ctypes.c_void_p(q.value + 4), ctypes.byref(c), z) == E_ALIGN
     assert L.vx_rope_qk(ctypes.c_void_p(q.value + 4), z, 1, 4, 2, 0, ctypes.byref(c), z) == E_ALIGN
     assert L.vx_rope_qk(q, z, 1, 4, -2, 0, ctypes.byref(c), z) == E_SHAPE
     assert L.vx_rope_table(z, 0, 10, ctypes.byref(c), z) == E_NULL

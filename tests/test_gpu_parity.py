@@ -197,8 +197,8 @@ def test_prefill_position_offset_and_table_window():
     got = run_prefill(x, 750, "bf16", pos0=12345, table=table, table_p0=12000)
     want = oracle.prefill(x["q"], x["k"], x["v"], 750, pos=12345, bf16=True)
     check_bf16(got, want, "pos0 12345")
-    with pytest.raises(vx.VxError):
-        run_prefill(x, 750, "bf16", pos0=13700, table=table, table_p0=12000)
+    # positions 13700 .. 14099 run past the table: found on the device, loud
+    assert np.all(np.isnan(run_prefill(x, 750, "bf16", pos0=13700, table=table, table_p0=12000)))
 
 
 def test_stack_layer_sampled():
