@@ -151,6 +151,21 @@ vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void 
 size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
                                           const vx_attn_cfg *cfg);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as vx_swa_attn_prefill with rope_table == NULL and a workspace, but
+ * the cos/sin rows live in a library-owned static device array of 16 MiB
+ * (one per GPU, held until the process ends), so the call allocates nothing.
+ * cfg->workspace is ignored.  Requires B*T <= 65536 when rope_applied == 0
+ * (VX_E_SHAPE otherwise, nothing launched).  Every call on a GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * host threads) race and must not be made.  Same results, bit for bit, as
+ * vx_swa_attn_prefill given a table of the same positions. */
+vx_status vx_swa_attn_prefill_noalloc(const void *q, const void *k, const void *v, void *o,
+                                      int32_t B, int32_t T, int32_t H, const int64_t *pos0,
+                                      int32_t rope_applied, const vx_attn_cfg *cfg,
+                                      void *stream);
+
 /* Batched first-chunk prefill over streams of different lengths, which can
  * also seed each stream's KV ring for the streaming step (Voxtral Mini 4B
  * Realtime Core AI page, "Why two encoders?" and the Streaming table: the

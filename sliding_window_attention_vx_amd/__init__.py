@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "VxError", "Config", "lib", "rope_table", "rope_qk", "prefill", "prefill_workspace_size",
-    "prefill_workspace", "prefill_varlen", "stream_step", "ring_append",
+    "prefill_workspace", "prefill_noalloc", "prefill_varlen", "stream_step", "ring_append",
     "stream_step_append", "gqa_prefill", "gqa_decode", "linear", "enc_qkv_rope",
     "enc_attn_step", "rmsnorm", "enc_work", "enc_stem_step", "enc_layer_step", "enc_step",
     "LAYER_KEYS", "STEM_KEYS",
@@ -83,6 +83,8 @@ _SIGS = {
                                            _i64, _i64, ctypes.POINTER(_Cfg), _vp]),
     "vx_swa_attn_prefill_workspace_size": (ctypes.c_size_t, [_i32, _i32, _i32,
                                                              ctypes.POINTER(_Cfg)]),
+    "vx_swa_attn_prefill_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
+                                                   _i32, ctypes.POINTER(_Cfg), _vp]),
     "vx_swa_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                _i32, _i32, ctypes.POINTER(_Cfg), _vp]),
     "vx_kv_ring_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -311,6 +313,35 @@ def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_appl
                                      _ptr(table) if not rope_applied else None, int(table_p0),
                                      int(tlen), ctypes.byref(cfg), _stream(q)),
            "vx_swa_attn_prefill")
+    return out
+
+
+def prefill_noalloc(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0,
+                    rope_applied=False, out=None, out_dtype=None):
+    """prefill() whose cos/sin rows live in the library's static device scratch
+    (no workspace, nothing allocated by the library); B*T <= 65536 rows."""
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(x, name)
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4 or q.shape[-1] != HEAD_DIM:
+        raise ValueError("q, k, v must all be [B, T, H, 64]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, T, H, _ = q.shape
+    io = _dt(q)
+    od = out_dtype or (_dt(out) if out is not None else io)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                          device=q.device)
+    _dev_tensor(out, "out")
+    if out.shape != q.shape or _dt(out) != od:
+        raise ValueError("out has the wrong shape or dtype")
+    p0 = _pos0(pos0, B, q.device)
+    cfg = Config(window, theta, scale, io, od).c()
+    _check(lib().vx_swa_attn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H,
+                                             _ptr(p0), int(bool(rope_applied)),
+                                             ctypes.byref(cfg), _stream(q)),
+           "vx_swa_attn_prefill_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -126,6 +127,36 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 vx_status launched(hipError_t e) {
   if (e != hipSuccess) return fail(VX_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// ---- Library-owned scratch for vx_swa_attn_prefill_noalloc -----------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address (in host code it is a stand-in, not device memory); it uses the
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current and kept per device.
+constexpr size_t kNoAllocBytes = (size_t)16 << 20;  // 65536 cos/sin rows of 256 bytes
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's `scratch`, or NULL with *err set.
+void* scratch_address(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 }  // namespace
@@ -277,6 +308,32 @@ size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
                                           const vx_attn_cfg* cfg) {
   if (check_cfg(cfg) != VX_OK || check_dims("prefill", B, T, H) != VX_OK) return 0;
   return prefill_table_bytes(B, T);
+}
+
+vx_status vx_swa_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
+                                      int32_t B, int32_t T, int32_t H, const int64_t* pos0,
+                                      int32_t rope_applied, const vx_attn_cfg* cfg,
+                                      void* stream) {
+  vx_status st = check_cfg(cfg);
+  if (st) return st;
+  if ((st = check_dims("prefill_noalloc", B, T, H))) return st;
+  if (rope_applied == 0 && prefill_table_bytes(B, T) > kNoAllocBytes)
+    return fail(VX_E_SHAPE,
+                "prefill_noalloc: B*T = %lld rows exceed the library scratch (%zu rows); "
+                "use vx_swa_attn_prefill with a workspace or a table",
+                (long long)B * T, kNoAllocBytes / (vx::kD * sizeof(float)));
+  if ((int64_t)B * T == 0) return ok();
+  vx_attn_cfg c = *cfg;
+  c.workspace = nullptr;
+  c.workspace_bytes = 0;
+  if (rope_applied == 0) {
+    hipError_t e = hipSuccess;
+    void* p = scratch_address(&e);
+    if (!p) return fail(VX_E_HIP, "prefill_noalloc: no scratch address: %s", hipGetErrorString(e));
+    c.workspace = p;
+    c.workspace_bytes = kNoAllocBytes;
+  }
+  return vx_swa_attn_prefill(q, k, v, o, B, T, H, pos0, rope_applied, nullptr, 0, 0, &c, stream);
 }
 
 vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,

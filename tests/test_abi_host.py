@@ -184,6 +184,23 @@ def test_prefill_workspace_size(L):
     assert size(1, 1500, 32, ctypes.byref(cfg(window=0))) == 0
 
 
+def test_prefill_noalloc_host_checks(L):
+    """The allocation-free prefill refuses more rows than its static scratch
+    holds (before any HIP call) and validates like vx_swa_attn_prefill."""
+    b = Bufs()
+    c = cfg()
+    q, k, v, o = b.new(), b.new(), b.new(), b.new()
+    f = L.vx_swa_attn_prefill_noalloc
+    assert f(q, k, v, o, 1, 65537, 1, None, 0, ctypes.byref(c), None) == E_SHAPE
+    assert "scratch" in L.vx_last_error().decode()
+    assert f(q, k, v, o, 2, 40000, 1, None, 0, ctypes.byref(c), None) == E_SHAPE
+    assert f(q, k, v, o, 1, 8, 2, None, 0, None, None) == E_NULL
+    assert f(q, k, v, o, 1, 8, 2, None, 0, ctypes.byref(cfg(window=0)), None) == E_RANGE
+    z = ctypes.c_void_p(0)
+    assert f(z, z, z, z, 0, 8, 2, None, 0, ctypes.byref(c), None) == OK
+    assert b.untouched()
+
+
 def test_prefill_empty_is_ok_without_launch(L):
     c = cfg()
     z = ctypes.c_void_p(0)
