@@ -13,9 +13,12 @@ pre-drawn batches.
 
 Printed value: prefill TFLOP/s over the unmasked band FLOPs
 (4*64*pairs*H*B, pairs = W(W+1)/2 + (T-W)W), from HIP events around
-back-to-back launches on the launch stream.  The streaming step is reported
-in microseconds and GB/s of algorithmic HBM bytes.  The CPU baseline is the
-float64 oracle timed on the host on the same prefill workload.
+back-to-back launches on the launch stream: every leg is timed in 5 passes,
+interleaved with the other legs, and the per-call median is reported.  The
+streaming step runs 200 consecutive steps per pass with positions advancing
+and is reported in microseconds and GB/s of algorithmic HBM bytes.  The CPU
+baseline is the float64 oracle timed on the host on the same prefill
+workload (all host threads, and one thread on a slice of it).
 
 Beside the step, the same line reports the 32-layer attention stack (B4
 T1500 per layer) and the long-form prefill (B8 T6000), the batched first-chunk
@@ -48,26 +51,32 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                "b7d76de672f04327ab5d81353d8c274815dd1c5fb756443519ad93d0e7006def",
-                21_652_096 + 6_144_000),
+                "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
+                21_656_530 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
-               "95d1d5b13d35cc99fb57042be5d3a40dc6c347c74bdda9b9d02adc8f3e80c33a",
-               396_090_112 + 3_146_698),
+               "4b94d8f36c1768bf9e97a79237f965a66a9f69d1e23f335562ccf9299dd6d169",
+               396_092_019 + 3_146_752),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                    "b7d76de672f04327ab5d81353d8c274815dd1c5fb756443519ad93d0e7006def",
-                    160_879_808 + 107_364_696),
+                    "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
+                    160_787_777 + 107_364_576),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
-                   "fb00d0e49e2db62fe0a12580dae4411abeba24d79a8e5dce9e772ac9963af74e",
-                   2_148_394_965 + 786_981),
+                   "7424da827aee8e558a8042db7618711e2315ec68d139d6cdc1eacf685770711b",
+                   2_148_352_958 + 786_976),
     "qkv": (("linear.hip", "linear_launch.h", "vx_device.h"),
-            "ae016fb04b70096e287909df76377577f041d02b6a6932ec7cfbf8ecf1b0d73d",
-            21_202_517 + 3_145_728),
+            "be1c7a753b7e5fb5708a9847e001d1dada457899e51d18c1a29120462ed1f75f",
+            21_204_158 + 3_145_728),
     "oproj": (("linear.hip", "linear_launch.h", "vx_device.h"),
-              "ae016fb04b70096e287909df76377577f041d02b6a6932ec7cfbf8ecf1b0d73d",
-              13_718_698 + 655_360),
+              "be1c7a753b7e5fb5708a9847e001d1dada457899e51d18c1a29120462ed1f75f",
+              13_718_730 + 655_360),
     "gqa_prefill": (("gqa_prefill.hip", "gqa_launch.h", "vx_device.h"),
-                    "9842b7b822612279c8760871b962db02dbe480fc29226d8aa415db66670e0f96",
-                    450_901_056 + 134_630_400),
+                    "6cfc224a689b82ccabe6e94fcc52970fcac694814a3bbfb60bf2bd48d1117190",
+                    450_992_122 + 134_456_232),
+    "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
+              "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
+              116_808_304 + 24_577_928),
+    "long": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
+             "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
+             1_715_702_831 + 196_622_056),
 }
 
 
@@ -126,7 +135,7 @@ def main():
                     help="oracle repetitions of the prefill workload for the CPU baseline")
     ap.add_argument("--only", choices=["prefill", "stream", "first_chunk", "gqa_prefill",
                                        "gqa_decode", "qkv", "oproj", "enc_block", "enc_step",
-                                       "copy"],
+                                       "stack", "long", "copy"],
                     default=None,
                     help="profiling aid: launch only this kernel (or a plain device copy of "
                          "--copy-mib MiB, to calibrate HBM byte counters) and print its timing")
@@ -173,6 +182,10 @@ def main():
     def to(x, dt=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
 
+    def need(*legs):
+        # --only builds the inputs of its own leg only
+        return args.only is None or args.only in legs
+
     # ---- prefill workload: one encoder layer, T=1500
     pc = synth.CONFIGS["layer"]
     x = synth.make_config("layer")
@@ -184,7 +197,7 @@ def main():
     # ---- streaming workload
     sc = synth.CONFIGS["stream"]
     rings = []
-    for r in range(2):
+    for r in range(2 if need("stream") else 0):
         st = synth.make_stream_state(sc.S, sc.H, sc.W, seed=[sc.seed, r], pos_lo=sc.pos_lo,
                                      pos_hi=sc.pos_hi)
         p0 = torch.from_numpy(st["pos"].copy()).to(dev)
@@ -192,16 +205,17 @@ def main():
         rings.append({"k": to(st["ring_k"]), "v": to(st["ring_v"]), "pos": [p0, p0.clone()],
                       "c": 0})
     frames = []
-    for i in range(8):
+    for i in range(8 if need("stream") else 0):
         fr = synth.make_stream_frames(sc.S, sc.n, sc.H, seed=sc.seed, step=i)
         frames.append((to(fr["q"]), to(fr["k"]), to(fr["v"])))
-    so = torch.empty_like(frames[0][0])
+    so = torch.empty_like(frames[0][0]) if frames else None
     sbytes = stream_bytes(sc.S, sc.n, sc.H, sc.W)
 
     # ---- batched first chunks (varlen prefill seeding the rings)
     fc = synth.FIRST_CHUNK
     fc_len = synth.first_chunk_lengths(fc["S"], fc["t_lo"], fc["t_hi"], seed=fc["seed"])
     xf = synth.make_first_chunks(fc["S"], fc["H"], fc_len, seed=fc["seed"], scale=fc["scale"])
+    # (small: drawn for every leg)
     fq, fk, fv = to(xf["q"]), to(xf["k"]), to(xf["v"])
     fcu = torch.from_numpy(xf["cu"]).to(dev)
     fo = torch.empty_like(fq)
@@ -220,7 +234,7 @@ def main():
     # ---- 32-layer attention stack (B4 T1500, fresh seeded Q/K/V per layer) and long-form
     # prefill (B8 T6000, 1 % of key rows x8), both with fused RoPE
     stack_in, long_in = [], None
-    if not args.no_stack and args.only is None:
+    if not args.no_stack and args.only in (None, "stack", "long"):
         stc, lgc = synth.CONFIGS["stack"], synth.CONFIGS["long"]
         for l in range(stc.layers):
             xx = synth.make_config("stack", layer=l)
@@ -238,29 +252,42 @@ def main():
         for sq, sk, sv in stack_in:
             vx.prefill(sq, sk, sv, window=stc.W, table=table, out=stack_o)
 
+    # the same 32 layers as one call of B = 128 (an upper bound: one launch,
+    # four times the workgroups of a layer)
+    stack_all = None
+    if stack_in and args.only is None:
+        stack_all = tuple(torch.cat([l_[j] for l_ in stack_in]) for j in range(3))
+        stack_all_o = torch.empty_like(stack_all[0])
+
+    def stack_one_call(i):
+        vx.prefill(*stack_all, window=stc.W, table=table, out=stack_all_o)
+
     def long_pass(i):
         vx.prefill(*long_in, window=lgc.W, table=long_tab, out=long_o)
 
     # ---- text decoder (grouped-query attention, head_dim 128)
     dc = synth.GQA_CONFIGS["dec_decode"]
-    dst = synth.make_gqa_decode_state("dec_decode")
-    dring = {"k": to(dst["ring_k"]), "v": to(dst["ring_v"]), "c": 0,
-             "pos": [torch.from_numpy(dst["pos"].copy()).to(dev)]}
-    dring["pos"].append(dring["pos"][0].clone())
-    del dst
-    dframes = []
-    for i in range(8):
-        fr = synth.make_gqa_frames(dc.B, dc.T, dc.Hq, dc.Hkv, seed=dc.seed, step=i)
-        dframes.append((to(fr["q"]), to(fr["k"]), to(fr["v"])))
-    do = torch.empty_like(dframes[0][0])
-    dbytes = gqa_decode_bytes(dc.B, dc.T, dc.Hq, dc.Hkv, dc.W)
     gc = synth.GQA_CONFIGS["dec_prefill"]
-    xg = synth.make_gqa_config("dec_prefill")
-    gq, gk, gv = to(xg["q"]), to(xg["k"]), to(xg["v"])
-    go = torch.empty_like(gq)
-    gkr = torch.empty_like(gk)  # rotated keys, written once per call
-    gtab = vx.rope_table(0, gc.T, head_dim=vx.DEC_HEAD_DIM)
+    dbytes = gqa_decode_bytes(dc.B, dc.T, dc.Hq, dc.Hkv, dc.W)
     g_flops = band_flops(gc.B, gc.T, gc.Hq, gc.W, D=gc.D)
+    dring, dframes, do = {}, [], None
+    if need("gqa_decode"):
+        dst = synth.make_gqa_decode_state("dec_decode")
+        dring = {"k": to(dst["ring_k"]), "v": to(dst["ring_v"]), "c": 0,
+                 "pos": [torch.from_numpy(dst["pos"].copy()).to(dev)]}
+        dring["pos"].append(dring["pos"][0].clone())
+        del dst
+        for i in range(8):
+            fr = synth.make_gqa_frames(dc.B, dc.T, dc.Hq, dc.Hkv, seed=dc.seed, step=i)
+            dframes.append((to(fr["q"]), to(fr["k"]), to(fr["v"])))
+        do = torch.empty_like(dframes[0][0])
+    if need("gqa_prefill"):
+        xg = synth.make_gqa_config("dec_prefill")
+        gq, gk, gv = to(xg["q"]), to(xg["k"]), to(xg["v"])
+        del xg
+        go = torch.empty_like(gq)
+        gkr = torch.empty_like(gk)  # rotated keys, written once per call
+        gtab = vx.rope_table(0, gc.T, head_dim=vx.DEC_HEAD_DIM)
 
     def gqa_decode(i):
         qn, kn, vn = dframes[i % 8]
@@ -277,18 +304,20 @@ def main():
 
     # ---- encoder attention block: q/k/v projection + RoPE, attention step, output projection
     ec = synth.ENC_BLOCK
-    ew = {k_: to(v_) for k_, v_ in synth.make_enc_block_weights(ec["d_model"], ec["H"],
-                                                                 seed=ec["seed"]).items()}
-    est = synth.make_stream_state(ec["S"], ec["H"], ec["W"], seed=[ec["seed"], 1],
-                                  pos_lo=ec["pos_lo"], pos_hi=ec["pos_hi"])
-    ering = {"k": to(est["ring_k"]), "v": to(est["ring_v"]), "c": 0,
-             "pos": [torch.from_numpy(est["pos"].copy()).to(dev)]}
-    ering["pos"].append(ering["pos"][0].clone())
-    ex = [to(synth.make_enc_block_input(ec["S"], ec["n"], ec["d_model"], seed=ec["seed"], step=i))
-          for i in range(8)]
-    eshape = (ec["S"], ec["n"], ec["H"], 64)
-    ework = {k_: torch.empty(eshape, dtype=torch.bfloat16, device=dev) for k_ in "qkvo"}
-    ey = torch.empty_like(ex[0])
+    if need("enc_block", "qkv", "oproj", "enc_step"):
+        ew = {k_: to(v_) for k_, v_ in synth.make_enc_block_weights(ec["d_model"], ec["H"],
+                                                                     seed=ec["seed"]).items()}
+        est = synth.make_stream_state(ec["S"], ec["H"], ec["W"], seed=[ec["seed"], 1],
+                                      pos_lo=ec["pos_lo"], pos_hi=ec["pos_hi"])
+        ering = {"k": to(est["ring_k"]), "v": to(est["ring_v"]), "c": 0,
+                 "pos": [torch.from_numpy(est["pos"].copy()).to(dev)]}
+        ering["pos"].append(ering["pos"][0].clone())
+        del est
+        ex = [to(synth.make_enc_block_input(ec["S"], ec["n"], ec["d_model"], seed=ec["seed"],
+                                            step=i)) for i in range(8)]
+        eshape = (ec["S"], ec["n"], ec["H"], 64)
+        ework = {k_: torch.empty(eshape, dtype=torch.bfloat16, device=dev) for k_ in "qkvo"}
+        ey = torch.empty_like(ex[0])
     eM, eHD, edm = ec["S"] * ec["n"], ec["H"] * 64, ec["d_model"]
     qkv_bytes = 3 * eHD * edm * 2 + eM * edm * 2 + 3 * eM * eHD * 2 + 2 * eHD * 2 + ec["S"] * 8
     oproj_bytes = edm * eHD * 2 + eM * eHD * 2 + eM * edm * 2 + edm * 2
@@ -313,19 +342,20 @@ def main():
     cs = synth.ENC_STEP
     sL = args.enc_layers or cs["L"]
     sS, sn, sH, sdm, sffn, snm = cs["S"], cs["n"], cs["H"], cs["d_model"], cs["ffn"], cs["n_mels"]
-    s_stem = {k_: to(v_) for k_, v_ in synth.make_enc_stem_weights(sdm, snm,
-                                                                    seed=cs["seed"]).items()}
-    s_layers = [{k_: to(v_) for k_, v_ in synth.make_enc_layer_weights(
-        sdm, sH, sffn, seed=cs["seed"], layer=l).items()} for l in range(sL)]
-    s_rk = ering["k"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
-    s_rv = ering["v"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
-    s_pos = [ering["pos"][0].clone(), ering["pos"][0].clone()]
-    s_mel = [to(synth.make_mel(sS, 2 * sn, snm, seed=cs["seed"], step=i)) for i in range(8)]
-    s_melbuf = torch.zeros((sS, 2 * sn + 2, snm), dtype=torch.bfloat16, device=dev)
-    s_c1buf = torch.zeros((sS, 2 * sn + 2, sdm), dtype=torch.bfloat16, device=dev)
-    s_x = torch.empty((sS, sn, sdm), dtype=torch.float32, device=dev)
-    s_work = vx.enc_work(sS, sn, sH, sdm, sffn, device=dev)
     s_state = {"c": 0}
+    if need("enc_step"):
+        s_stem = {k_: to(v_) for k_, v_ in synth.make_enc_stem_weights(sdm, snm,
+                                                                        seed=cs["seed"]).items()}
+        s_layers = [{k_: to(v_) for k_, v_ in synth.make_enc_layer_weights(
+            sdm, sH, sffn, seed=cs["seed"], layer=l).items()} for l in range(sL)]
+        s_rk = ering["k"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
+        s_rv = ering["v"].unsqueeze(0).repeat(sL, 1, 1, 1, 1)
+        s_pos = [ering["pos"][0].clone(), ering["pos"][0].clone()]
+        s_mel = [to(synth.make_mel(sS, 2 * sn, snm, seed=cs["seed"], step=i)) for i in range(8)]
+        s_melbuf = torch.zeros((sS, 2 * sn + 2, snm), dtype=torch.bfloat16, device=dev)
+        s_c1buf = torch.zeros((sS, 2 * sn + 2, sdm), dtype=torch.bfloat16, device=dev)
+        s_x = torch.empty((sS, sn, sdm), dtype=torch.float32, device=dev)
+        s_work = vx.enc_work(sS, sn, sH, sdm, sffn, device=dev)
     sM, sHD, sF = sS * sn, sH * 64, 2 * sn + 2
     s_stem_bytes = (sdm * 3 * snm * 2 + sS * sF * snm * 2 + sS * 2 * sn * sdm * 2  # conv1
                     + sdm * 3 * sdm * 2 + sS * sF * sdm * 2 + sM * sdm * 4          # conv2
@@ -379,7 +409,10 @@ def main():
                                                          window=fc["W"], table=ftab, ring_k=frk,
                                                          ring_v=frv, pos=fpos, out=fo),
               "gqa_prefill": gqa_prefill, "gqa_decode": gqa_decode, "qkv": qkv, "oproj": oproj,
-              "enc_block": enc_block, "enc_step": enc_step}[args.only]
+              "enc_block": enc_block, "enc_step": enc_step,
+              "stack": lambda j: vx.prefill(*stack_in[j % len(stack_in)], window=stc.W,
+                                            table=table, out=stack_o),
+              "long": long_pass}[args.only]
         for j in range(args.warmup):
             fn(j)
         torch.cuda.synchronize()
@@ -415,10 +448,9 @@ def main():
     pre_in_step = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
     str_in_step = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
 
-    # ---- per-kernel average launch duration: back-to-back launches between two events
-    def per_launch_us(fn, reps):
-        fn(-1)  # one untimed call: first-launch and first-touch costs stay out
-        torch.cuda.synchronize()
+    # ---- per-call durations: back-to-back launches between two events on the
+    # launch stream, 5 passes interleaved over the legs, median per leg
+    def time_launches(fn, reps):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for j in range(reps):
@@ -431,83 +463,90 @@ def main():
 
     # the layer prefill as one HIP graph of 100 launches (no host launch cost
     # between kernels); the library's calls allocate nothing, so they capture
-    def prefill_graph_us():
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prefill()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    pre_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(pre_graph):
+        for _ in range(100):
             prefill()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(100):
-                prefill()
-        graph.replay()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(3):
-            graph.replay()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) * 1e3 / 300
+    pre_graph.replay()
+    torch.cuda.synchronize()
 
-    pre_graph_us = prefill_graph_us()
-    fc_us = per_launch_us(lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"], window=fc["W"],
-                                                      table=ftab, ring_k=frk, ring_v=frv,
-                                                      pos=fpos, out=fo), reps)
+    # the whole encoder step captured as a HIP graph: two steps (the position
+    # arrays ping-pong), so every replay advances the streams like the eager loop
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        enc_step(0)
+        enc_step(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    encs_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(encs_graph):
+        s_state["c"] = 0
+        enc_step(0)
+        enc_step(1)
+    encs_graph.replay()
+    torch.cuda.synchronize()
 
     def serial_first_chunks(j):
         for a_, b_ in fc_slices:
             vx.prefill(fq[a_:b_][None], fk[a_:b_][None], fv[a_:b_][None], window=fc["W"],
                        table=ftab, out=fo[a_:b_][None])
-    fc_serial_us = per_launch_us(serial_first_chunks, max(K // 4, 5))
-    pre_us = per_launch_us(lambda j: prefill(), reps)
-    # the same attention with q and k rotated upstream, as when the q/k/v
-    # projection's epilogue applies RoPE (reported beside the fused figure)
-    pre_rot_us = per_launch_us(
-        lambda j: vx.prefill(q, k, v, window=pc.W, rope_applied=True, out=o), reps)
-    step_us = per_launch_us(stream_fused, reps)
-    attend_us = per_launch_us(lambda j: stream(j), reps)
-    two_call_us = per_launch_us(lambda j: append(stream(j)), reps)
 
-    blk_us = per_launch_us(enc_block, reps)
-    qkv_us = per_launch_us(qkv, reps)
-    oproj_us = per_launch_us(oproj, reps)
-    encs_us = per_launch_us(enc_step, max(K // 5, 5))
-
-    # the same step captured as a HIP graph: two steps (the position arrays
-    # ping-pong), so every replay advances the streams like the eager loop
-    def enc_step_graph_us(replays):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            enc_step(0)
-            enc_step(1)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            s_state["c"] = 0
-            enc_step(0)
-            enc_step(1)
-        graph.replay()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(replays):
-            graph.replay()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) * 1e3 / (2 * replays)
-
-    encs_graph_us = enc_step_graph_us(max(K // 10, 3))
+    # name -> (function of the call index, calls per pass, calls counted per pass)
+    legs = {
+        "prefill": (lambda j: prefill(), reps, reps),
+        "prefill_graph": (lambda j: pre_graph.replay(), 1, 100),
+        # the same attention with q and k rotated upstream, as when the q/k/v
+        # projection's epilogue applies RoPE (reported beside the fused figure)
+        "prefill_rope_upstream": (lambda j: vx.prefill(q, k, v, window=pc.W, rope_applied=True,
+                                                       out=o), reps, reps),
+        # the cos/sin rows of the layer's 1500 positions (a cache built once per
+        # position range, outside the headline)
+        "rope_table": (lambda j: vx.rope_table(0, pc.T, out=table), reps, reps),
+        # 200 consecutive steps with positions advancing, per pass
+        "stream_step": (stream_fused, 200, 200),
+        "stream_attend": (lambda j: stream(j), reps, reps),
+        "stream_two_calls": (lambda j: append(stream(j)), reps, reps),
+        "first_chunk": (lambda j: vx.prefill_varlen(fq, fk, fv, fcu, fc["t_hi"], window=fc["W"],
+                                                    table=ftab, ring_k=frk, ring_v=frv, pos=fpos,
+                                                    out=fo), reps, reps),
+        "first_chunk_serial": (serial_first_chunks, max(K // 4, 5), max(K // 4, 5)),
+        "enc_block": (enc_block, reps, reps),
+        "qkv": (qkv, reps, reps),
+        "oproj": (oproj, reps, reps),
+        "enc_step": (enc_step, max(K // 5, 4), max(K // 5, 4)),
+        "enc_step_graph": (lambda j: encs_graph.replay(), max(K // 10, 2), 2 * max(K // 10, 2)),
+        "gqa_decode": (gqa_decode, reps, reps),
+        "gqa_prefill": (gqa_prefill, max(K // 5, 4), max(K // 5, 4)),
+        "gqa_prefill_fused": (gqa_prefill_fused, max(K // 5, 4), max(K // 5, 4)),
+    }
     if stack_in:
-        stack_us = per_launch_us(stack_pass, max(K // 10, 3))
-        long_us = per_launch_us(long_pass, max(K // 5, 5))
-    dec_us = per_launch_us(gqa_decode, reps)
-    gpre_us = per_launch_us(gqa_prefill, max(K // 5, 5))
-    gpre_fused_us = per_launch_us(gqa_prefill_fused, max(K // 5, 5))
+        legs["stack"] = (stack_pass, 1, 1)
+        legs["stack_one_call"] = (stack_one_call, 1, 1)
+        legs["long"] = (long_pass, max(K // 5, 4), max(K // 5, 4))
+    for name, (fn, n_, _) in legs.items():
+        fn(-1)  # first-launch and first-touch costs stay out of the passes
+    torch.cuda.synchronize()
+    PASSES = 5
+    samples = {name: [] for name in legs}
+    for _ in range(PASSES):
+        for name, (fn, n_, per) in legs.items():
+            samples[name].append(time_launches(fn, n_) * n_ / per)
+    med = {name: float(np.median(v_)) for name, v_ in samples.items()}
+    pre_us, pre_graph_us, pre_rot_us = med["prefill"], med["prefill_graph"], med["prefill_rope_upstream"]
+    step_us, attend_us, two_call_us = med["stream_step"], med["stream_attend"], med["stream_two_calls"]
+    fc_us, fc_serial_us = med["first_chunk"], med["first_chunk_serial"]
+    blk_us, qkv_us, oproj_us = med["enc_block"], med["qkv"], med["oproj"]
+    encs_us, encs_graph_us = med["enc_step"], med["enc_step_graph"]
+    dec_us, gpre_us, gpre_fused_us = med["gqa_decode"], med["gqa_prefill"], med["gqa_prefill_fused"]
+    if stack_in:
+        stack_us, stack_one_us, long_us = med["stack"], med["stack_one_call"], med["long"]
 
     tflops = flops / (pre_us * 1e-6) / 1e12
     stream_gbs = sbytes / (step_us * 1e-6) / 1e9
@@ -532,9 +571,13 @@ def main():
             "seq_len": pc.T,
             "parallelism": "none (one GPU)",
         },
+        "timing": "per-call median of 5 passes interleaved over the legs (HIP events around "
+                  "back-to-back launches); the streaming step over 200 consecutive steps per pass",
         "prefill_us": round(pre_us, 3),
+        "prefill_us_passes": [round(x_, 3) for x_ in samples["prefill"]],
         "prefill_us_graph": round(pre_graph_us, 3),
         "prefill_us_rope_upstream": round(pre_rot_us, 3),
+        "rope_table_us": round(med["rope_table"], 3),
         "stream_step_us": round(step_us, 3),
         "stream_step_two_calls_us": round(two_call_us, 3),
         "stream_attend_only_us": round(attend_us, 3),
@@ -628,10 +671,12 @@ def main():
                         "fresh Q/K/V per layer, RoPE fused, one call per layer",
             "us_per_stack": round(stack_us, 3),
             "us_per_layer": round(stack_us / stc.layers, 3),
+            "us_one_call_B128": round(stack_one_us, 3),
+            "tflops_one_call_B128": round(stack_flops / (stack_one_us * 1e-6) / 1e12, 2),
             "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
                          "achieved": round(stack_tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(stack_tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic("stack")},
         }
         out["long"] = {
             "workload": f"prefill B{lgc.B} T{lgc.T} H{lgc.H} D64 W{lgc.W} bf16, 1 % of key rows x8, "
@@ -640,7 +685,7 @@ def main():
             "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
                          "achieved": round(long_tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(long_tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic("long")},
         }
 
     encs_gbs = s_bytes / (encs_us * 1e-6) / 1e9
@@ -666,13 +711,31 @@ def main():
         for _ in range(args.cpu_reps):
             oracle.prefill(x["q"], x["k"], x["v"], pc.W, bf16=True, nthreads=nt)
         cpu_s = time.perf_counter() - t0
+        # one thread on 4 of the 32 heads (the oracle's work is per (batch, head))
+        hs = slice(0, 4)
+        t1 = time.perf_counter()
+        oracle.prefill(x["q"][:, :, hs], x["k"][:, :, hs], x["v"][:, :, hs], pc.W, bf16=True,
+                       nthreads=1)
+        one_s = time.perf_counter() - t1
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for line in fh:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         out["cpu_baseline"] = {
             "value": round(flops * args.cpu_reps / cpu_s / 1e12, 6),
             "unit": "TFLOP/s",
             "cores": nt,
             "kind": "oracle",
             "sample": f"float64 oracle (bf16 contract), the full prefill workload B1 T1500 H32 "
-                      f"W750 x {args.cpu_reps} repetitions, {cpu_s:.1f} s on {nt} threads",
+                      f"W750 x {args.cpu_reps} repetitions, {cpu_s:.1f} s on {nt} threads; one "
+                      f"thread: 4 of the 32 heads once, {one_s:.2f} s",
+            "value_1thread": round(flops / 8 / one_s / 1e12, 6),
+            "cpu_model": cpu_model,
         }
     print(json.dumps(out))
 

@@ -201,34 +201,59 @@ def test_prefill_position_offset_and_table_window():
     assert np.all(np.isnan(run_prefill(x, 750, "bf16", pos0=13700, table=table, table_p0=12000)))
 
 
-def test_stack_layer_sampled():
+def _check_picks(x, got, picks, W, what):
+    """The oracle on the chosen (b, h) pairs at once: each pair's head slice
+    becomes one batch entry of a single oracle call (threads over entries)."""
+    sel = lambda a: np.stack([a[b, :, h] for b, h in picks])[:, :, None]  # noqa: E731
+    want = oracle.prefill(sel(x["q"]), sel(x["k"]), sel(x["v"]), W, bf16=True)
+    for i, (b, h) in enumerate(picks):
+        check_bf16(got[b, :, h], want[i, :, 0], f"{what} b{b} h{h}")
+
+
+def test_stack_layers_sampled():
+    """Stack workload (B4 T1500 H32 per layer): 16 (b, h) pairs of layer 0 and
+    8 of layer 31 against the oracle, corners included."""
     c = synth.CONFIGS["stack"]
-    say("stack layer 0: B4 T1500 H32, oracle on sampled (b,h)")
-    x = synth.make_config("stack", layer=0)
-    got = run_prefill(x, c.W, "bf16")
     rng = np.random.default_rng(3)
-    for b, h in [(0, 0), (3, 31)] + [tuple(rng.integers([0, 0], [4, 32])) for _ in range(2)]:
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        want = oracle.prefill(x["q"][sl], x["k"][sl], x["v"][sl], c.W, bf16=True)
-        check_bf16(got[sl], want, f"stack b{b} h{h}")
+    for layer, n in ((0, 16), (c.layers - 1, 8)):
+        say(f"stack layer {layer}: B4 T1500 H32, oracle on {n} sampled (b,h)")
+        x = synth.make_config("stack", layer=layer)
+        got = run_prefill(x, c.W, "bf16")
+        picks = [(0, 0), (c.B - 1, c.H - 1)]
+        while len(picks) < n:
+            p_ = tuple(int(v) for v in rng.integers([0, 0], [c.B, c.H]))
+            if p_ not in picks:
+                picks.append(p_)
+        _check_picks(x, got, picks, c.W, f"stack layer {layer}")
 
 
 def test_long_sampled():
+    """Long-form workload (B8 T6000 H32, 1 % of key rows x8): every (b, h)
+    that holds one of the 16 largest stressed key rows, plus sampled pairs
+    (32 in all), against the oracle."""
     c = synth.CONFIGS["long"]
-    say("long: B8 T6000 H32 with stressed key rows, oracle on sampled (b,h)")
+    say("long: B8 T6000 H32 with stressed key rows, oracle on 32 (b,h)")
     x = synth.make_config("long")
     got = run_prefill(x, c.W, "bf16")
     assert np.all(np.isfinite(got))
-    stressed = x["stressed_rows"]
-    heads = (stressed % (c.T * c.H)) % c.H
-    bs = stressed // (c.T * c.H)
+    stressed = x["stressed_rows"]  # flat indices of (b, t, h) rows
+    k_rows = x["k"].reshape(-1, x["k"].shape[-1])
+    norms = np.linalg.norm(k_rows[stressed].astype(np.float64), axis=1)
+    top = stressed[np.argsort(-norms)[:16]]
+    picks = []
+    for r in top:
+        p_ = (int(r // (c.T * c.H)), int(r % c.H))
+        if p_ not in picks:
+            picks.append(p_)
     rng = np.random.default_rng(5)
-    picks = [(int(bs[0]), int(heads[0])), (7, 31)] + \
-        [tuple(int(v) for v in rng.integers([0, 0], [8, 32])) for _ in range(2)]
-    for b, h in picks:
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        want = oracle.prefill(x["q"][sl], x["k"][sl], x["v"][sl], c.W, bf16=True)
-        check_bf16(got[sl], want, f"long b{b} h{h}")
+    for p_ in [(0, 0), (c.B - 1, c.H - 1)]:
+        if p_ not in picks:
+            picks.append(p_)
+    while len(picks) < 32:
+        p_ = tuple(int(v) for v in rng.integers([0, 0], [c.B, c.H]))
+        if p_ not in picks:
+            picks.append(p_)
+    _check_picks(x, got, picks, c.W, "long")
 
 
 def test_prefill_deterministic():
