@@ -51,14 +51,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
-                21_656_530 + 6_144_000),
+                "14f1a2802f31a7782cae2bf1227f48cfee5bbb21a71348bb195377f5c5124fa5",
+                21_721_701 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
                "4b94d8f36c1768bf9e97a79237f965a66a9f69d1e23f335562ccf9299dd6d169",
                396_092_019 + 3_146_752),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                    "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
-                    160_787_777 + 107_364_576),
+                    "14f1a2802f31a7782cae2bf1227f48cfee5bbb21a71348bb195377f5c5124fa5",
+                    155_732_634 + 107_363_872),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "7424da827aee8e558a8042db7618711e2315ec68d139d6cdc1eacf685770711b",
                    2_148_352_958 + 786_976),
@@ -72,11 +72,11 @@ MEASURED_TRAFFIC = {
                     "6cfc224a689b82ccabe6e94fcc52970fcac694814a3bbfb60bf2bd48d1117190",
                     450_992_122 + 134_456_232),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-              "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
-              116_808_304 + 24_577_928),
+              "14f1a2802f31a7782cae2bf1227f48cfee5bbb21a71348bb195377f5c5124fa5",
+              103_775_966 + 24_576_000),
     "long": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "9885fc822b16466949c2d918e72fccba22ea23309f2bcfbd2d65d1562a04128b",
-             1_715_702_831 + 196_622_056),
+             "14f1a2802f31a7782cae2bf1227f48cfee5bbb21a71348bb195377f5c5124fa5",
+             865_333_693 + 196_611_128),
 }
 
 

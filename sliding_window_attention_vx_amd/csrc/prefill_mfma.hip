@@ -382,6 +382,24 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   const int kbeg = max(0, q0 - W + 1);
   const int klast = min(T, q0 + BM) - 1;
   const int it0 = kbeg / kBN, it1 = klast / kBN;
+  // Visiting order of the key tiles it0 .. it1.  P is the number of tiles in
+  // the band of a 128-query tile (at least that of any workgroup's band), and
+  // the walk starts at the band's tile whose index is a multiple of P,
+  // wrapping around to it0: every query tile whose band holds key tile j then
+  // visits it at about step j mod P, so workgroups that run side by side read
+  // the same K, V and table rows at about the same time and L2 serves all but
+  // the first.  (In ascending order a tile's neighbour, BM queries later,
+  // reaches the same keys BM/64 steps later, by which time the XCD's resident
+  // workgroups have streamed more rows than its L2 keeps on large grids.)
+  // A band holds at most one multiple of P; one that holds none (cut at key 0
+  // or at T) is walked in ascending order.  So a 32-query block sees its key
+  // tiles in an order set by the tile indices alone, the same with two- or
+  // four-wave workgroups, and both give the same bits.
+  const int P = 2 + (W - 1 + kBN - 1) / kBN;
+  int it_start = it0 + (P - it0 % P) % P;
+  if (it_start > it1) it_start = it0;
+  // (the same in every lane; the division above is expanded on the vector ALU)
+  it_start = __builtin_amdgcn_readfirstlane(it_start);
 
   // ---- Q' fragments (B operand of S^T = K' Q'^T) -------------------------
   // MFMA step m covers dims 16m .. 16m+15; lane half hh holds dims 16m+8hh+(0..7),
@@ -419,7 +437,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
   Stage<NW> st;
   const StageOffs<NW> so = stage_offsets<NW>(tid, rs);
-  stage_load<NW, OTF>(st, k, v, rs, T, it0 * kBN, rope, a, trow0, p0, so);
+  stage_load<NW, OTF>(st, k, v, rs, T, it_start * kBN, rope, a, trow0, p0, so);
   if (rope && !OTF) {
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
@@ -494,13 +512,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     sd.kt0 = kt0;
     return sd;
   };
-  stage_commit<NW, SEED>(st, lds, lds + kTileK, rope, tid, seed_for(it0 * kBN));
+  stage_commit<NW, SEED>(st, lds, lds + kTileK, rope, tid, seed_for(it_start * kBN));
   __syncthreads();
 
-  for (int it = it0; it <= it1; ++it) {
-    const int buf = (it - it0) & 1;
-    // the next tile's loads (past the last tile: an empty descriptor)
-    stage_load<NW, OTF>(st, k, v, rs, T, (it + 1) * kBN, rope, a, trow0, p0, so);
+  // One step per key tile: the next tile's loads go out first (after the
+  // last tile: rows from T on, an empty descriptor), then this tile's scores,
+  // softmax and P·V, then the next tile's commit to the other LDS buffer.
+  // The walk is two loops with an affine tile index each (it_start .. it1,
+  // then it0 .. it_start-1): a wrapped index in one loop makes the compiler
+  // keep a staged tile live across the whole step (32 more VGPRs).
+  int j = 0;
+  auto tile_step = [&](const int it, const int kt_next) {
+    const int buf = j & 1;
+    stage_load<NW, OTF>(st, k, v, rs, T, kt_next, rope, a, trow0, p0, so);
 
     const char* Kb = lds + buf * kStageBytes;
     const char* Vb = Kb + kTileK;
@@ -594,12 +618,16 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       }
     }
 
-    if (it < it1)
+    if (kt_next < T)
       stage_commit<NW, SEED>(st, lds + (buf ^ 1) * kStageBytes,
                              lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid,
-                             seed_for((it + 1) * kBN));
+                             seed_for(kt_next));
     __syncthreads();
-  }
+    ++j;
+  };
+  const int kt_wrap = it_start > it0 ? it0 * kBN : T;
+  for (int it = it_start; it <= it1; ++it) tile_step(it, it < it1 ? (it + 1) * kBN : kt_wrap);
+  for (int it = it0; it < it_start; ++it) tile_step(it, it + 1 < it_start ? (it + 1) * kBN : T);
 
   // ---- epilogue: O = O^T / l, lane holds query tq, dims 32db + 8g + 4hh + (0..3)
   const float l_tot = partner_sum(l_run);
