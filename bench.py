@@ -19,7 +19,11 @@ other legs, and the per-call median is reported.  The
 streaming step runs 200 consecutive steps per pass with positions advancing
 and is reported in microseconds and GB/s of algorithmic HBM bytes.  The CPU
 baseline is the float64 oracle timed on the host on the same prefill
-workload (all host threads, and one thread on a slice of it).
+workload (all host threads, and one thread on a slice of it); the other
+workloads' oracle times ride along, measured on a share and scaled where the
+whole would take minutes.  `attainable` gives this GPU's measured bf16 GEMM
+rate (hipBLASLt through torch) and device-copy bandwidth, for scale beside the
+published peaks the rooflines use.
 
 Beside the step, the same line reports the 32-layer attention stack (B4
 T1500 per layer) and the long-form prefill (B8 T6000), the batched first-chunk
@@ -708,6 +712,29 @@ def main():
                      "frac": round(encs_gbs / PEAK_HBM_GBS, 4), "traffic": None},
     }
 
+    # attainable peaks on this GPU, for scale beside the published ones: a large
+    # bf16 GEMM through torch (hipBLASLt) and a 1 GiB device-to-device copy
+    ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    gc_ = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    cp_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_src.fill_(1)
+    torch.matmul(ga, gb, out=gc_)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    gemm_us = float(np.median([time_launches(lambda j: torch.matmul(ga, gb, out=gc_), 5)
+                               for _ in range(5)]))
+    copy_us = float(np.median([time_launches(lambda j: cp_dst.copy_(cp_src), 5)
+                               for _ in range(5)]))
+    out["attainable"] = {
+        "bf16_gemm_tflops": round(2 * 8192 ** 3 / gemm_us / 1e6, 1),
+        "hbm_copy_gbs": round(2 * (1 << 30) / copy_us / 1e3, 1),
+        "how": "torch.matmul of two 8192x8192 bf16 matrices (hipBLASLt) and a 1 GiB "
+               "device-to-device copy (bytes read + written), medians of 5 passes of 5",
+    }
+    del ga, gb, gc_, cp_src, cp_dst
+
     if not args.no_cpu_baseline:
         import oracle
         nt = len(os.sched_getaffinity(0))
@@ -730,6 +757,48 @@ def main():
                         break
         except OSError:
             pass
+        # the other workloads on the oracle: the tiny fp32 case and one streaming
+        # step's worth in full or by a share scaled to the whole (labelled)
+        others = {}
+
+        def timed(fn):
+            t = time.perf_counter()
+            fn()
+            return time.perf_counter() - t
+
+        c1 = synth.CONFIGS["tiny"]
+        x1 = synth.make_prefill(c1.B, c1.T, c1.H, seed=c1.seed, dtype=c1.dtype, scale=c1.scale)
+        t_c1 = timed(lambda: oracle.prefill(x1["q"], x1["k"], x1["v"], c1.W, nthreads=nt))
+        others["tiny_B1_T64_H4_W16_f32"] = {"seconds": round(t_c1, 6), "extrapolated": False}
+        # one streaming step of 8 of the 64 streams (per-stream work is the same), x8
+        sc_ = synth.CONFIGS["stream"]
+        st8 = synth.make_stream_state(8, sc_.H, sc_.W, seed=[sc_.seed, 99], pos_lo=sc_.pos_lo,
+                                      pos_hi=sc_.pos_hi)
+        fr8 = synth.make_stream_frames(8, sc_.n, sc_.H, seed=[sc_.seed, 99], step=0)
+        t_c4 = timed(lambda: oracle.stream_step(fr8["q"], fr8["k"], fr8["v"], st8["ring_k"],
+                                                st8["ring_v"], st8["pos"], sc_.W, bf16=True,
+                                                nthreads=nt)) * (sc_.S / 8)
+        others["stream_step_S64_n4"] = {"seconds": round(t_c4, 4),
+                                        "GBps": round(sbytes / t_c4 / 1e9, 3),
+                                        "extrapolated": True,
+                                        "sample": "8 of the 64 streams, one step, x8"}
+        del st8, fr8
+        # the stack: one batch entry of layer 0 (1/128 of the 32 layers x B4), x128
+        x3 = synth.make_prefill(1, pc.T, pc.H, seed=[3, 0], dtype="bf16", scale=0.5)
+        t_c3 = timed(lambda: oracle.prefill(x3["q"], x3["k"], x3["v"], pc.W, bf16=True,
+                                            nthreads=nt)) * 128
+        others["stack_32x_B4_T1500"] = {"seconds": round(t_c3, 2),
+                                        "tflops": round(128 * flops / t_c3 / 1e12, 6),
+                                        "extrapolated": True,
+                                        "sample": "layer 0, batch entry 0, x128"}
+        # the long form: batch entry 0 (1/8), x8
+        x5 = synth.make_prefill(1, 6000, pc.H, seed=[5, 0], dtype="bf16", scale=1.0)
+        f5 = band_flops(1, 6000, pc.H, pc.W)
+        t_c5 = timed(lambda: oracle.prefill(x5["q"], x5["k"], x5["v"], pc.W, bf16=True,
+                                            nthreads=nt)) * 8
+        others["long_B8_T6000"] = {"seconds": round(t_c5, 2),
+                                   "tflops": round(8 * f5 / t_c5 / 1e12, 6),
+                                   "extrapolated": True, "sample": "batch entry 0, x8"}
         out["cpu_baseline"] = {
             "value": round(flops * args.cpu_reps / cpu_s / 1e12, 6),
             "unit": "TFLOP/s",
@@ -740,6 +809,7 @@ def main():
                       f"thread: 4 of the 32 heads once, {one_s:.2f} s",
             "value_1thread": round(flops / 8 / one_s / 1e12, 6),
             "cpu_model": cpu_model,
+            "other_workloads": others,
         }
     print(json.dumps(out))
 
