@@ -76,6 +76,24 @@ def test_rope_table_values():
     assert torch.cuda.is_available()
 
 
+@pytest.mark.parametrize("p0", [2_147_000_000, (1 << 52) - 4096])
+def test_rope_table_values_large_positions(p0):
+    """Large angles (positions near 2^31 and near the 2^52 the ABI allows): the
+    float64 reduction by pi/2 must still give each cos/sin of the float64 angle
+    within half a float32 ulp of its exact value.  At such positions the angle
+    p*f moves by about f for one ulp of f, so the frequencies here are the
+    correctly rounded ones (libm pow, as the library and the C oracle use;
+    numpy's vectorised power is one ulp low for i = 11 and 25)."""
+    import math
+    say(f"rope_table p {p0} .. {p0 + 4095}")
+    t = host(vx.rope_table(p0, 4096))
+    p = (p0 + np.arange(4096, dtype=np.int64)).astype(np.float64)[:, None]
+    f = np.array([math.pow(1e6, -2.0 * i / 64.0) for i in range(32)])
+    want_c, want_s = np.cos(p * f), np.sin(p * f)
+    assert np.max(np.abs(t[:, 0] - want_c)) <= 6.0e-8
+    assert np.max(np.abs(t[:, 1] - want_s)) <= 6.0e-8
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rope_qk_matches_oracle(dtype):
     say(f"rope_qk {dtype}")
