@@ -198,6 +198,14 @@ def main():
     o = torch.empty_like(q)
     table = vx.rope_table(0, pc.T)
     flops = band_flops(pc.B, pc.T, pc.H, pc.W)
+    # a 500-frame chunk of the same layer: 128 query tiles, half a query tile
+    # per CU, which takes the split walk given a workspace (two workgroups per
+    # query tile, one per half of its key band)
+    spT = 500
+    spq, spk, spv = q[:, :spT].contiguous(), k[:, :spT].contiguous(), v[:, :spT].contiguous()
+    spo = torch.empty_like(spq)
+    sws = vx.prefill_workspace(1, spT, pc.H, pc.W)
+    sp_flops = band_flops(1, spT, pc.H, pc.W)
 
     # ---- streaming workload
     sc = synth.CONFIGS["stream"]
@@ -513,6 +521,11 @@ def main():
         # projection's epilogue applies RoPE (reported beside the fused figure)
         "prefill_rope_upstream": (lambda j: vx.prefill(q, k, v, window=pc.W, rope_applied=True,
                                                        out=o), reps, reps),
+        # the 500-frame chunk with the split walk, and without a workspace
+        "split_walk": (lambda j: vx.prefill(spq, spk, spv, window=pc.W, table=table, out=spo,
+                                            workspace=sws), reps, reps),
+        "split_walk_off": (lambda j: vx.prefill(spq, spk, spv, window=pc.W, table=table, out=spo),
+                           reps, reps),
         # the cos/sin rows of the layer's 1500 positions (a cache built once per
         # position range, outside the headline)
         "rope_table": (lambda j: vx.rope_table(0, pc.T, out=table), reps, reps),
@@ -586,6 +599,13 @@ def main():
         "prefill_us_graph": round(pre_graph_us, 3),
         "prefill_us_rope_upstream": round(pre_rot_us, 3),
         "rope_table_us": round(med["rope_table"], 3),
+        "split_walk": {
+            "workload": f"prefill B1 T{spT} H{pc.H} D64 W{pc.W} bf16 (RoPE fused): 128 query "
+                        "tiles, each key band walked by two workgroups",
+            "us": round(med["split_walk"], 3),
+            "tflops": round(sp_flops / (med["split_walk"] * 1e-6) / 1e12, 2),
+            "us_unsplit": round(med["split_walk_off"], 3),
+        },
         "stream_step_us": round(step_us, 3),
         "stream_step_two_calls_us": round(two_call_us, 3),
         "stream_attend_only_us": round(attend_us, 3),

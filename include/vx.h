@@ -62,6 +62,9 @@ typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
 #define VX_FLAG_VALU_KERNEL 1u /* prefill: use the float32 vector-ALU kernel instead of the
                                   bf16 matrix-core kernel (a cross-check; bf16 inputs still
                                   get bf16-rounded rotated q and k) */
+#define VX_FLAG_SPLIT_WALK 2u  /* prefill: take the split walk (see vx_swa_attn_prefill) on
+                                  every grid of at most 1.5 query tiles per compute unit,
+                                  also where it does not pay off */
 
 typedef struct {
   int32_t head_dim;      /* must be 64                                              */
@@ -138,29 +141,47 @@ vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, const in
  * cfg->workspace (optional): with at least
  * vx_swa_attn_prefill_workspace_size() bytes, a NULL rope_table is served
  * from a table built in it (one extra launch); the results are the same bits
- * as with a caller table or cos/sin computed in the kernel. */
+ * as with a caller table or cos/sin computed in the kernel.  The same
+ * workspace also enables the split walk (bf16 matrix-core path, with a
+ * table or rope_applied) on grids of at most one 128-query tile per compute
+ * unit whose key bands span at least 8 tiles of 64 keys (with
+ * VX_FLAG_SPLIT_WALK: every grid of at most 1.5 tiles per unit): two
+ * workgroups per query tile, one per half of its key band, whose softmax
+ * partials the later of the two merges (the exact rescaling of running
+ * maxima and sums that flash attention's online softmax uses).  Its flag
+ * words and partial results follow the table in the workspace (which must
+ * then not be shared by calls that overlap in time); each call leaves the
+ * flag words zero, and any content other than the kernel's two tokens reads
+ * as zero, so the workspace needs no clearing.  Split results are
+ * deterministic but not the same bits as the unsplit walk's (another
+ * summation order; within the same tolerance of the exact result). */
 vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
                               int32_t T, int32_t H, const int64_t *pos0, int32_t rope_applied,
                               const float *rope_table, int64_t table_p0, int64_t table_len,
                               const vx_attn_cfg *cfg, void *stream);
 
 /* Workspace bytes (cfg->workspace_bytes) with which vx_swa_attn_prefill of
- * this shape, given no rope_table, keeps its cos/sin table in the workspace:
- * B*T rows of 256 bytes (row b*T + t for position pos0[b] + t).  Returns 0
- * for invalid arguments. */
+ * this shape and cfg->window, given no rope_table, keeps its cos/sin table in
+ * the workspace (B*T rows of 256 bytes, row b*T + t for position pos0[b] + t,
+ * rounded up to 256) and, where it takes the split walk on the current
+ * device (cfg->flags counts), the walk's flag word per (b, h, 128-query tile,
+ * wave of 32 queries), rounded up to 256 bytes, and two 9216-byte partial
+ * results per flag word.  Returns 0 for invalid arguments. */
 size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
                                           const vx_attn_cfg *cfg);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * call as vx_swa_attn_prefill with rope_table == NULL and a workspace, but
+ * call as vx_swa_attn_prefill with rope_table == NULL and a workspace (but
+ * never the split walk, nor VX_FLAG_SPLIT_WALK), where
  * the cos/sin rows live in a library-owned static device array of 16 MiB
  * (one per GPU, held until the process ends), so the call allocates nothing.
  * cfg->workspace is ignored.  Requires B*T <= 65536 when rope_applied == 0
  * (VX_E_SHAPE otherwise, nothing launched).  Every call on a GPU shares that
  * GPU's array: calls that overlap in time on one GPU (other streams, other
  * host threads) race and must not be made.  Same results, bit for bit, as
- * vx_swa_attn_prefill given a table of the same positions. */
+ * vx_swa_attn_prefill given a table of the same positions and no
+ * workspace. */
 vx_status vx_swa_attn_prefill_noalloc(const void *q, const void *k, const void *v, void *o,
                                       int32_t B, int32_t T, int32_t H, const int64_t *pos0,
                                       int32_t rope_applied, const vx_attn_cfg *cfg,

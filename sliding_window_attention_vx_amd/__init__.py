@@ -31,6 +31,7 @@ DEC_HEAD_DIM = 128
 
 VX_F32, VX_BF16 = 0, 1
 VX_FLAG_VALU_KERNEL = 1
+VX_FLAG_SPLIT_WALK = 2
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported dtype",
            4: "misaligned pointer", 5: "value out of range", 6: "HIP runtime error"}
 
@@ -143,7 +144,7 @@ class Config:
     """Attention parameters (mirrors vx_attn_cfg)."""
 
     def __init__(self, window=WINDOW, theta=THETA, scale=0.0, io_dtype="bf16", out_dtype=None,
-                 valu=False, head_dim=HEAD_DIM, workspace=None):
+                 valu=False, head_dim=HEAD_DIM, workspace=None, force_split=False):
         self.head_dim = int(head_dim)
         self.window = int(window)
         self.theta = float(theta)
@@ -152,12 +153,15 @@ class Config:
         self.out_dtype = out_dtype or io_dtype
         self.valu = bool(valu)
         self.workspace = workspace  # device tensor or None
+        self.force_split = bool(force_split)
 
     def c(self):
         d = {"bf16": VX_BF16, "f32": VX_F32}
         ws = self.workspace
         return _Cfg(self.head_dim, self.window, self.theta, self.scale, d[self.io_dtype],
-                    d[self.out_dtype], VX_FLAG_VALU_KERNEL if self.valu else 0,
+                    d[self.out_dtype],
+                    (VX_FLAG_VALU_KERNEL if self.valu else 0)
+                    | (VX_FLAG_SPLIT_WALK if self.force_split else 0),
                     None if ws is None else ws.data_ptr(),
                     0 if ws is None else ws.numel() * ws.element_size())
 
@@ -250,22 +254,23 @@ def rope_qk(q, k, pos0=None, theta=THETA):
            "vx_rope_qk")
 
 
-def prefill_workspace_size(B, T, H, window=WINDOW, theta=THETA):
-    """Bytes of workspace in which prefill() of this shape keeps its cos/sin table."""
-    cfg = Config(window, theta).c()
+def prefill_workspace_size(B, T, H, window=WINDOW, theta=THETA, force_split=False):
+    """Bytes of workspace with which prefill() of this shape keeps its cos/sin table
+    there and, on grids small enough for it, takes the split walk."""
+    cfg = Config(window, theta, force_split=force_split).c()
     return int(lib().vx_swa_attn_prefill_workspace_size(int(B), int(T), int(H), ctypes.byref(cfg)))
 
 
-def prefill_workspace(B, T, H, window=WINDOW, device="cuda"):
-    """A workspace of prefill_workspace_size() bytes (reusable across calls)."""
+def prefill_workspace(B, T, H, window=WINDOW, device="cuda", force_split=False):
+    """A workspace of prefill_workspace_size() bytes (reusable across calls on one stream)."""
     import torch
-    n = prefill_workspace_size(B, T, H, window)
+    n = prefill_workspace_size(B, T, H, window, force_split=force_split)
     return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
 def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_applied=False,
             table=None, table_p0=0, out=None, out_dtype=None, valu=False, workspace=None,
-            auto_table=True):
+            auto_table=True, force_split=False):
     """Causal sliding-window attention over whole chunks; q,k,v [B,T,H,64] -> o [B,T,H,64].
 
     pos0: None (positions 0..T-1), an int, or a device int64 tensor [B] (entry b
@@ -275,7 +280,10 @@ def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_appl
     the chunk's positions is made here (auto_table=True); otherwise the
     library builds one in the workspace if it has room, else computes cos/sin
     in the kernel.  workspace: a uint8 device tensor (prefill_workspace), reused
-    across calls; None runs without one.
+    across calls; None runs without one.  With a workspace, grids of at most
+    one 128-query tile per compute unit and key bands of 8 tiles or more
+    take the split walk (two workgroups per query tile); force_split takes it
+    on every grid small enough for it.
     """
     import torch
     for name, x in (("q", q), ("k", k), ("v", v)):
@@ -307,7 +315,8 @@ def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_appl
         _dev_tensor(workspace, "workspace")
         if workspace.dtype != torch.uint8:
             raise ValueError("workspace must be a uint8 tensor (see prefill_workspace)")
-    cfg = Config(window, theta, scale, io, od, valu, workspace=workspace).c()
+    cfg = Config(window, theta, scale, io, od, valu, workspace=workspace,
+                 force_split=force_split).c()
     _check(lib().vx_swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, H, _ptr(p0),
                                      int(bool(rope_applied)),
                                      _ptr(table) if not rope_applied else None, int(table_p0),

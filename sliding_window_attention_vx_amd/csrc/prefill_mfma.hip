@@ -37,6 +37,22 @@
 // 32-key halves that straddle a band edge, as one unsigned range test per
 // score.  Accumulators stay in VGPRs (the build asks for the VGPR form of
 // MFMA) so the softmax never moves them between register files.
+//
+// Split walk, for grids too small to fill the device (about 1.5 workgroups
+// per CU, e.g. one 1500-frame chunk of 32 heads): each query tile gets two
+// workgroups, the first walking the older half of its key tiles and the
+// second the newer half, so each wave's chain of dependent tile steps is
+// half as long and the device holds twice the waves.  Softmax partials
+// combine exactly: with running maxima m0, m1 and m = max(m0, m1), the
+// merged sum is l0 2^(m0-m) + l1 2^(m1-m) and likewise for O^T.  Per wave,
+// whichever half finishes second does the merge: a half that finds its
+// partner's token already in the wave's flag word merges at once; otherwise
+// it stores its partial result (device-coherent stores, waited for) and
+// swaps its own token into the flag, and merges only if the swap returns
+// the partner's token.  The merger resets the flag to zero, so every call leaves the flags
+// as it found them (also across graph replays), and computes the merge with
+// the halves in a fixed order, so the bits do not depend on which finished
+// first.  Nothing ever waits on another workgroup.
 #include "vx_launch.h"
 
 namespace vx {
@@ -53,6 +69,10 @@ constexpr int kTileV = 64 * kRowV;         // one V tile
 constexpr int kStageBytes = kTileK + kTileV;
 constexpr float kLazy = 8.0f;              // log2-domain slack of the running max
 constexpr float kNoMax = -3.0e38f;          // running max before the first score
+// split-walk flag tokens: kSplitTok + half (any other flag value counts as
+// "partner not done")
+constexpr unsigned long long kSplitTok = 0x6a09e667f3bcc908ull;
+constexpr int kCoherent = 16;  // buffer cache policy sc1: device-coherent access
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -108,8 +128,9 @@ __device__ void poison_rows(TO* o, size_t rs, int r0, int r1) {
   }
 }
 
+template <bool SPLIT>
 __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, int hx, int cpx,
-                                          int& bh, int& qt) {
+                                          int& bh, int& qt, int& half) {
   // Work order.  The dispatcher deals workgroups round-robin to the 8 XCDs
   // (workgroup id mod 8), and each XCD has its own L2.  With at least 8
   // (batch, head) pairs, XCD x owns pairs [x*hx, (x+1)*hx).  Its N = hx *
@@ -126,12 +147,26 @@ __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, i
   //    first, which arrive last and pair up with a long workgroup on a CU
   //    that still has room.
   // With fewer pairs every XCD takes query tiles of every pair, longest first.
+  // Split walk: the two halves of a query tile are consecutive in their
+  // XCD's sequence (ids 16j + x and 16j + 8 + x), and the tiles go in the
+  // larger-grid order (every workgroup of such a grid is resident at once).
+  int id = blockIdx.x;
+  half = 0;
+  if (SPLIT) {
+    if (hx > 0) {
+      half = (id >> 3) & 1;
+      id = ((id >> 4) << 3) | (id & 7);
+    } else {
+      half = id & 1;
+      id >>= 1;
+    }
+  }
   if (hx > 0) {
-    const int i = blockIdx.x >> 3;
+    const int i = id >> 3;
     const int n_long = n_qtiles - n_short;
     const int N = hx * n_qtiles;
     int bl;
-    if (N <= 2 * cpx) {
+    if (!SPLIT && N <= 2 * cpx) {
       const int R = max(N - cpx, 0);
       const int k = i < N - R ? R + i : R - 1 - (i - (N - R));
       if (k < hx * n_short) {
@@ -150,9 +185,9 @@ __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, i
       qt = n_short - 1 - j / hx;
       bl = j % hx;
     }
-    bh = (blockIdx.x & 7) * hx + bl;
+    bh = (id & 7) * hx + bl;
   } else {
-    const int i = blockIdx.x;
+    const int i = id;
     qt = n_qtiles - 1 - i / n_bh;
     bh = i % n_bh;
   }
@@ -320,14 +355,22 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
   }
 }
 
-template <int NW, typename TO, bool SEED, bool OTF>
+// Broadcast of lane 0's 64-bit value (every lane active).
+__device__ __forceinline__ unsigned long long lane0_u64(unsigned long long x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
                                                                   int n_short, int hx, int cpx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   constexpr int BM = NW * 32;
+  static_assert(!SPLIT || (!SEED && !OTF), "the split walk serves fixed-length calls with a table");
 
-  int bh, qt;
-  if (!work_item(a.B * a.H, n_qtiles, n_short, hx, cpx, bh, qt)) return;
+  int bh, qt, half;
+  if (!work_item<SPLIT>(a.B * a.H, n_qtiles, n_short, hx, cpx, bh, qt, half)) return;
   const int h = bh % a.H, b = bh / a.H;
 
   const int tid = threadIdx.x;
@@ -371,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   if (!OTF && rope && (trow0 < 0 || trow0 + T > a.table_len)) bad = true;
   if (bad) {
     // every row of this entry and head is NaN, written by query tile 0
-    if (qt == 0) poison_rows<TO>(o, rs, 0, T);
+    if (qt == 0 && half == 0) poison_rows<TO>(o, rs, 0, T);
     return;
   }
 
@@ -381,7 +424,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
 
   const int kbeg = max(0, q0 - W + 1);
   const int klast = min(T, q0 + BM) - 1;
-  const int it0 = kbeg / kBN, it1 = klast / kBN;
+  int it0 = kbeg / kBN, it1 = klast / kBN;
+  if (SPLIT) {
+    // the older half of the band (the larger, if odd) to half 0, the newer to
+    // half 1; a one-tile band leaves half 1 without tiles (it still merges)
+    const int mid = it0 + (it1 - it0 + 2) / 2;
+    if (half == 0) it1 = mid - 1;
+    else it0 = mid;
+  }
   // Visiting order of the key tiles it0 .. it1.  P is the number of tiles in
   // the band of a 128-query tile (at least that of any workgroup's band), and
   // the walk starts at the band's tile whose index is a multiple of P,
@@ -395,8 +445,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   // or at T) is walked in ascending order.  So a 32-query block sees its key
   // tiles in an order set by the tile indices alone, the same with two- or
   // four-wave workgroups, and both give the same bits.
+  // (The split walk serves grids whose K, V and table rows all stay in L2:
+  // its halves go in ascending order.)
   const int P = 2 + (W - 1 + kBN - 1) / kBN;
-  int it_start = it0 + (P - it0 % P) % P;
+  int it_start = SPLIT ? it0 : it0 + (P - it0 % P) % P;
   if (it_start > it1) it_start = it0;
   // (the same in every lane; the division above is expanded on the vector ALU)
   it_start = __builtin_amdgcn_readfirstlane(it_start);
@@ -625,9 +677,82 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     __syncthreads();
     ++j;
   };
+  // split walk: this wave's flag word, read as the last tile starts so that
+  // its memory latency hides under that tile (a partner that finishes
+  // meanwhile is found by the token swap instead)
+  unsigned long long* flag = nullptr;
+  unsigned long long seen = 0;
+  if (SPLIT) flag = a.split_flags + ((size_t)bh * n_qtiles + qt) * NW + wave;
   const int kt_wrap = it_start > it0 ? it0 * kBN : T;
-  for (int it = it_start; it <= it1; ++it) tile_step(it, it < it1 ? (it + 1) * kBN : kt_wrap);
+  for (int it = it_start; it <= it1; ++it) {
+    if (SPLIT && it == it1) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tile_step(it, it < it1 ? (it + 1) * kBN : kt_wrap);
+  }
   for (int it = it0; it < it_start; ++it) tile_step(it, it + 1 < it_start ? (it + 1) * kBN : T);
+
+  if constexpr (SPLIT) {
+    const size_t slot = ((size_t)bh * n_qtiles + qt) * NW + wave;
+    if (qw >= T) {
+      // both halves skip a wave past the end alike; its flag is left zero too
+      if (half == 0 && lane == 0)
+        __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // The partial results move with device-coherent stores and loads (cache
+    // policy sc1, the encoding of device-scope atomic stores and loads): a
+    // store is visible to every XCD once the wave's memory counter shows it
+    // done, and a load reads the device-coherent value.  So a half waits for
+    // its stores before it swaps its token in, and loads its partner's only
+    // after seeing the partner's token; no cache is written back or
+    // invalidated (device-scope fences would do both to the whole L2).
+    const auto pr = rows_rsrc(reinterpret_cast<const char*>(a.split_part) + slot * 2 * kSplitPartBytes,
+                              (uint32_t)(2 * kSplitPartBytes));
+    const uint32_t v_mine = (uint32_t)(half * kSplitPartBytes) + 16 * lane;
+    const uint32_t v_other = (uint32_t)((half ^ 1) * kSplitPartBytes) + 16 * lane;
+    const unsigned long long tok_other = kSplitTok + (half ^ 1);
+    bool merge = lane0_u64(seen) == tok_other;
+    if (!merge) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{oacc[r >> 2][4 * (r & 3)], oacc[r >> 2][4 * (r & 3) + 1],
+                                            oacc[r >> 2][4 * (r & 3) + 2],
+                                            oacc[r >> 2][4 * (r & 3) + 3]}),
+            pr, v_mine + r * 1024, 0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{m_run, l_run, 0.f, 0.f}),
+                                             pr, v_mine + 8 * 1024, 0, kCoherent);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      unsigned long long old = 0;
+      if (lane == 0)
+        old = __hip_atomic_exchange(flag, kSplitTok + half, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      merge = lane0_u64(old) == tok_other;
+      if (!merge) return;  // the partner merges
+    }
+    asm volatile("" ::: "memory");  // the loads below stay after the token test
+    f32x4 po[9];
+#pragma unroll
+    for (int r = 0; r < 9; ++r)
+      po[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, v_other + r * 1024,
+                                                                              0, kCoherent));
+    if (lane == 0) __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // merge with the halves in a fixed order (0 then 1): the same bits
+    // whichever half merges
+    const float m0 = half ? po[8][0] : m_run, m1 = half ? m_run : po[8][0];
+    const float l0 = half ? po[8][1] : l_run, l1 = half ? l_run : po[8][1];
+    const float mm = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l0 * a0 + l1 * a1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = oacc[r >> 2][4 * (r & 3) + e], y = po[r][e];
+        const float o0 = half ? y : x, o1 = half ? x : y;
+        oacc[r >> 2][4 * (r & 3) + e] = o0 * a0 + o1 * a1;
+      }
+    }
+  }
 
   // ---- epilogue: O = O^T / l, lane holds query tq, dims 32db + 8g + 4hh + (0..3)
   const float l_tot = partner_sum(l_run);
@@ -673,11 +798,11 @@ int cus_per_xcd() {
   return c;
 }
 
-template <int NW, typename TO, bool SEED, bool OTF>
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT = false>
 void launch_k(dim3 g, dim3 blk, hipStream_t st, const PrefillArgs& a, int n_qtiles, int n_short,
               int hx, int cpx) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF>), g, blk, 0, st, a, n_qtiles, n_short,
-                     hx, cpx);
+  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF, SPLIT>), g, blk, 0, st, a, n_qtiles,
+                     n_short, hx, cpx);
 }
 
 template <int NW>
@@ -689,8 +814,17 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
   const int hx = n_bh >= 8 ? (n_bh + 7) / 8 : 0;
   const int cpx = cus_per_xcd();
   const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
-  const dim3 g((unsigned)grid), blk(NW * 64);
+  const dim3 blk(NW * 64);
   const bool otf = a.rope && !a.table;  // no table: cos/sin computed in the kernel
+  if constexpr (NW == 4) {
+    if (a.split_flags && !a.cu && !a.ring_k && !otf) {
+      const dim3 g2((unsigned)(2 * grid));
+      if (out == DT::BF16) launch_k<NW, bf16, false, false, true>(g2, blk, st, a, n_qtiles, n_short, hx, cpx);
+      else launch_k<NW, float, false, false, true>(g2, blk, st, a, n_qtiles, n_short, hx, cpx);
+      return hipGetLastError();
+    }
+  }
+  const dim3 g((unsigned)grid);
   if (a.ring_k) {
     // (seeding with in-kernel cos/sin runs four-wave workgroups only: the
     // two-wave variant would need more than 256 VGPRs)
@@ -717,12 +851,32 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
 
 }  // namespace
 
+// The split walk pays off while the unsplit grid has at most one four-wave
+// workgroup per CU (its doubled grid then stays resident, at most two per
+// CU) and the key bands are long: the merge adds about three dependent
+// device-coherent memory round trips to a wave's end, which costs more than
+// halving the walk saves once the CUs hold more than one query tile each,
+// or when a band is only a few tiles long.
+size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_bytes) {
+  const int64_t wg4 = (int64_t)((T + 127) / 128) * H * B;
+  const int64_t cus = (int64_t)cus_per_xcd() * 8;
+  const int64_t band = (int64_t)W + 127 < T ? (int64_t)W + 127 : (int64_t)T;  // longest band
+  const int64_t band_tiles = (band + kBN - 1) / kBN;
+  const bool fits = 2 * wg4 <= 3 * cus;  // the doubled grid is resident at once
+  const bool pays = wg4 <= cus && band_tiles >= 8;
+  if (wg4 <= 0 || !(force ? fits : pays)) return 0;
+  const size_t slots = (size_t)wg4 * 4;
+  const size_t fb = (slots * sizeof(unsigned long long) + 255) & ~(size_t)255;
+  if (flag_bytes) *flag_bytes = fb;
+  return fb + slots * 2 * kSplitPartBytes;
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st) {
   // Four-wave workgroups share each staged (and rotated) K tile among more
   // queries; two-wave ones keep enough workgroups to cover the 256 CUs when
-  // the problem is small.
+  // the problem is small (unless the split walk is on).
   const int64_t wg4 = (int64_t)((a.T + 127) / 128) * a.H * a.B;
-  if (wg4 >= 256 || (a.ring_k && a.rope && !a.table)) return launch_nw<4>(a, out, st);
+  if (wg4 >= 256 || (a.ring_k && a.rope && !a.table) || a.split_flags) return launch_nw<4>(a, out, st);
   return launch_nw<2>(a, out, st);
 }
 

@@ -61,7 +61,8 @@ vx_status check_cfg(const vx_attn_cfg* cfg) {
     return fail(VX_E_DTYPE, "unknown dtype (io %d, out %d)", io, out);
   if (io == VX_F32 && out == VX_BF16)
     return fail(VX_E_DTYPE, "float32 inputs with bfloat16 output is not supported");
-  if (cfg->flags & ~VX_FLAG_VALU_KERNEL) return fail(VX_E_RANGE, "unknown flag bits 0x%x", cfg->flags);
+  if (cfg->flags & ~(VX_FLAG_VALU_KERNEL | VX_FLAG_SPLIT_WALK))
+    return fail(VX_E_RANGE, "unknown flag bits 0x%x", cfg->flags);
   if (cfg->workspace_bytes > 0 && !cfg->workspace)
     return fail(VX_E_NULL, "workspace is NULL but workspace_bytes is %zu", cfg->workspace_bytes);
   if (cfg->workspace && !aligned16(cfg->workspace))
@@ -232,10 +233,18 @@ size_t prefill_table_bytes(int32_t B, int32_t T) {
   return (size_t)B * T * vx::kD * sizeof(float);
 }
 
-vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t B,
-                              int32_t T, int32_t H, const int64_t* pos0, int32_t rope_applied,
-                              const float* rope_table, int64_t table_p0, int64_t table_len,
-                              const vx_attn_cfg* cfg, void* stream) {
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // extern "C"
+
+namespace {
+
+// vx_swa_attn_prefill; allow_split = false keeps the unsplit walk whatever
+// the workspace holds (the allocation-free entry point's bits).
+vx_status prefill_impl(const void* q, const void* k, const void* v, void* o, int32_t B,
+                       int32_t T, int32_t H, const int64_t* pos0, int32_t rope_applied,
+                       const float* rope_table, int64_t table_p0, int64_t table_len,
+                       const vx_attn_cfg* cfg, void* stream, bool allow_split) {
   vx_status st = check_cfg(cfg);
   if (st) return st;
   if ((st = check_dims("prefill", B, T, H))) return st;
@@ -292,6 +301,18 @@ vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void*
       a.table_len = (int64_t)B * T;
     }  // else: cos/sin computed in the kernel
   }
+  // the split walk's flags and partial results, after the table if one is
+  // built there (it serves calls with a table or pre-rotated inputs)
+  if (allow_split && !valu && cfg->workspace && (!a.rope || a.table)) {
+    const size_t off = build_table ? align256(prefill_table_bytes(B, T)) : 0;
+    size_t fb = 0;
+    const size_t sb = vx::prefill_split_bytes(B, T, H, cfg->window,
+                                              (cfg->flags & VX_FLAG_SPLIT_WALK) != 0, &fb);
+    if (sb && cfg->workspace_bytes >= off + sb) {
+      a.split_flags = (unsigned long long*)((char*)cfg->workspace + off);
+      a.split_part = (float*)((char*)cfg->workspace + off + fb);
+    }
+  }
   (void)hipGetLastError();
   if (build_table) {
     vx_status s1 = launched(vx::launch_rope_table_batched((float*)a.table, pos0, B, T, a.fr,
@@ -304,10 +325,24 @@ vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void*
   return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
 }
 
+}  // namespace
+
+extern "C" {
+
+vx_status vx_swa_attn_prefill(const void* q, const void* k, const void* v, void* o, int32_t B,
+                              int32_t T, int32_t H, const int64_t* pos0, int32_t rope_applied,
+                              const float* rope_table, int64_t table_p0, int64_t table_len,
+                              const vx_attn_cfg* cfg, void* stream) {
+  return prefill_impl(q, k, v, o, B, T, H, pos0, rope_applied, rope_table, table_p0, table_len,
+                      cfg, stream, true);
+}
+
 size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
                                           const vx_attn_cfg* cfg) {
   if (check_cfg(cfg) != VX_OK || check_dims("prefill", B, T, H) != VX_OK) return 0;
-  return prefill_table_bytes(B, T);
+  return align256(prefill_table_bytes(B, T)) +
+         vx::prefill_split_bytes(B, T, H, cfg->window, (cfg->flags & VX_FLAG_SPLIT_WALK) != 0,
+                                 nullptr);
 }
 
 vx_status vx_swa_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
@@ -333,7 +368,7 @@ vx_status vx_swa_attn_prefill_noalloc(const void* q, const void* k, const void* 
     c.workspace = p;
     c.workspace_bytes = kNoAllocBytes;
   }
-  return vx_swa_attn_prefill(q, k, v, o, B, T, H, pos0, rope_applied, nullptr, 0, 0, &c, stream);
+  return prefill_impl(q, k, v, o, B, T, H, pos0, rope_applied, nullptr, 0, 0, &c, stream, false);
 }
 
 vx_status vx_swa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,

@@ -45,7 +45,28 @@ struct PrefillArgs {
   void* ring_k = nullptr;
   void* ring_v = nullptr;
   int64_t* pos_out = nullptr;
+  // Split walk (split_flags != nullptr; fixed-length batches with a cos/sin
+  // table or pre-rotated inputs): two workgroups per 128-query tile, each
+  // walking one half of the tile's key band, and per wave the later of the
+  // two merges both partial results.  Layout from prefill_split_bytes:
+  // one flag word per (b, h, query tile, wave), zero between calls (each
+  // call leaves them zero; any value but the kernel's two tokens is taken
+  // as zero), then two partial results of kSplitPartBytes per flag.
+  unsigned long long* split_flags = nullptr;
+  float* split_part = nullptr;
 };
+
+// Bytes of one wave's partial result in the split walk: the 64 x 32 float
+// O^T accumulators and the running max and sum, as 9 rows of 64 x 16 bytes.
+constexpr size_t kSplitPartBytes = (size_t)9 * 64 * 16;
+
+// Workspace bytes of the split walk for a fixed-length prefill of this shape
+// and window on the current device (flag words first, *flag_bytes of them,
+// 256-byte aligned, then the partial results), or 0 where the walk is not
+// taken: grids of more than one 128-query tile per CU or key bands of fewer
+// than 8 tiles; with force, grids whose doubled size is not resident at
+// once (more than 1.5 query tiles per CU).
+size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_bytes);
 
 struct StreamArgs {
   const void* q;

@@ -128,7 +128,7 @@ def prefill(L, b, c, q=None, k=None, v=None, o=None, B=1, T=8, H=2, pos0=None, r
     (dict(rope_theta=0.0), E_RANGE), (dict(rope_theta=float("nan")), E_RANGE),
     (dict(rope_theta=float("inf")), E_RANGE), (dict(softmax_scale=-1.0), E_RANGE),
     (dict(softmax_scale=float("nan")), E_RANGE), (dict(io_dtype=vx.VX_F32, out_dtype=vx.VX_BF16), E_DTYPE),
-    (dict(io_dtype=7), E_DTYPE), (dict(out_dtype=-1), E_DTYPE), (dict(flags=2), E_RANGE),
+    (dict(io_dtype=7), E_DTYPE), (dict(out_dtype=-1), E_DTYPE), (dict(flags=4), E_RANGE),
 ])
 def test_prefill_rejects_bad_cfg(L, kw, status):
     b = Bufs()
@@ -176,9 +176,23 @@ def test_prefill_workspace_checks(L):
 def test_prefill_workspace_size(L):
     size = L.vx_swa_attn_prefill_workspace_size
     c = cfg()
-    # a cos/sin table of B*T rows of 256 bytes
+    # a cos/sin table of B*T rows of 256 bytes (rounded up to 256), then, where
+    # the split walk is taken (at most one 128-query tile per compute unit,
+    # 256 CUs without a device, and key bands of at least 8 tiles; with
+    # VX_FLAG_SPLIT_WALK at most 1.5 tiles per CU, any band), a flag word per
+    # (b, h, query tile, wave), 256-byte aligned, and two 9216-byte partial
+    # results per flag
     assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256
-    assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256
+    assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256  # 384 query tiles: not split
+    slots = 12 * 16 * 4
+    assert size(1, 1500, 16, ctypes.byref(c)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
+    force = cfg(flags=2)
+    slots = 12 * 32 * 4
+    assert size(1, 1500, 32, ctypes.byref(force)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
+    assert size(2, 1500, 32, ctypes.byref(force)) == 2 * 1500 * 256  # 768 tiles: never split
+    assert size(1, 3, 1, ctypes.byref(c)) == 3 * 256  # a one-tile band: not split
+    assert size(1, 3, 1, ctypes.byref(force)) == 3 * 256 + 256 + 4 * 2 * 9216
+    assert size(1, 1500, 16, ctypes.byref(cfg(window=64))) == 1500 * 256  # 3-tile bands
     assert size(1, 1500, 32, None) == 0
     assert size(-1, 1500, 32, ctypes.byref(c)) == 0
     assert size(1, 1500, 32, ctypes.byref(cfg(window=0))) == 0
