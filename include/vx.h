@@ -154,7 +154,13 @@ vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, const in
  * flag words zero, and any content other than the kernel's two tokens reads
  * as zero, so the workspace needs no clearing.  Split results are
  * deterministic but not the same bits as the unsplit walk's (another
- * summation order; within the same tolerance of the exact result). */
+ * summation order; within the same tolerance of the exact result).
+ * On grids of at least 16 query tiles per compute unit (B8 T2048 H32, say)
+ * with a table (the caller's or one built in the workspace), the workspace
+ * also takes the keys rotated once ahead of the attention kernel (one more
+ * launch, B*T*H*64 bf16 after the table), which then stages them without
+ * rotating them again; the rotation reads the same cos/sin rows, so the
+ * results keep their bits. */
 vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void *o, int32_t B,
                               int32_t T, int32_t H, const int64_t *pos0, int32_t rope_applied,
                               const float *rope_table, int64_t table_p0, int64_t table_len,
@@ -166,7 +172,8 @@ vx_status vx_swa_attn_prefill(const void *q, const void *k, const void *v, void 
  * rounded up to 256) and, where it takes the split walk on the current
  * device (cfg->flags counts), the walk's flag word per (b, h, 128-query tile,
  * wave of 32 queries), rounded up to 256 bytes, and two 9216-byte partial
- * results per flag word.  Returns 0 for invalid arguments. */
+ * results per flag word; or, where the keys are rotated ahead of the kernel,
+ * B*T*H rows of 128 bytes for them.  Returns 0 for invalid arguments. */
 size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
                                           const vx_attn_cfg *cfg);
 

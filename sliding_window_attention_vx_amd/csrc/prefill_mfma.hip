@@ -255,8 +255,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, uint3
 }
 
 // With OTF the cos/sin of the staged keys are computed from their positions
-// (p0 = position of frame 0) instead of read from the table.
-template <int NW, bool OTF>
+// (p0 = position of frame 0) instead of read from the table; without KROT
+// the keys arrive rotated and no cos/sin is loaded at all.
+template <int NW, bool OTF, bool KROT>
 __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict__ k,
                                            const bf16* __restrict__ v, size_t rs, int T, int kt0,
                                            bool rope, const PrefillArgs& a, int64_t trow0,
@@ -269,7 +270,8 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
   for (int j = 0; j < Stage<NW>::UK; ++j) {
     st.kx[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j], 0, 0);
     st.ky[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j] + 2 * kHalf, 0, 0);
-    if (OTF) {
+    if (!KROT) {
+    } else if (OTF) {
       if (rope) {
         const int64_t p = p0 + kt0 + so.kr[j];
 #pragma unroll
@@ -312,7 +314,7 @@ struct Seed {
   }
 };
 
-template <int NW, bool SEED = false>
+template <int NW, bool SEED = false, bool KROT = true>
 __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char* Vb, bool rope,
                                              int tid, const Seed& sd = Seed{}) {
   constexpr int NT = Stage<NW>::NT;
@@ -321,7 +323,7 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
     int r, cp;
     k_unit(tid + j * NT, r, cp);
     u32x4 x = st.kx[j], y = st.ky[j];
-    if (rope) {
+    if (KROT && rope) {
       float xf[8], yf[8];
       unpack8(st.kx[j], xf);
       unpack8(st.ky[j], yf);
@@ -362,12 +364,13 @@ __device__ __forceinline__ unsigned long long lane0_u64(unsigned long long x) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT>
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT, bool KROT>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
                                                                   int n_short, int hx, int cpx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   constexpr int BM = NW * 32;
   static_assert(!SPLIT || (!SEED && !OTF), "the split walk serves fixed-length calls with a table");
+  static_assert(KROT || (!SEED && !OTF && !SPLIT), "keys arrive rotated only in plain calls");
 
   int bh, qt, half;
   if (!work_item<SPLIT>(a.B * a.H, n_qtiles, n_short, hx, cpx, bh, qt, half)) return;
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
   Stage<NW> st;
   const StageOffs<NW> so = stage_offsets<NW>(tid, rs);
-  stage_load<NW, OTF>(st, k, v, rs, T, it_start * kBN, rope, a, trow0, p0, so);
+  stage_load<NW, OTF, KROT>(st, k, v, rs, T, it_start * kBN, rope, a, trow0, p0, so);
   if (rope && !OTF) {
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     sd.kt0 = kt0;
     return sd;
   };
-  stage_commit<NW, SEED>(st, lds, lds + kTileK, rope, tid, seed_for(it_start * kBN));
+  stage_commit<NW, SEED, KROT>(st, lds, lds + kTileK, rope, tid, seed_for(it_start * kBN));
   __syncthreads();
 
   // One step per key tile: the next tile's loads go out first (after the
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   int j = 0;
   auto tile_step = [&](const int it, const int kt_next) {
     const int buf = j & 1;
-    stage_load<NW, OTF>(st, k, v, rs, T, kt_next, rope, a, trow0, p0, so);
+    stage_load<NW, OTF, KROT>(st, k, v, rs, T, kt_next, rope, a, trow0, p0, so);
 
     const char* Kb = lds + buf * kStageBytes;
     const char* Vb = Kb + kTileK;
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     }
 
     if (kt_next < T)
-      stage_commit<NW, SEED>(st, lds + (buf ^ 1) * kStageBytes,
+      stage_commit<NW, SEED, KROT>(st, lds + (buf ^ 1) * kStageBytes,
                              lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid,
                              seed_for(kt_next));
     __syncthreads();
@@ -798,11 +801,11 @@ int cus_per_xcd() {
   return c;
 }
 
-template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT = false>
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT = false, bool KROT = true>
 void launch_k(dim3 g, dim3 blk, hipStream_t st, const PrefillArgs& a, int n_qtiles, int n_short,
               int hx, int cpx) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF, SPLIT>), g, blk, 0, st, a, n_qtiles,
-                     n_short, hx, cpx);
+  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF, SPLIT, KROT>), g, blk, 0, st, a,
+                     n_qtiles, n_short, hx, cpx);
 }
 
 template <int NW>
@@ -825,6 +828,15 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
     }
   }
   const dim3 g((unsigned)grid);
+  if constexpr (NW == 4) {
+    // keys already rotated (ahead of the kernel, or pre-rotated input): no
+    // cos/sin loads or key rotation in the staging
+    if (!a.cu && !a.ring_k && !otf && (a.k_rotated || !a.rope)) {
+      if (out == DT::BF16) launch_k<NW, bf16, false, false, false, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+      else launch_k<NW, float, false, false, false, false>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+      return hipGetLastError();
+    }
+  }
   if (a.ring_k) {
     // (seeding with in-kernel cos/sin runs four-wave workgroups only: the
     // two-wave variant would need more than 256 VGPRs)
@@ -869,6 +881,18 @@ size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_
   const size_t fb = (slots * sizeof(unsigned long long) + 255) & ~(size_t)255;
   if (flag_bytes) *flag_bytes = fb;
   return fb + slots * 2 * kSplitPartBytes;
+}
+
+// Rotating the keys ahead of the kernel costs one more read and write of K
+// (a launch of its own) and saves the kernel about a quarter of its vector
+// work, which sets its pace at full occupancy: measured, B8 T6000 H32 523
+// against 549 us and B32 T1500 H32 461 against 478, but B4 T1500 H32 60.7
+// against 59.0.  So only grids of at least 16 query tiles per CU take it.
+size_t prefill_krot_bytes(int B, int T, int H) {
+  const int64_t wg4 = (int64_t)((T + 127) / 128) * H * B;
+  const int64_t cus = (int64_t)cus_per_xcd() * 8;
+  if (wg4 < 16 * cus) return 0;
+  return (size_t)B * T * H * kD * sizeof(bf16);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st) {

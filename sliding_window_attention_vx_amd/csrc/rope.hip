@@ -78,6 +78,70 @@ __global__ __launch_bounds__(128) void rope_qk_kernel(T* __restrict__ q, T* __re
   }
 }
 
+// Keys rotated once, into a separate buffer, for a prefill that then stages
+// them as they are: frame t of batch entry b takes the cos/sin row the
+// prefill's own staging would read (row table_bstride*b + (table_pos ?
+// pos0[b] : 0) + t + table_off), and the same rotation, so the prefill's
+// results keep their bits.  One workgroup per (b, t) frame, its row of the
+// table in LDS for all H heads.  Frames whose row lies outside the table, or
+// whose entry has a negative position, are skipped: the prefill writes NaN
+// over such an entry without reading its keys.
+__global__ __launch_bounds__(128) void rope_k_table_kernel(
+    const bf16* __restrict__ k, bf16* __restrict__ ko, int T_, int H,
+    const int64_t* __restrict__ pos0, const float* __restrict__ table, int64_t table_off,
+    int64_t table_bstride, bool table_pos, int64_t table_len) {
+  __shared__ __attribute__((aligned(16))) float cs[kD];
+  const int64_t row = blockIdx.x;  // b * T + t
+  const int64_t b = row / T_;
+  const int t = (int)(row - b * T_);
+  const int64_t p0 = pos0 ? pos0[b] : 0;
+  const int64_t tr = table_bstride * b + (table_pos ? p0 : 0) + table_off + t;
+  if (p0 < 0 || tr < 0 || tr >= table_len) return;  // the same for the whole workgroup
+  const int units = H * 4;  // (head, 8-pair chunk)
+  // with one chunk per thread (H <= 32) its key loads go out before the
+  // table row's, so the two memory latencies overlap
+  const bool one = units <= (int)blockDim.x;
+  float x[8], y[8];
+  const size_t off1 = (size_t)row * H * kD + (size_t)(threadIdx.x >> 2) * kD + 8 * (threadIdx.x & 3);
+  if (one && (int)threadIdx.x < units) {
+    load8(k + off1, x);
+    load8(k + off1 + kHalf, y);
+  }
+  if (threadIdx.x < kD / 4)
+    reinterpret_cast<f32x4*>(cs)[threadIdx.x] =
+        reinterpret_cast<const f32x4*>(table + tr * kD)[threadIdx.x];
+  __syncthreads();
+  auto rotate = [&](size_t off, int c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float xo, yo;
+      rope_pair(x[e], y[e], cs[8 * c + e], cs[kHalf + 8 * c + e], &xo, &yo);
+      x[e] = xo;
+      y[e] = yo;
+    }
+    store8(ko + off, x);
+    store8(ko + off + kHalf, y);
+  };
+  if (one) {
+    if ((int)threadIdx.x < units) rotate(off1, threadIdx.x & 3);
+    return;
+  }
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const size_t off = (size_t)(row * H + (u >> 2)) * kD + 8 * (u & 3);
+    load8(k + off, x);
+    load8(k + off + kHalf, y);
+    rotate(off, u & 3);
+  }
+}
+
+hipError_t launch_rope_k_table(const PrefillArgs& a, void* k_out, hipStream_t st) {
+  const unsigned blocks = (unsigned)((int64_t)a.B * a.T);
+  hipLaunchKernelGGL(rope_k_table_kernel, dim3(blocks), dim3(128), 0, st, (const bf16*)a.k,
+                     (bf16*)k_out, a.T, a.H, a.pos0, a.table, a.table_off, a.table_bstride,
+                     a.table_pos, a.table_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table(float* table, int64_t p_begin, int count, const RopeFreqs& fr,
                              hipStream_t st) {
   const int64_t total = (int64_t)count * kHalf;

@@ -301,10 +301,18 @@ vx_status prefill_impl(const void* q, const void* k, const void* v, void* o, int
       a.table_len = (int64_t)B * T;
     }  // else: cos/sin computed in the kernel
   }
-  // the split walk's flags and partial results, after the table if one is
-  // built there (it serves calls with a table or pre-rotated inputs)
+  // After the table if one is built there: the split walk's flags and
+  // partial results (small grids, with a table or pre-rotated inputs), or
+  // the keys rotated ahead of the kernel (large grids with a table); the two
+  // never apply to the same grid.
+  const size_t ws_off = build_table ? align256(prefill_table_bytes(B, T)) : 0;
+  void* k_rot = nullptr;
+  if (!valu && cfg->workspace && a.rope && a.table) {
+    const size_t kb = vx::prefill_krot_bytes(B, T, H);
+    if (kb && cfg->workspace_bytes >= ws_off + kb) k_rot = (char*)cfg->workspace + ws_off;
+  }
   if (allow_split && !valu && cfg->workspace && (!a.rope || a.table)) {
-    const size_t off = build_table ? align256(prefill_table_bytes(B, T)) : 0;
+    const size_t off = ws_off;
     size_t fb = 0;
     const size_t sb = vx::prefill_split_bytes(B, T, H, cfg->window,
                                               (cfg->flags & VX_FLAG_SPLIT_WALK) != 0, &fb);
@@ -322,6 +330,12 @@ vx_status prefill_impl(const void* q, const void* k, const void* v, void* o, int
   if (valu)
     return launched(vx::launch_prefill_valu(a, to_dt(cfg->io_dtype), to_dt(cfg->out_dtype),
                                             (hipStream_t)stream));
+  if (k_rot) {
+    vx_status s2 = launched(vx::launch_rope_k_table(a, k_rot, (hipStream_t)stream));
+    if (s2) return s2;
+    a.k = k_rot;
+    a.k_rotated = true;
+  }
   return launched(vx::launch_prefill_mfma(a, to_dt(cfg->out_dtype), (hipStream_t)stream));
 }
 
@@ -342,7 +356,8 @@ size_t vx_swa_attn_prefill_workspace_size(int32_t B, int32_t T, int32_t H,
   if (check_cfg(cfg) != VX_OK || check_dims("prefill", B, T, H) != VX_OK) return 0;
   return align256(prefill_table_bytes(B, T)) +
          vx::prefill_split_bytes(B, T, H, cfg->window, (cfg->flags & VX_FLAG_SPLIT_WALK) != 0,
-                                 nullptr);
+                                 nullptr) +
+         vx::prefill_krot_bytes(B, T, H);
 }
 
 vx_status vx_swa_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,

@@ -54,6 +54,9 @@ struct PrefillArgs {
   // as zero), then two partial results of kSplitPartBytes per flag.
   unsigned long long* split_flags = nullptr;
   float* split_part = nullptr;
+  // k holds keys already rotated (by launch_rope_k_table) while q is rotated
+  // per `rope`: the kernel stages the keys as they are
+  bool k_rotated = false;
 };
 
 // Bytes of one wave's partial result in the split walk: the 64 x 32 float
@@ -67,6 +70,11 @@ constexpr size_t kSplitPartBytes = (size_t)9 * 64 * 16;
 // than 8 tiles; with force, grids whose doubled size is not resident at
 // once (more than 1.5 query tiles per CU).
 size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_bytes);
+
+// Workspace bytes of the rotated keys for a fixed-length prefill of this
+// shape on the current device (B*T*H*64 bf16), or 0 where the grid is too
+// small for rotating the keys once, ahead of the kernel, to pay off.
+size_t prefill_krot_bytes(int B, int T, int H);
 
 struct StreamArgs {
   const void* q;
@@ -107,6 +115,9 @@ hipError_t launch_rope_qk(void* q, void* k, int B, int T, int H, const int64_t* 
 // Table rows b*T + t = cos/sin of position pos0[b] + t (pos0 nullptr = 0).
 hipError_t launch_rope_table_batched(float* table, const int64_t* pos0, int B, int T,
                                      const RopeFreqs& fr, hipStream_t st);
+// Rotated keys of a prefill with a cos/sin table (a.table, its row mapping)
+// written to k_out ([B, T, H, 64] bf16).
+hipError_t launch_rope_k_table(const PrefillArgs& a, void* k_out, hipStream_t st);
 hipError_t launch_prefill_valu(const PrefillArgs& a, DT io, DT out, hipStream_t st);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st);
 hipError_t launch_stream_step(const StreamArgs& a, DT io, DT out, const RopeFreqs& fr,

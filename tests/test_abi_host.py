@@ -182,7 +182,13 @@ def test_prefill_workspace_size(L):
     # VX_FLAG_SPLIT_WALK at most 1.5 tiles per CU, any band), a flag word per
     # (b, h, query tile, wave), 256-byte aligned, and two 9216-byte partial
     # results per flag
-    assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256
+    # grids of at least 16 query tiles per CU also keep the keys rotated
+    # ahead of the kernel there (B*T*H rows of 128 bytes)
+    assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256 + 8 * 6000 * 32 * 128
+    assert size(8, 2048, 32, ctypes.byref(c)) == 8 * 2048 * 256 + 8 * 2048 * 32 * 128
+    assert size(8, 1500, 32, ctypes.byref(c)) == 8 * 1500 * 256  # 12 tiles per CU: not
+    assert size(4, 1500, 32, ctypes.byref(c)) == 4 * 1500 * 256
+    assert size(2, 1500, 32, ctypes.byref(c)) == 2 * 1500 * 256  # 768 query tiles: neither
     assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256  # 384 query tiles: not split
     slots = 12 * 16 * 4
     assert size(1, 1500, 16, ctypes.byref(c)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
