@@ -256,7 +256,7 @@ def rope_qk(q, k, pos0=None, theta=THETA):
 
 def prefill_workspace_size(B, T, H, window=WINDOW, theta=THETA, force_split=False):
     """Bytes of workspace with which prefill() of this shape keeps its cos/sin table
-    there and, on grids small enough for it, takes the split walk."""
+    there and takes the split walk (small grids) or rotates its keys ahead (large ones)."""
     cfg = Config(window, theta, force_split=force_split).c()
     return int(lib().vx_swa_attn_prefill_workspace_size(int(B), int(T), int(H), ctypes.byref(cfg)))
 
@@ -283,7 +283,9 @@ def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_appl
     across calls; None runs without one.  With a workspace, grids of at most
     one 128-query tile per compute unit and key bands of 8 tiles or more
     take the split walk (two workgroups per query tile); force_split takes it
-    on every grid small enough for it.
+    on every grid small enough for it.  Grids of at least 16 tiles per unit
+    with a table rotate their keys once, into the workspace, ahead of the
+    attention kernel (the same bits).
     """
     import torch
     for name, x in (("q", q), ("k", k), ("v", v)):
