@@ -284,6 +284,12 @@ def main():
     def long_pass(i):
         vx.prefill(*long_in, window=lgc.W, table=long_tab, out=long_o, workspace=long_ws)
 
+    # one stack layer on q and k rotated upstream (RoPE applied by the q/k/v
+    # projection's epilogue, as in the encoder step): no cos/sin staging at all
+    def stack_layer_rope_upstream(i):
+        sq, sk, sv = stack_in[0]
+        vx.prefill(sq, sk, sv, window=stc.W, rope_applied=True, out=stack_o)
+
     # the same call without a workspace: keys rotated in the kernel's staging
     def long_in_kernel(i):
         vx.prefill(*long_in, window=lgc.W, table=long_tab, out=long_o)
@@ -561,6 +567,7 @@ def main():
         legs["stack_one_call"] = (stack_one_call, 1, 1)
         legs["long"] = (long_pass, max(K // 5, 4), max(K // 5, 4))
         legs["long_in_kernel"] = (long_in_kernel, max(K // 5, 4), max(K // 5, 4))
+        legs["stack_layer_rope_upstream"] = (stack_layer_rope_upstream, reps, reps)
     for name, (fn, n_, _) in legs.items():
         fn(-1)  # first-launch and first-touch costs stay out of the passes
     torch.cuda.synchronize()
@@ -711,6 +718,7 @@ def main():
                         "call rotates its keys once, ahead of the attention kernel)",
             "us_per_stack": round(stack_us, 3),
             "us_per_layer": round(stack_us / stc.layers, 3),
+            "us_per_layer_rope_upstream": round(med["stack_layer_rope_upstream"], 3),
             "us_one_call_B128": round(stack_one_us, 3),
             "tflops_one_call_B128": round(stack_flops / (stack_one_us * 1e-6) / 1e12, 2),
             "roofline": {"kernel": "prefill_mfma_kernel", "bound": "mfma",
