@@ -152,7 +152,7 @@ def main():
                          "about 30 s to draw on the host)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the work shards by batch, head or stream with no communication).",
               file=sys.stderr)
         sys.exit(2)
