@@ -56,14 +56,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-               "1d2c8e87e1f8a5a1e8f9fb76224481b84578bd4f906dac3b4c9288044c652bff",
-               21_719_410 + 6_144_000),
+               "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
+               21_719_881 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
               "7823f39e6c6bb863f6330420c0f9775166a1ba66eed09eda0c641f0ded7f9820",
               396_079_283 + 3_146_512),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                   "1d2c8e87e1f8a5a1e8f9fb76224481b84578bd4f906dac3b4c9288044c652bff",
-                   155_821_333 + 107_363_584),
+                   "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
+                   155_773_176 + 107_363_608),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "71d51d1bade315e29fb14b1164cdef63eb44efb65221e448a1e6a7302bfe4288",
                    2_148_346_558 + 786_944),
@@ -77,11 +77,11 @@ MEASURED_TRAFFIC = {
                     "5feee362e008dbf0c8734e53c411e85c079a11a14a2749654e18950708698381",
                     450_948_348 + 134_504_800),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "1d2c8e87e1f8a5a1e8f9fb76224481b84578bd4f906dac3b4c9288044c652bff",
-             103_951_735 + 24_576_128),
+             "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
+             103_888_047 + 24_576_000),
     "long": (("prefill_mfma.hip", "rope.hip", "vx_device.h", "vx_launch.h"),
-            "2c28eb693314ddb3012097c275104c9fed0d9646eed639dcd10b3827a4548e63",
-            (951_475_739 + 196_608_960) + (208_804_501 + 196_608_128)),
+            "71aa5b889d4328905b1a91440a32b2b37240e99bfdbc540c168f6a3df9ea9ab5",
+            (951_333_253 + 196_608_432) + (208_806_050 + 196_608_112)),
 }
 
 

@@ -38,21 +38,28 @@
 // score.  Accumulators stay in VGPRs (the build asks for the VGPR form of
 // MFMA) so the softmax never moves them between register files.
 //
-// Split walk, for grids too small to fill the device (about 1.5 workgroups
-// per CU, e.g. one 1500-frame chunk of 32 heads): each query tile gets two
-// workgroups, the first walking the older half of its key tiles and the
-// second the newer half, so each wave's chain of dependent tile steps is
-// half as long and the device holds twice the waves.  Softmax partials
-// combine exactly: with running maxima m0, m1 and m = max(m0, m1), the
-// merged sum is l0 2^(m0-m) + l1 2^(m1-m) and likewise for O^T.  Per wave,
-// whichever half finishes second does the merge: a half that finds its
-// partner's token already in the wave's flag word merges at once; otherwise
-// it stores its partial result (device-coherent stores, waited for) and
-// swaps its own token into the flag, and merges only if the swap returns
-// the partner's token.  The merger resets the flag to zero, so every call leaves the flags
-// as it found them (also across graph replays), and computes the merge with
-// the halves in a fixed order, so the bits do not depend on which finished
-// first.  Nothing ever waits on another workgroup.
+// Split walk, for grids too small to fill the device (at most one query
+// tile per CU with key bands of 8 tiles or more, e.g. one 500-frame chunk
+// of 32 heads): each query tile gets two workgroups, the first walking the
+// older half of its key tiles and the second the newer half, so each wave's
+// chain of dependent tile steps is half as long and the device holds twice
+// the waves.  Softmax partials combine exactly: with running maxima m0, m1
+// and m = max(m0, m1), the merged sum is l0 2^(m0-m) + l1 2^(m1-m) and
+// likewise for O^T.  Per wave, whichever half finishes second does the
+// merge: a half that finds its partner's token already in the wave's flag
+// word merges at once; otherwise it stores its partial result
+// (device-coherent stores, waited for) and swaps its own token into the
+// flag, and merges only if the swap returns the partner's token.  The
+// merger resets the flag to zero, so every call leaves the flags as it found
+// them (also across graph replays), and computes the merge with the halves
+// in a fixed order, so the bits do not depend on which finished first.
+// Nothing ever waits on another workgroup.
+//
+// Rotated keys (KROT = false): when the keys were rotated ahead of the
+// kernel (large grids, where the staging's rotation of every key tile in
+// each of the ~7 workgroups that visit it costs more than one extra pass
+// over K) or come pre-rotated, the staging loads neither cos/sin nor
+// rotates; queries are still rotated per `rope`.
 #include "vx_launch.h"
 
 namespace vx {
@@ -270,7 +277,8 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
   for (int j = 0; j < Stage<NW>::UK; ++j) {
     st.kx[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j], 0, 0);
     st.ky[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, so.k[j] + 2 * kHalf, 0, 0);
-    if (!KROT) {
+    if constexpr (!KROT) {
+      // rotated keys: no cos/sin
     } else if (OTF) {
       if (rope) {
         const int64_t p = p0 + kt0 + so.kr[j];
