@@ -62,9 +62,9 @@ typedef enum { VX_F32 = 0, VX_BF16 = 1 } vx_dtype;
 #define VX_FLAG_VALU_KERNEL 1u /* prefill: use the float32 vector-ALU kernel instead of the
                                   bf16 matrix-core kernel (a cross-check; bf16 inputs still
                                   get bf16-rounded rotated q and k) */
-#define VX_FLAG_SPLIT_WALK 2u  /* prefill: take the split walk (see vx_swa_attn_prefill) on
-                                  every grid of at most 1.5 query tiles per compute unit,
-                                  also where it does not pay off */
+#define VX_FLAG_SPLIT_WALK 2u  /* prefill: take the split walk (see vx_swa_attn_prefill),
+                                  given a workspace, on grids of at most 1.5 query tiles
+                                  per compute unit instead of the halves-split workgroups */
 
 typedef struct {
   int32_t head_dim;      /* must be 64                                              */
@@ -141,19 +141,24 @@ vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, const in
  * cfg->workspace (optional): with at least
  * vx_swa_attn_prefill_workspace_size() bytes, a NULL rope_table is served
  * from a table built in it (one extra launch); the results are the same bits
- * as with a caller table or cos/sin computed in the kernel.  The same
- * workspace also enables the split walk (bf16 matrix-core path, with a
- * table or rope_applied) on grids of at most one 128-query tile per compute
- * unit whose key bands span at least 8 tiles of 64 keys (with
- * VX_FLAG_SPLIT_WALK: every grid of at most 1.5 tiles per unit): two
- * workgroups per query tile, one per half of its key band, whose softmax
- * partials the later of the two merges (the exact rescaling of running
- * maxima and sums that flash attention's online softmax uses).  Its flag
+ * as with a caller table or cos/sin computed in the kernel.
+ * Schedules (bf16 matrix-core path): grids of at most 1.5 128-query tiles
+ * per compute unit (one 1500-frame chunk of 32 heads and smaller) run
+ * 64-query workgroups whose two waves per 32-query block each take one
+ * 32-key half of every key tile and merge their softmax partials at the
+ * end (the exact rescaling of running maxima and sums that flash
+ * attention's online softmax uses); larger grids run 128-query workgroups.
+ * The two schedules differ in summation order, so a call's bits depend on
+ * its grid size (within the same tolerance of the exact result).
+ * With VX_FLAG_SPLIT_WALK and a workspace (with a table or rope_applied),
+ * such small grids take the split walk instead: two workgroups per 128-query
+ * tile, one per half of its key band, the later of the two merging both
+ * partials.  Its flag
  * words and partial results follow the table in the workspace (which must
  * then not be shared by calls that overlap in time); each call leaves the
  * flag words zero, and any content other than the kernel's two tokens reads
  * as zero, so the workspace needs no clearing.  Split results are
- * deterministic but not the same bits as the unsplit walk's (another
+ * deterministic but not the same bits as the default schedule's (another
  * summation order; within the same tolerance of the exact result).
  * On grids of at least 16 query tiles per compute unit (B8 T2048 H32, say)
  * with a table (the caller's or one built in the workspace), the workspace

@@ -38,9 +38,17 @@
 // score.  Accumulators stay in VGPRs (the build asks for the VGPR form of
 // MFMA) so the softmax never moves them between register files.
 //
-// Split walk, for grids too small to fill the device (at most one query
-// tile per CU with key bands of 8 tiles or more, e.g. one 500-frame chunk
-// of 32 heads): each query tile gets two workgroups, the first walking the
+// Halves split (HS), the schedule of grids too small to fill the device (at
+// most 1.5 four-wave query tiles per CU, e.g. one 1500-frame chunk of 32
+// heads): 64-query workgroups of four waves, two per 32-query block, each
+// wave taking one 32-key half of every staged tile, so a wave's tile step is
+// half as long and the device holds twice the workgroups; the two waves of a
+// block merge their partial results through LDS at the end.  Each key tile
+// is staged for 64 queries instead of 128, which costs more vector work in
+// all, so larger grids keep 128-query workgroups.
+//
+// Split walk (on request, with a workspace), for the same small grids: each
+// query tile gets two workgroups, the first walking the
 // older half of its key tiles and the second the newer half, so each wave's
 // chain of dependent tile steps is half as long and the device holds twice
 // the waves.  Softmax partials combine exactly: with running maxima m0, m1
@@ -372,13 +380,17 @@ __device__ __forceinline__ unsigned long long lane0_u64(unsigned long long x) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT, bool KROT>
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT, bool KROT, bool HS>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
                                                                   int n_short, int hx, int cpx) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
-  constexpr int BM = NW * 32;
+  // HS (halves split): four waves cover 64 queries, two per 32-query block,
+  // each taking one 32-key half of every staged tile; the two merge through
+  // LDS at the end
+  constexpr int BM = HS ? 64 : NW * 32;
   static_assert(!SPLIT || (!SEED && !OTF), "the split walk serves fixed-length calls with a table");
   static_assert(KROT || (!SEED && !OTF && !SPLIT), "keys arrive rotated only in plain calls");
+  static_assert(!HS || (NW == 4 && !SEED && !SPLIT), "halves split: plain four-wave calls");
 
   int bh, qt, half;
   if (!work_item<SPLIT>(a.B * a.H, n_qtiles, n_short, hx, cpx, bh, qt, half)) return;
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       bad = true;  // a stream longer than the call's bound: NaN rows, pos untouched
     } else {
       if (SEED && h == 0 && qt == 0 && threadIdx.x == 0) a.pos_out[b] = T;
-      if (qt * NW * 32 >= T) return;
+      if (qt * BM >= T) return;
     }
   }
   // T and row0 are the same in every lane; saying so keeps the buffer
@@ -430,7 +442,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
   }
 
   const int q0 = qt * BM;
-  const int qw = q0 + wave * 32;
+  const int qblk = HS ? (wave & 1) : wave;  // this wave's 32-query block
+  const int hsb = HS ? (wave >> 1) : 0;     // HS: this wave's 32-key half of each tile
+  const int qw = q0 + qblk * 32;
   const int tq = qw + l32;  // this lane's query
 
   const int kbeg = max(0, q0 - W + 1);
@@ -652,7 +666,25 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
       act[sb] = (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
       msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
     }
-    if (act[0] || act[1]) {
+    if constexpr (HS) {
+      if (act[hsb]) {
+        f32x16 sc = s_half(hsb);
+        if (msk[hsb]) {
+          const int d0 = tq - (kt0 + 32 * hsb + 4 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            sc[r] = ((unsigned)(d0 - off) <= wm1) ? sc[r] : -INFINITY;
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        update_max(mx);
+        const float mu = m_run;
+        pv_half(sc, hsb, mu);
+      }
+    } else if (act[0] || act[1]) {
       // Software pipeline over the two 32-key halves: the second half's score
       // MFMAs are issued before the first half's softmax, so the matrix core
       // runs while the VALU computes exponentials.
@@ -765,6 +797,36 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     }
   }
 
+  if constexpr (HS) {
+    // the wave of the second key half hands its partial result (O^T, m, l)
+    // to the wave of the first through LDS (the tiles are done with: every
+    // wave passed the last step's barrier); the merge takes the halves in a
+    // fixed order
+    f32x4* part = reinterpret_cast<f32x4*>(lds) + qblk * 9 * 64 + lane;
+    if (hsb == 1) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        part[r * 64] = f32x4{oacc[r >> 2][4 * (r & 3)], oacc[r >> 2][4 * (r & 3) + 1],
+                             oacc[r >> 2][4 * (r & 3) + 2], oacc[r >> 2][4 * (r & 3) + 3]};
+      part[8 * 64] = f32x4{m_run, l_run, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (hsb == 1) return;
+    f32x4 po[9];
+#pragma unroll
+    for (int r = 0; r < 9; ++r) po[r] = part[r * 64];
+    const float m0 = m_run, m1 = po[8][0];
+    const float mm = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l_run * a0 + po[8][1] * a1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        oacc[r >> 2][4 * (r & 3) + e] = oacc[r >> 2][4 * (r & 3) + e] * a0 + po[r][e] * a1;
+    }
+  }
+
   // ---- epilogue: O = O^T / l, lane holds query tq, dims 32db + 8g + 4hh + (0..3)
   const float l_tot = partner_sum(l_run);
   if (tq < T) {
@@ -809,11 +871,36 @@ int cus_per_xcd() {
   return c;
 }
 
-template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT = false, bool KROT = true>
+template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT = false, bool KROT = true,
+          bool HS = false>
 void launch_k(dim3 g, dim3 blk, hipStream_t st, const PrefillArgs& a, int n_qtiles, int n_short,
               int hx, int cpx) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF, SPLIT, KROT>), g, blk, 0, st, a,
+  hipLaunchKernelGGL((prefill_mfma_kernel<NW, TO, SEED, OTF, SPLIT, KROT, HS>), g, blk, 0, st, a,
                      n_qtiles, n_short, hx, cpx);
+}
+
+// Halves split: 64-query workgroups of four waves (see the kernel).
+hipError_t launch_hs(const PrefillArgs& a, DT out, hipStream_t st) {
+  constexpr int BM = 64;
+  const int n_qtiles = (a.T + BM - 1) / BM;
+  const int n_short = min(n_qtiles, (a.W - 1 + BM - 1) / BM);
+  const int n_bh = a.B * a.H;
+  const int hx = n_bh >= 8 ? (n_bh + 7) / 8 : 0;
+  const int cpx = cus_per_xcd();
+  const int64_t grid = hx > 0 ? (int64_t)8 * hx * n_qtiles : (int64_t)n_bh * n_qtiles;
+  const dim3 g((unsigned)grid), blk(256);
+  const bool krot = a.rope && !a.k_rotated;
+  const bool otf = a.rope && !a.table;  // no table: cos/sin computed in the kernel
+  if (out == DT::BF16) {
+    if (otf) launch_k<4, bf16, false, true, false, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    else if (krot) launch_k<4, bf16, false, false, false, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    else launch_k<4, bf16, false, false, false, false, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+  } else {
+    if (otf) launch_k<4, float, false, true, false, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    else if (krot) launch_k<4, float, false, false, false, true, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+    else launch_k<4, float, false, false, false, false, true>(g, blk, st, a, n_qtiles, n_short, hx, cpx);
+  }
+  return hipGetLastError();
 }
 
 template <int NW>
@@ -871,20 +958,24 @@ hipError_t launch_nw(const PrefillArgs& a, DT out, hipStream_t st) {
 
 }  // namespace
 
-// The split walk pays off while the unsplit grid has at most one four-wave
-// workgroup per CU (its doubled grid then stays resident, at most two per
-// CU) and the key bands are long: the merge adds about three dependent
-// device-coherent memory round trips to a wave's end, which costs more than
-// halving the walk saves once the CUs hold more than one query tile each,
-// or when a band is only a few tiles long.
+// The split walk pays off against the plain four-wave grid while that grid
+// has at most one workgroup per CU and the key bands are long: the merge
+// adds about three dependent device-coherent memory round trips to a wave's
+// end, which costs more than halving the walk saves once the CUs hold more
+// than one query tile each, or when a band is only a few tiles long.
 size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_bytes) {
   const int64_t wg4 = (int64_t)((T + 127) / 128) * H * B;
   const int64_t cus = (int64_t)cus_per_xcd() * 8;
   const int64_t band = (int64_t)W + 127 < T ? (int64_t)W + 127 : (int64_t)T;  // longest band
   const int64_t band_tiles = (band + kBN - 1) / kBN;
+  // The halves-split workgroups serve the same small grids as well or better
+  // (B1 T1500 H16 17.3 against 17.7 us, B1 T500 H32 11.7 against 11.8, B4
+  // T150 H32 7.2 against 10.2; the tiniest grids 2 % slower, B1 T1500 H4
+  // 16.3 against 16.0) with no workspace, so the split walk runs only on
+  // request (VX_FLAG_SPLIT_WALK), on grids whose doubled size is resident.
+  (void)band_tiles;
   const bool fits = 2 * wg4 <= 3 * cus;  // the doubled grid is resident at once
-  const bool pays = wg4 <= cus && band_tiles >= 8;
-  if (wg4 <= 0 || !(force ? fits : pays)) return 0;
+  if (wg4 <= 0 || !force || !fits) return 0;
   const size_t slots = (size_t)wg4 * 4;
   const size_t fb = (slots * sizeof(unsigned long long) + 255) & ~(size_t)255;
   if (flag_bytes) *flag_bytes = fb;
@@ -903,11 +994,21 @@ size_t prefill_krot_bytes(int B, int T, int H) {
   return (size_t)B * T * H * kD * sizeof(bf16);
 }
 
+// Halves split for grids whose 64-query workgroups are all resident at once
+// (three per CU): twice the workgroups of the four-wave grid, each wave's
+// tile step half as long.
+bool prefill_half_split(int B, int T, int H) {
+  const int64_t wg4 = (int64_t)((T + 127) / 128) * H * B;
+  const int64_t cus = (int64_t)cus_per_xcd() * 8;
+  return wg4 > 0 && 2 * wg4 <= 3 * cus;
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, DT out, hipStream_t st) {
   // Four-wave workgroups share each staged (and rotated) K tile among more
   // queries; two-wave ones keep enough workgroups to cover the 256 CUs when
   // the problem is small (unless the split walk is on).
   const int64_t wg4 = (int64_t)((a.T + 127) / 128) * a.H * a.B;
+  if (a.half_split && !a.split_flags && !a.cu && !a.ring_k) return launch_hs(a, out, st);
   if (wg4 >= 256 || (a.ring_k && a.rope && !a.table) || a.split_flags) return launch_nw<4>(a, out, st);
   return launch_nw<2>(a, out, st);
 }

@@ -330,6 +330,7 @@ vx_status prefill_impl(const void* q, const void* k, const void* v, void* o, int
   if (valu)
     return launched(vx::launch_prefill_valu(a, to_dt(cfg->io_dtype), to_dt(cfg->out_dtype),
                                             (hipStream_t)stream));
+  a.half_split = vx::prefill_half_split(B, T, H);
   if (k_rot) {
     vx_status s2 = launched(vx::launch_rope_k_table(a, k_rot, (hipStream_t)stream));
     if (s2) return s2;

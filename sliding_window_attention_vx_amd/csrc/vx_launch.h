@@ -57,6 +57,8 @@ struct PrefillArgs {
   // k holds keys already rotated (by launch_rope_k_table) while q is rotated
   // per `rope`: the kernel stages the keys as they are
   bool k_rotated = false;
+  // 64-query workgroups whose waves take one 32-key half of each tile
+  bool half_split = false;
 };
 
 // Bytes of one wave's partial result in the split walk: the 64 x 32 float
@@ -66,8 +68,8 @@ constexpr size_t kSplitPartBytes = (size_t)9 * 64 * 16;
 // Workspace bytes of the split walk for a fixed-length prefill of this shape
 // and window on the current device (flag words first, *flag_bytes of them,
 // 256-byte aligned, then the partial results), or 0 where the walk is not
-// taken: grids of more than one 128-query tile per CU or key bands of fewer
-// than 8 tiles; with force, grids whose doubled size is not resident at
+// taken: always without force (the halves-split workgroups serve small
+// grids), and with force on grids whose doubled size is not resident at
 // once (more than 1.5 query tiles per CU).
 size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_bytes);
 
@@ -75,6 +77,10 @@ size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_
 // shape on the current device (B*T*H*64 bf16), or 0 where the grid is too
 // small for rotating the keys once, ahead of the kernel, to pay off.
 size_t prefill_krot_bytes(int B, int T, int H);
+
+// Whether a fixed-length prefill of this shape takes the halves-split
+// workgroups (64 queries, each wave one 32-key half of every tile).
+bool prefill_half_split(int B, int T, int H);
 
 struct StreamArgs {
   const void* q;

@@ -177,11 +177,10 @@ def test_prefill_workspace_size(L):
     size = L.vx_swa_attn_prefill_workspace_size
     c = cfg()
     # a cos/sin table of B*T rows of 256 bytes (rounded up to 256), then, where
-    # the split walk is taken (at most one 128-query tile per compute unit,
-    # 256 CUs without a device, and key bands of at least 8 tiles; with
-    # VX_FLAG_SPLIT_WALK at most 1.5 tiles per CU, any band), a flag word per
-    # (b, h, query tile, wave), 256-byte aligned, and two 9216-byte partial
-    # results per flag
+    # the split walk is taken (only with VX_FLAG_SPLIT_WALK, on grids of at
+    # most 1.5 128-query tiles per compute unit: 256 CUs without a device), a
+    # flag word per (b, h, query tile, wave), 256-byte aligned, and two
+    # 9216-byte partial results per flag
     # grids of at least 16 query tiles per CU also keep the keys rotated
     # ahead of the kernel there (B*T*H rows of 128 bytes)
     assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256 + 8 * 6000 * 32 * 128
@@ -190,9 +189,10 @@ def test_prefill_workspace_size(L):
     assert size(4, 1500, 32, ctypes.byref(c)) == 4 * 1500 * 256
     assert size(2, 1500, 32, ctypes.byref(c)) == 2 * 1500 * 256  # 768 query tiles: neither
     assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256  # 384 query tiles: not split
-    slots = 12 * 16 * 4
-    assert size(1, 1500, 16, ctypes.byref(c)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
+    assert size(1, 1500, 16, ctypes.byref(c)) == 1500 * 256  # no split without the flag
     force = cfg(flags=2)
+    slots = 12 * 16 * 4
+    assert size(1, 1500, 16, ctypes.byref(force)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
     slots = 12 * 32 * 4
     assert size(1, 1500, 32, ctypes.byref(force)) == 1500 * 256 + slots * 8 + slots * 2 * 9216
     assert size(2, 1500, 32, ctypes.byref(force)) == 2 * 1500 * 256  # 768 tiles: never split

@@ -1,20 +1,19 @@
 """GPU tests of the split walk of vx_swa_attn_prefill.
 
-With a workspace of vx_swa_attn_prefill_workspace_size() bytes, grids of at
-most one four-wave (128-query) tile per compute unit whose key bands span at
-least 8 tiles (one 1500-frame chunk of 16 heads, say) take the split walk:
-each query tile gets two workgroups, one per half of its key band, and per
-wave the one that finishes second merges the two softmax partials.
-VX_FLAG_SPLIT_WALK (force_split) takes it on every grid of at most 1.5
-tiles per CU, which lets these tests reach its degenerate cases.  Checked
-here, through the C ABI:
+With VX_FLAG_SPLIT_WALK (force_split) and a workspace of
+vx_swa_attn_prefill_workspace_size() bytes, grids of at most 1.5
+four-wave (128-query) tiles per compute unit take the split walk instead of
+the default halves-split workgroups: each query tile gets two workgroups,
+one per half of its key band, and per wave the one that finishes second
+merges the two softmax partials through the workspace.  Checked here,
+through the C ABI:
 - the outputs against the bf16-contract oracle, at the parity tests'
   tolerance, on the layer workload and on ragged and degenerate shapes (one
   key tile, so one half walks nothing; fewer than 8 (batch, head) pairs;
   W = 1; W above T; pre-rotated input; float32 output; per-entry positions);
 - the split actually ran: the flag words, filled with a byte pattern before
-  the call, read zero after it (each merge resets its flag), and the default
-  choice (split at 192 query tiles, not at 384);
+  the call, read zero after it (each merge resets its flag); without the
+  flag the workspace's flag region is left alone;
 - run-to-run identical bits (the merge order does not depend on which half
   finishes first), also when the workspace starts out holding random bytes;
 - graph replays equal to the eager call (the flags are zero again after
@@ -37,8 +36,7 @@ N_CUS = 256
 def split_layout(B, T, H, W, force):
     """(flag bytes, partial bytes) of the split walk, or None where it is not taken."""
     wg = -(-T // 128) * B * H
-    band_tiles = -(-min(T, W + 127) // 64)
-    if not (2 * wg <= 3 * N_CUS if force else (wg <= N_CUS and band_tiles >= 8)):
+    if not (force and 2 * wg <= 3 * N_CUS):
         return None
     slots = wg * 4
     return (slots * 8 + 255) // 256 * 256, slots * 2 * PART_BYTES
@@ -169,28 +167,24 @@ def test_split_graph_replays_match_eager():
     assert flags_zero(ws, 0, c.B, c.T, c.H)
 
 
-def test_split_default_choice():
-    """Without the flag: 192 query tiles of 14-tile bands split, 384 do not
-    (the workspace then holds the table only and the output equals the
-    call without a workspace, bit for bit)."""
+def test_no_split_without_the_flag():
+    """Without VX_FLAG_SPLIT_WALK a workspace holds the table only: the flag
+    region of a workspace sized for the split is left alone, and the output
+    equals the call without a workspace bit for bit (the halves-split
+    schedule both times)."""
     import torch
     W = 750
-    for H, split in ((16, True), (32, False)):
-        say(f"split walk default: B1 T1500 H{H} -> {'split' if split else 'unsplit'}")
-        x = synth.make_prefill(1, 1500, H, seed=760 + H, dtype="bf16", scale=0.5)
-        table = vx.rope_table(0, 1500)
-        n = vx.prefill_workspace_size(1, 1500, H, W)
-        assert (split_layout(1, 1500, H, W, False) is not None) == split
-        assert (n > 1500 * 256) == split
-        ws = torch.full(((n + 15) // 16 * 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    for T, H in ((1500, 16), (500, 32)):
+        say(f"no split without the flag: B1 T{T} H{H}")
+        x = synth.make_prefill(1, T, H, seed=760 + H, dtype="bf16", scale=0.5)
+        table = vx.rope_table(0, T)
+        assert vx.prefill_workspace_size(1, T, H, W) == T * 256
+        ws = workspace(1, T, H, W)  # sized for the split (with the flag)
         got = run(x, W, ws, table=table, force=False)
         q, k, v = (dev(x[n_], "bf16") for n_ in ("q", "k", "v"))
         plain = vx.prefill(q, k, v, window=W, table=table)
         torch.cuda.synchronize()
-        if split:
-            assert flags_zero(ws, 0, 1, 1500, H)
-            assert not torch.equal(got, plain)  # a different summation order
-            check_bf16(host(got), oracle.prefill(x["q"], x["k"], x["v"], W, bf16=True),
-                       f"split default H{H}")
-        else:
-            assert torch.equal(got, plain)
+        assert torch.equal(got, plain)
+        assert bool(torch.all(ws[: 4 * -(-T // 128) * H * 8] == 0xA5).item())
+        check_bf16(host(got), oracle.prefill(x["q"], x["k"], x["v"], W, bf16=True),
+                   f"default schedule T{T} H{H}")
