@@ -57,14 +57,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-               "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
-               21_719_881 + 6_144_000),
+               "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
+               21_684_970 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
-              "7823f39e6c6bb863f6330420c0f9775166a1ba66eed09eda0c641f0ded7f9820",
-              396_079_283 + 3_146_512),
+              "735e9f9bf00ba20ab84eec779c6a8fe18c87926d3e6cd79d91dcdbc3f46b5cda",
+              396_079_413 + 3_146_672),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                   "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
-                   155_773_176 + 107_363_608),
+                   "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
+                   155_747_097 + 107_363_008),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "71d51d1bade315e29fb14b1164cdef63eb44efb65221e448a1e6a7302bfe4288",
                    2_148_346_558 + 786_944),
@@ -78,11 +78,11 @@ MEASURED_TRAFFIC = {
                     "5feee362e008dbf0c8734e53c411e85c079a11a14a2749654e18950708698381",
                     450_948_348 + 134_504_800),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "15b252553591d538e6b6904de50237641b659aeeaffdc5e2cc5179a4c386899b",
-             103_888_047 + 24_576_000),
+             "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
+             104_003_436 + 24_576_000),
     "long": (("prefill_mfma.hip", "rope.hip", "vx_device.h", "vx_launch.h"),
-            "71aa5b889d4328905b1a91440a32b2b37240e99bfdbc540c168f6a3df9ea9ab5",
-            (951_333_253 + 196_608_432) + (208_806_050 + 196_608_112)),
+            "76006df7e4d55941748d2c85d7df3a0a80ac6a441cda9085a1c0bb403c6d5389",
+            (950_903_473 + 196_608_704) + (208_805_570 + 196_608_288)),
 }
 
 
