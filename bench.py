@@ -57,14 +57,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-               "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
-               21_684_970 + 6_144_000),
+               "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
+               21_684_910 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
               "735e9f9bf00ba20ab84eec779c6a8fe18c87926d3e6cd79d91dcdbc3f46b5cda",
               396_079_413 + 3_146_672),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                   "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
-                   155_747_097 + 107_363_008),
+                   "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
+                   155_832_918 + 107_365_344),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "71d51d1bade315e29fb14b1164cdef63eb44efb65221e448a1e6a7302bfe4288",
                    2_148_346_558 + 786_944),
@@ -78,11 +78,11 @@ MEASURED_TRAFFIC = {
                     "5feee362e008dbf0c8734e53c411e85c079a11a14a2749654e18950708698381",
                     450_948_348 + 134_504_800),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "38ed4a79101acd2ebf06fc50f6c38925e843a2dbee4e436f91a5ee81c88ed1e1",
-             104_003_436 + 24_576_000),
+             "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
+             103_863_204 + 24_576_032),
     "long": (("prefill_mfma.hip", "rope.hip", "vx_device.h", "vx_launch.h"),
-            "76006df7e4d55941748d2c85d7df3a0a80ac6a441cda9085a1c0bb403c6d5389",
-            (950_903_473 + 196_608_704) + (208_805_570 + 196_608_288)),
+            "9d3490daff455a8eae247671c4e88a9f390c2d6c653edf1f2925f1cea34a3d7d",
+            (953_707_745 + 196_608_240) + (208_817_419 + 196_608_928)),
 }
 
 
@@ -247,7 +247,7 @@ def main():
 
     # ---- 32-layer attention stack (B4 T1500, fresh seeded Q/K/V per layer) and long-form
     # prefill (B8 T6000, 1 % of key rows x8), both with fused RoPE; each call gets a
-    # workspace, in which grids of at least 16 query tiles per CU (the long form, the
+    # workspace, in which grids of at least 8 query tiles per CU (the long form, the
     # stack as one B128 call) keep their keys rotated once, ahead of the attention
     # kernel (the same bits as rotating them in the kernel's staging)
     stack_in, long_in = [], None

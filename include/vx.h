@@ -160,7 +160,7 @@ vx_status vx_rope_qk(void *q, void *k, int32_t B, int32_t T, int32_t H, const in
  * as zero, so the workspace needs no clearing.  Split results are
  * deterministic but not the same bits as the default schedule's (another
  * summation order; within the same tolerance of the exact result).
- * On grids of at least 16 query tiles per compute unit (B8 T2048 H32, say)
+ * On grids of at least 8 query tiles per compute unit (B8 T1500 H32, say)
  * with a table (the caller's or one built in the workspace), the workspace
  * also takes the keys rotated once ahead of the attention kernel (one more
  * launch, B*T*H*64 bf16 after the table), which then stages them without

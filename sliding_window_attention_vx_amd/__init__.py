@@ -280,12 +280,11 @@ def prefill(q, k, v, window=WINDOW, pos0=None, theta=THETA, scale=0.0, rope_appl
     the chunk's positions is made here (auto_table=True); otherwise the
     library builds one in the workspace if it has room, else computes cos/sin
     in the kernel.  workspace: a uint8 device tensor (prefill_workspace), reused
-    across calls; None runs without one.  With a workspace, grids of at most
-    one 128-query tile per compute unit and key bands of 8 tiles or more
-    take the split walk (two workgroups per query tile); force_split takes it
-    on every grid small enough for it.  Grids of at least 16 tiles per unit
-    with a table rotate their keys once, into the workspace, ahead of the
-    attention kernel (the same bits).
+    across calls; None runs without one.  With a workspace and force_split,
+    grids of at most 1.5 128-query tiles per compute unit take the split
+    walk (two workgroups per query tile).  Grids of at least 8 tiles per
+    unit with a table rotate their keys once, into the workspace, ahead of
+    the attention kernel (the same bits).
     """
     import torch
     for name, x in (("q", q), ("k", k), ("v", v)):

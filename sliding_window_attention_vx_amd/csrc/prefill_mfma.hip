@@ -29,9 +29,10 @@
 // Frame t of batch entry b sits at position pos0[b] + t; an entry whose
 // positions are negative or outside the table, or a varlen stream longer
 // than the call allows, gets NaN outputs (loud, never a silent partial).
-// LDS rows are padded (K' 144 bytes, V 192 bytes) and the staging threads
-// are mapped to rows so that the MFMA operand reads and the staging writes
-// hit distinct banks.  K/V staging is double buffered: the next tile's buffer
+// LDS rows are padded (K' 144 bytes, V 192 bytes; V in swizzled 128-byte
+// rows on rotated keys, see VLayout) and the staging threads are mapped to
+// rows so that the MFMA operand reads and the staging writes hit distinct
+// banks.  K/V staging is double buffered: the next tile's buffer
 // loads (per-tile descriptors in scalar registers) are issued before the
 // current tile's MFMAs.  Masks are applied only to the
 // 32-key halves that straddle a band edge, as one unsigned range test per
@@ -77,11 +78,24 @@ namespace {
 constexpr int kBN = 64;                    // keys per staged tile
 constexpr int kRowK = 144;                 // LDS bytes per K' row: 16-byte reads of 32
                                            // consecutive rows hit distinct banks
-constexpr int kRowV = 192;                 // LDS bytes per V row: the 8-byte transpose
-                                           // reads of 4 rows x 2 dim blocks hit distinct banks
 constexpr int kTileK = 64 * kRowK;         // one K' tile
-constexpr int kTileV = 64 * kRowV;         // one V tile
-constexpr int kStageBytes = kTileK + kTileV;
+// V rows in LDS.  Padded (CV false): 192-byte rows, where the 8-byte transpose
+// reads of 4 rows x 2 dim blocks hit distinct banks.  Compact (CV true):
+// 128-byte rows with row r's 16-byte chunk c at chunk c ^ 4*((r>>1)&1), which
+// keeps the transpose reads and the staging writes on distinct banks (see
+// v_unit and the kernel's v_off) in two thirds of the bytes: the kernel on
+// rotated keys, at 128 VGPRs, then fits four workgroups per CU (34 KB of LDS
+// each instead of 42 KB).
+template <bool CV>
+struct VLayout {
+  static constexpr int kRowV = CV ? 128 : 192;  // LDS bytes per V row
+  static constexpr int kTileV = 64 * kRowV;     // one V tile
+  static constexpr int kStageBytes = kTileK + kTileV;
+  // byte offset of row r's 16-byte chunk c
+  static __device__ __forceinline__ int chunk(int r, int c) {
+    return r * kRowV + (CV ? ((16 * c) ^ (64 * ((r >> 1) & 1))) : 16 * c);
+  }
+};
 constexpr float kLazy = 8.0f;              // log2-domain slack of the running max
 constexpr float kNoMax = -3.0e38f;          // running max before the first score
 // split-walk flag tokens: kSplitTok + half (any other flag value counts as
@@ -113,11 +127,21 @@ __device__ __forceinline__ void k_unit(int u, int& r, int& cp) {
   cp = u & 3;
   r = 16 * (u >> 6) + 4 * ((u >> 2) & 3) + ((u >> 4) & 3);
 }
-// V unit u -> (row, 16-byte chunk): 16 consecutive lanes cover rows 0..3 x 4 chunks,
-// conflict-free at the 192-byte row stride; 8 lanes still read each 128-byte row.
+// V unit u -> (row, 16-byte chunk), 8 lanes reading each 128-byte row.  Padded
+// rows: 16 consecutive lanes cover rows 0..3 x 4 chunks, whose stores hit distinct
+// banks at the 192-byte stride.  Compact rows: 8 consecutive lanes store one whole
+// row, which the chunk swizzle only permutes, so every group of lanes writes whole
+// 128-byte rows (with rows 0..3 x 4 chunks the compact layout counted about a
+// million bank-conflict cycles per launch at B4 T1500, about 7 per store).
+template <bool CV>
 __device__ __forceinline__ void v_unit(int u, int& r, int& c) {
-  r = 8 * (u >> 6) + 4 * ((u >> 5) & 1) + ((u >> 2) & 3);
-  c = 4 * ((u >> 4) & 1) + (u & 3);
+  if constexpr (CV) {
+    r = u >> 3;
+    c = u & 7;
+  } else {
+    r = 8 * (u >> 6) + 4 * ((u >> 5) & 1) + ((u >> 2) & 3);
+    c = 4 * ((u >> 4) & 1) + (u & 3);
+  }
 }
 
 // Frequency of pair 8c+e, c in 0..3 chosen per lane: selects between
@@ -234,7 +258,7 @@ struct StageOffs {
   int kr[Stage<NW>::UK], kcp[Stage<NW>::UK];  // row and chunk pair of each K unit
 };
 
-template <int NW>
+template <int NW, bool CV>
 __device__ __forceinline__ StageOffs<NW> stage_offsets(int tid, size_t rs) {
   constexpr int NT = Stage<NW>::NT;
   const uint32_t rb = (uint32_t)(rs * sizeof(bf16));
@@ -251,7 +275,7 @@ __device__ __forceinline__ StageOffs<NW> stage_offsets(int tid, size_t rs) {
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
     int r, c;
-    v_unit(tid + j * NT, r, c);
+    v_unit<CV>(tid + j * NT, r, c);
     so.v[j] = r * rb + 16 * c;
   }
   return so;
@@ -330,7 +354,7 @@ struct Seed {
   }
 };
 
-template <int NW, bool SEED = false, bool KROT = true>
+template <int NW, bool SEED = false, bool KROT = true, bool CV = false>
 __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char* Vb, bool rope,
                                              int tid, const Seed& sd = Seed{}) {
   constexpr int NT = Stage<NW>::NT;
@@ -365,8 +389,8 @@ __device__ __forceinline__ void stage_commit(const Stage<NW>& st, char* Kb, char
 #pragma unroll
   for (int j = 0; j < Stage<NW>::UV; ++j) {
     int r, c;
-    v_unit(tid + j * NT, r, c);
-    *reinterpret_cast<u32x4*>(Vb + r * kRowV + 16 * c) = st.v[j];
+    v_unit<CV>(tid + j * NT, r, c);
+    *reinterpret_cast<u32x4*>(Vb + VLayout<CV>::chunk(r, c)) = st.v[j];
     int slot;
     if (SEED && sd.take(r, slot))
       *reinterpret_cast<u32x4*>(sd.ring_v + (size_t)slot * kD + 8 * c) = st.v[j];
@@ -381,8 +405,12 @@ __device__ __forceinline__ unsigned long long lane0_u64(unsigned long long x) {
 }
 
 template <int NW, typename TO, bool SEED, bool OTF, bool SPLIT, bool KROT, bool HS>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a, int n_qtiles,
-                                                                  int n_short, int hx, int cpx) {
+__global__ __launch_bounds__(NW * 64, (NW == 4 && !KROT && !HS) ? 4 : 2) void prefill_mfma_kernel(
+    PrefillArgs a, int n_qtiles, int n_short, int hx, int cpx) {
+  // compact V rows where they let four workgroups share a CU
+  constexpr bool CV = NW == 4 && !KROT && !HS;
+  using VL = VLayout<CV>;
+  constexpr int kRowV = VL::kRowV, kStageBytes = VL::kStageBytes;
   __shared__ __attribute__((aligned(16))) char lds[2 * kStageBytes];
   // HS (halves split): four waves cover 64 queries, two per 32-query block,
   // each taking one 32-key half of every staged tile; the two merge through
@@ -513,7 +541,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     }
   }
   Stage<NW> st;
-  const StageOffs<NW> so = stage_offsets<NW>(tid, rs);
+  const StageOffs<NW> so = stage_offsets<NW, CV>(tid, rs);
   stage_load<NW, OTF, KROT>(st, k, v, rs, T, it_start * kBN, rope, a, trow0, p0, so);
   if (rope && !OTF) {
 #pragma unroll
@@ -558,9 +586,15 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
 
   // per-lane LDS offsets: K' fragment row/col, and the transpose-read address
   // (lane L of each 16-lane group points at row L/4, dims 4*(L%4) of its block)
+  // per 32-dim block db.  In compact V rows the chunk swizzle swaps the row's
+  // 64-byte halves for rows with bit 1 set, which for these rows is bit 3 of
+  // L; a read of 32 lanes then covers rows 4i..4i+3 at banks 32*(r&1) +
+  // [0, 16) and [16, 32).
   const int k_off = l32 * kRowK + 16 * hh;
   const int g = lane >> 4, L = lane & 15;
-  const int v_off = (4 * (g >> 1) + (L >> 2)) * kRowV + (16 * (g & 1) + 4 * (L & 3)) * 2;
+  const int v_row = (4 * (g >> 1) + (L >> 2)) * kRowV + (16 * (g & 1) + 4 * (L & 3)) * 2;
+  const int v_sw = CV ? 64 * (L >> 3) : 0;
+  const int v_off[2] = {v_row + v_sw, v_row + (64 ^ v_sw)};
 
   f32x16 oacc[2];
   oacc[0] = f32x16{};
@@ -589,7 +623,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     sd.kt0 = kt0;
     return sd;
   };
-  stage_commit<NW, SEED, KROT>(st, lds, lds + kTileK, rope, tid, seed_for(it_start * kBN));
+  stage_commit<NW, SEED, KROT, CV>(st, lds, lds + kTileK, rope, tid, seed_for(it_start * kBN));
   __syncthreads();
 
   // One step per key tile: the next tile's loads go out first (after the
@@ -630,12 +664,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
         l_run = dot2_ones(w1[i], l_run);
       }
       const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, w0), __builtin_bit_cast(bf16x8, w1)};
-      const char* vr = Vb + 32 * sb * kRowV + v_off;
+      const char* vr = Vb + 32 * sb * kRowV;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const char* p0 = vr + 16 * ks * kRowV + 64 * db;
+          const char* p0 = vr + 16 * ks * kRowV + v_off[db];
           const bf16x8 vf = lds_tr_pair(p0, p0 + 8 * kRowV);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[db], 0, 0, 0);
         }
@@ -714,7 +748,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_mfma_kernel(PrefillArgs a,
     }
 
     if (kt_next < T)
-      stage_commit<NW, SEED, KROT>(st, lds + (buf ^ 1) * kStageBytes,
+      stage_commit<NW, SEED, KROT, CV>(st, lds + (buf ^ 1) * kStageBytes,
                              lds + (buf ^ 1) * kStageBytes + kTileK, rope, tid,
                              seed_for(kt_next));
     __syncthreads();
@@ -984,13 +1018,16 @@ size_t prefill_split_bytes(int B, int T, int H, int W, bool force, size_t* flag_
 
 // Rotating the keys ahead of the kernel costs one more read and write of K
 // (a launch of its own) and saves the kernel about a quarter of its vector
-// work, which sets its pace at full occupancy: measured, B8 T6000 H32 523
-// against 549 us and B32 T1500 H32 461 against 478, but B4 T1500 H32 60.7
-// against 59.0.  So only grids of at least 16 query tiles per CU take it.
+// work, which sets its pace at full occupancy; the kernel on rotated keys
+// also fits four workgroups per CU instead of three (compact V rows).
+// Measured against rotating them in the staging: B8 T6000 H32 498 against
+// 560 us, B8 T1500 H32 106.7 against 111.6, but B4 T1500 H32 57.6 against
+// 56.7 and B2 T3000 H32 65.1 against 64.4 (6 query tiles per CU).  So grids
+// of at least 8 query tiles per CU take it.
 size_t prefill_krot_bytes(int B, int T, int H) {
   const int64_t wg4 = (int64_t)((T + 127) / 128) * H * B;
   const int64_t cus = (int64_t)cus_per_xcd() * 8;
-  if (wg4 < 16 * cus) return 0;
+  if (wg4 < 8 * cus) return 0;
   return (size_t)B * T * H * kD * sizeof(bf16);
 }
 

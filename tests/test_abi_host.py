@@ -181,11 +181,12 @@ def test_prefill_workspace_size(L):
     # most 1.5 128-query tiles per compute unit: 256 CUs without a device), a
     # flag word per (b, h, query tile, wave), 256-byte aligned, and two
     # 9216-byte partial results per flag
-    # grids of at least 16 query tiles per CU also keep the keys rotated
+    # grids of at least 8 query tiles per CU also keep the keys rotated
     # ahead of the kernel there (B*T*H rows of 128 bytes)
     assert size(8, 6000, 32, ctypes.byref(c)) == 8 * 6000 * 256 + 8 * 6000 * 32 * 128
-    assert size(8, 2048, 32, ctypes.byref(c)) == 8 * 2048 * 256 + 8 * 2048 * 32 * 128
-    assert size(8, 1500, 32, ctypes.byref(c)) == 8 * 1500 * 256  # 12 tiles per CU: not
+    assert size(8, 1500, 32, ctypes.byref(c)) == 8 * 1500 * 256 + 8 * 1500 * 32 * 128
+    assert size(8, 1024, 32, ctypes.byref(c)) == 8 * 1024 * 256 + 8 * 1024 * 32 * 128  # 8 per CU
+    assert size(7, 1024, 32, ctypes.byref(c)) == 7 * 1024 * 256  # 7 tiles per CU: not
     assert size(4, 1500, 32, ctypes.byref(c)) == 4 * 1500 * 256
     assert size(2, 1500, 32, ctypes.byref(c)) == 2 * 1500 * 256  # 768 query tiles: neither
     assert size(1, 1500, 32, ctypes.byref(c)) == 1500 * 256  # 384 query tiles: not split

@@ -1,6 +1,6 @@
 """GPU tests of the prefill with keys rotated ahead of the kernel.
 
-On grids of at least 16 four-wave query tiles per compute unit (B8 T2048
+On grids of at least 8 four-wave query tiles per compute unit (B8 T1024
 H32 and up) and with a workspace of vx_swa_attn_prefill_workspace_size() bytes,
 vx_swa_attn_prefill first rotates K once into the workspace, reading for
 each frame the cos/sin row its own staging would read, and the kernel then
