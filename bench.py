@@ -57,14 +57,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-               "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
-               21_684_910 + 6_144_000),
+               "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
+               21_678_993 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
               "735e9f9bf00ba20ab84eec779c6a8fe18c87926d3e6cd79d91dcdbc3f46b5cda",
               396_079_413 + 3_146_672),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                   "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
-                   155_832_918 + 107_365_344),
+                   "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
+                   155_817_769 + 107_364_080),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "71d51d1bade315e29fb14b1164cdef63eb44efb65221e448a1e6a7302bfe4288",
                    2_148_346_558 + 786_944),
@@ -78,11 +78,11 @@ MEASURED_TRAFFIC = {
                     "5feee362e008dbf0c8734e53c411e85c079a11a14a2749654e18950708698381",
                     450_948_348 + 134_504_800),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "ada114268bd66bdc5c97bceb62c4c95bf3a765003c89c31ad695b8c388029196",
-             103_863_204 + 24_576_032),
+             "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
+             103_710_933 + 24_576_360),
     "long": (("prefill_mfma.hip", "rope.hip", "vx_device.h", "vx_launch.h"),
-            "9d3490daff455a8eae247671c4e88a9f390c2d6c653edf1f2925f1cea34a3d7d",
-            (953_707_745 + 196_608_240) + (208_817_419 + 196_608_928)),
+            "c405f5fb5275e36485ef09ad4eb1163734afca59329ba2ace1484fb48adc2b2a",
+            (952_984_550 + 196_609_712) + (208_807_140 + 196_608_064)),
 }
 
 

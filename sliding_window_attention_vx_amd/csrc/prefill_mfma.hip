@@ -301,7 +301,10 @@ __device__ __forceinline__ void stage_load(Stage<NW>& st, const bf16* __restrict
                                            const bf16* __restrict__ v, size_t rs, int T, int kt0,
                                            bool rope, const PrefillArgs& a, int64_t trow0,
                                            int64_t p0, const StageOffs<NW>& so) {
-  const uint32_t nrows = (uint32_t)max(min(T - kt0, kBN), 0);
+  // kt0 <= T on every call (tiles of the band, or T past the last one), so a
+  // plain min: a clamp at 0 as well becomes a vector med3 and a vector
+  // multiply whose results go back to scalar registers, every tile
+  const uint32_t nrows = (uint32_t)min(T - kt0, kBN);
   const uint32_t rb = (uint32_t)(rs * sizeof(bf16));
   const auto kr = rows_rsrc(k + (size_t)kt0 * rs, nrows * rb);
   const auto vr = rows_rsrc(v + (size_t)kt0 * rs, nrows * rb);
@@ -693,17 +696,21 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && !KROT && !HS) ? 4 : 2) void pr
       }
     };
 
-    bool act[2], msk[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    // 32-key half sb: active if it meets this wave's band, masked if it
+    // straddles an edge of it
+    auto active = [&](int sb) {
       const int kb = kt0 + 32 * sb;
-      act[sb] = (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
-      msk[sb] = (kb + 31 > qw) || (kb < qw + 31 - W + 1);
-    }
+      return (qw < T) && (kb < T) && (kb + 31 >= qw - W + 1) && (kb <= qw + 31);
+    };
+    auto edge = [&](int sb) {
+      const int kb = kt0 + 32 * sb;
+      return (kb + 31 > qw) || (kb < qw + 31 - W + 1);
+    };
     if constexpr (HS) {
-      if (act[hsb]) {
+      // only this wave's half: its flags stay scalar
+      if (active(hsb)) {
         f32x16 sc = s_half(hsb);
-        if (msk[hsb]) {
+        if (edge(hsb)) {
           const int d0 = tq - (kt0 + 32 * hsb + 4 * hh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -718,32 +725,35 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && !KROT && !HS) ? 4 : 2) void pr
         const float mu = m_run;
         pv_half(sc, hsb, mu);
       }
-    } else if (act[0] || act[1]) {
-      // Software pipeline over the two 32-key halves: the second half's score
-      // MFMAs are issued before the first half's softmax, so the matrix core
-      // runs while the VALU computes exponentials.
-      f32x16 s_cur = act[0] ? s_half(0) : s_half(1);
-      f32x16 s_nxt = f32x16{};
+    } else {
+      const bool act[2] = {active(0), active(1)}, msk[2] = {edge(0), edge(1)};
+      if (act[0] || act[1]) {
+        // Software pipeline over the two 32-key halves: the second half's score
+        // MFMAs are issued before the first half's softmax, so the matrix core
+        // runs while the VALU computes exponentials.
+        f32x16 s_cur = act[0] ? s_half(0) : s_half(1);
+        f32x16 s_nxt = f32x16{};
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (!act[sb]) continue;
-        if (msk[sb]) {
-          // key of register r: kb + 4hh + 8(r/4) + r%4; keep iff 0 <= tq - key <= W-1
-          const int d0 = tq - (kt0 + 32 * sb + 4 * hh);
+        for (int sb = 0; sb < 2; ++sb) {
+          if (!act[sb]) continue;
+          if (msk[sb]) {
+            // key of register r: kb + 4hh + 8(r/4) + r%4; keep iff 0 <= tq - key <= W-1
+            const int d0 = tq - (kt0 + 32 * sb + 4 * hh);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);
-            s_cur[r] = ((unsigned)(d0 - off) <= wm1) ? s_cur[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int off = 8 * (r >> 2) + (r & 3);
+              s_cur[r] = ((unsigned)(d0 - off) <= wm1) ? s_cur[r] : -INFINITY;
+            }
           }
-        }
-        float mx = -INFINITY;
+          float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-        if (sb == 0 && act[1]) s_nxt = s_half(1);
-        update_max(mx);
-        const float mu = m_run;
-        pv_half(s_cur, sb, mu);
-        s_cur = s_nxt;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+          if (sb == 0 && act[1]) s_nxt = s_half(1);
+          update_max(mx);
+          const float mu = m_run;
+          pv_half(s_cur, sb, mu);
+          s_cur = s_nxt;
+        }
       }
     }
 
