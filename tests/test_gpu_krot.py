@@ -23,6 +23,7 @@ from tests.test_gpu_parity import check_bf16, dev, host, say
 pytestmark = pytest.mark.gpu
 
 B, T, H, W = 8, 2048, 32, 750
+N_CUS = 256  # compute units of an MI355X
 
 
 def inputs(seed):
@@ -107,3 +108,29 @@ def test_prerotated_input_on_a_large_grid_equals_fused():
     pre = vx.prefill(q2, k2, v, window=W, rope_applied=True)
     torch.cuda.synchronize()
     assert torch.equal(fused, pre)
+
+
+@pytest.mark.parametrize("B,T,H,W_", [(3, 1001, 32, 97), (2, 777, 64, 750), (1, 3001, 48, 1),
+                                      (5, 450, 48, 2000)])
+def test_prerotated_ragged_shapes_equal_fused_and_match_oracle(B, T, H, W_):
+    """Grids of more than 1.5 four-wave query tiles per compute unit on
+    pre-rotated input run the kernel on rotated keys, whose V tiles sit in
+    compact swizzled 128-byte rows (four workgroups per CU); the fused call
+    on the same grid runs the same schedule with padded V rows.  Ragged T
+    (a partial last key tile), W from 1 to above T: the two agree bit for
+    bit, and sampled (b, h) pairs match the oracle."""
+    import torch
+    from tests.test_gpu_parity import _check_picks
+    wg4 = -(-T // 128) * H * B
+    assert 2 * wg4 > 3 * N_CUS, "the shape should take 128-query workgroups"
+    say(f"pre-rotated vs fused, 128-query workgroups: B{B} T{T} H{H} W{W_}")
+    x = synth.make_prefill(B, T, H, seed=950 + T + W_, dtype="bf16", scale=0.5)
+    q, k, v = (dev(x[n], "bf16") for n in ("q", "k", "v"))
+    fused = vx.prefill(q, k, v, window=W_)
+    q2, k2 = q.clone(), k.clone()
+    vx.rope_qk(q2, k2)
+    pre = vx.prefill(q2, k2, v, window=W_, rope_applied=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, pre)
+    picks = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    _check_picks(x, host(pre), picks, W_, f"pre-rotated B{B} T{T} H{H} W{W_}")
