@@ -46,7 +46,8 @@
 // half as long and the device holds twice the workgroups; the two waves of a
 // block merge their partial results through LDS at the end.  Each key tile
 // is staged for 64 queries instead of 128, which costs more vector work in
-// all, so larger grids keep 128-query workgroups.
+// all, so larger grids keep 128-query workgroups.  The halves split walks
+// each band from its newest key tile down to its oldest.
 //
 // Split walk (on request, with a workspace), for the same small grids: each
 // query tile gets two workgroups, the first walking the
@@ -506,6 +507,12 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && !KROT && !HS) ? 4 : 2) void pr
   const int P = 2 + (W - 1 + kBN - 1) / kBN;
   int it_start = SPLIT ? it0 : it0 + (P - it0 % P) % P;
   if (it_start > it1) it_start = it0;
+  // The halves split (small grids, whose K, V and table rows all stay in L2)
+  // walks its band from the newest tile down to the oldest instead: with no
+  // reuse to arrange, each wave starts on the tile that holds its own
+  // queries' keys (layer workload 21.98 -> 21.72 us, same box, three
+  // alternating runs).
+  if (HS) it_start = it1;
   // (the same in every lane; the division above is expanded on the vector ALU)
   it_start = __builtin_amdgcn_readfirstlane(it_start);
 
@@ -770,12 +777,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && !KROT && !HS) ? 4 : 2) void pr
   unsigned long long* flag = nullptr;
   unsigned long long seen = 0;
   if (SPLIT) flag = a.split_flags + ((size_t)bh * n_qtiles + qt) * NW + wave;
-  const int kt_wrap = it_start > it0 ? it0 * kBN : T;
-  for (int it = it_start; it <= it1; ++it) {
-    if (SPLIT && it == it1) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tile_step(it, it < it1 ? (it + 1) * kBN : kt_wrap);
+  if constexpr (HS) {
+    for (int it = it1; it >= it0; --it) tile_step(it, it > it0 ? (it - 1) * kBN : T);
+  } else {
+    const int kt_wrap = it_start > it0 ? it0 * kBN : T;
+    for (int it = it_start; it <= it1; ++it) {
+      if (SPLIT && it == it1) seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tile_step(it, it < it1 ? (it + 1) * kBN : kt_wrap);
+    }
+    for (int it = it0; it < it_start; ++it) tile_step(it, it + 1 < it_start ? (it + 1) * kBN : T);
   }
-  for (int it = it0; it < it_start; ++it) tile_step(it, it + 1 < it_start ? (it + 1) * kBN : T);
 
   if constexpr (SPLIT) {
     const size_t slot = ((size_t)bh * n_qtiles + qt) * NW + wave;
