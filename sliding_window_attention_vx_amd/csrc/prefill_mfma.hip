@@ -183,6 +183,9 @@ __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, i
   //    tiles go first in ascending order and the R smallest follow in
   //    descending order: the largest of the late ones shares a CU with the
   //    smallest of the early ones, which evens out the work per CU.
+  //  - N <= 3 cpx (all resident too, e.g. one 1500-frame chunk of 32 heads
+  //    in 64-query workgroups): a snake over the tiles ranked longest first,
+  //    CU c taking ranks c, 2 cpx - 1 - c and 2 cpx + c.
   //  - larger grids: full-length tiles first, then the short ones longest
   //    first, which arrive last and pair up with a long workgroup on a CU
   //    that still has room.
@@ -206,9 +209,18 @@ __device__ __forceinline__ bool work_item(int n_bh, int n_qtiles, int n_short, i
     const int n_long = n_qtiles - n_short;
     const int N = hx * n_qtiles;
     int bl;
-    if (!SPLIT && N <= 2 * cpx) {
-      const int R = max(N - cpx, 0);
-      const int k = i < N - R ? R + i : R - 1 - (i - (N - R));
+    if (!SPLIT && N <= 3 * cpx) {
+      int k;
+      if (N <= 2 * cpx) {
+        const int R = max(N - cpx, 0);
+        k = i < N - R ? R + i : R - 1 - (i - (N - R));
+      } else {
+        // three rounds: a snake over the tiles ranked longest first (CU c
+        // takes ranks c, 2 cpx - 1 - c and 2 cpx + c), so the CUs' sums of
+        // tile steps differ by at most about one tile
+        const int d = i < cpx ? i : (i < 2 * cpx ? 3 * cpx - 1 - i : i);
+        k = N - 1 - d;
+      }
       if (k < hx * n_short) {
         qt = k / hx;
         bl = k % hx;
