@@ -57,14 +57,14 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "sliding_window_attention_vx_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-               "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
-               21_678_993 + 6_144_000),
+               "70385c15869df08b761bb7315b018f75da4ea7edaab5c8be07aa83d62461ef55",
+               21_644_768 + 6_144_000),
     "stream": (("stream.hip", "vx_device.h", "vx_launch.h"),
               "735e9f9bf00ba20ab84eec779c6a8fe18c87926d3e6cd79d91dcdbc3f46b5cda",
               396_079_413 + 3_146_672),
     "first_chunk": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-                   "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
-                   155_817_769 + 107_364_080),
+                   "70385c15869df08b761bb7315b018f75da4ea7edaab5c8be07aa83d62461ef55",
+                   155_812_800 + 107_363_920),
     "gqa_decode": (("gqa_decode.hip", "gqa_launch.h", "vx_device.h"),
                    "71d51d1bade315e29fb14b1164cdef63eb44efb65221e448a1e6a7302bfe4288",
                    2_148_346_558 + 786_944),
@@ -78,11 +78,11 @@ MEASURED_TRAFFIC = {
                     "5feee362e008dbf0c8734e53c411e85c079a11a14a2749654e18950708698381",
                     450_948_348 + 134_504_800),
     "stack": (("prefill_mfma.hip", "vx_device.h", "vx_launch.h"),
-             "833db3c6733bb36c21b8e910175eb021af25b3d0e3fb696b8d3164346ca32fb1",
-             103_710_933 + 24_576_360),
+             "70385c15869df08b761bb7315b018f75da4ea7edaab5c8be07aa83d62461ef55",
+             103_764_736 + 24_576_000),
     "long": (("prefill_mfma.hip", "rope.hip", "vx_device.h", "vx_launch.h"),
-            "c405f5fb5275e36485ef09ad4eb1163734afca59329ba2ace1484fb48adc2b2a",
-            (952_984_550 + 196_609_712) + (208_807_140 + 196_608_064)),
+            "a324a3a587e03e18df83ffe59dc4a70ad091cc8fcb18baec0de92f504796039c",
+            (952_918_304 + 196_612_264) + (208_812_960 + 196_608_288)),
 }
 
 
